@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for the shared-KV cross-attention path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py``; never by the product package.
+"""
+from .xattn import (  # noqa: F401
+    attend_rows,
+    decode_ref,
+    kv_append_ref,
+    kv_head_of,
+    prefill_ref,
+    scores,
+    softmax_weights,
+    visible_rows,
+)

@@ -1,0 +1,225 @@
+"""fp64 CPU oracle of YOCO's Cross-Decoder attention over the one shared K̂,V̂.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, links or runs
+this module; only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` do. It shares no code with the HIP kernels.
+
+What it computes is the plain definition, written out step by step:
+
+* Every Cross-Decoder layer l attends with its own queries Q̂^l to the single
+  shared pair K̂, V̂ that the Self-Decoder output produced once
+  ("YOCO", zdszero.github.io: section "架构总览" (architecture overview),
+  the equations for K̂, V̂ and Q̂^l, and section "Cross-Decoder：共享 KV，但不共享
+  Query", the Attn_l equation)::
+
+      Attn_l = softmax(Q̂^l K̂^T / sqrt(d_k) + M_causal) V̂
+
+* M_causal lets the query at position i see shared-cache rows j no later than i,
+  i.e. j <= i (same page, end of "架构总览").
+* Grouped-query attention: several query heads read one KV head ("YOCO 深度技术分析",
+  liuhc.cn: section 2.1 (architecture), Cross-Decoder bullet list; the shared KV
+  may itself use fewer KV heads: "YOCO", section "与其他 KV 优化方法的区别").
+* Decode: the new token passes the Self-Decoder first, so its own K̂,V̂ row is in
+  the cache before the Cross-Decoder layers read it ("YOCO", section "Decode：
+  新 token 仍需经过两部分").
+
+Readings where the pages are silent (each is listed in the design notes):
+
+* d_k is the head dimension; the scale is passed explicitly.
+* The query head h reads KV head h // (Hq / Hkv) (contiguous groups).
+* The mask is inclusive (j <= i) and exact (masked rows carry zero weight).
+* Prefill queries and keys index the same positions; a decode query sits at
+  position seq_len - 1 after its row was appended.
+* No positional transform inside the cross-attention.
+* LSE is the natural-log log-sum-exp of the scaled scores; an empty sequence
+  yields O = 0 and LSE = -inf.
+
+All arithmetic is float64 on exact upcasts of the stored values. Query rows are
+processed in blocks only to bound memory: each row's arithmetic is the
+definition above, independently of every other row.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "visible_rows",
+    "prefill_position",
+    "decode_position",
+    "scores",
+    "softmax_weights",
+    "log_sum_exp",
+    "attend_rows",
+    "prefill_ref",
+    "decode_ref",
+    "kv_append_ref",
+]
+
+
+# ---------------------------------------------------------------------------
+# The definition's steps, one small function each.
+# ---------------------------------------------------------------------------
+
+def kv_head_of(h: int, q_heads: int, kv_heads: int) -> int:
+    """KV head read by query head h: contiguous groups of Hq/Hkv query heads."""
+    return h // (q_heads // kv_heads)
+
+
+def visible_rows(p: int) -> int:
+    """Number of shared-cache rows the query at position p sees: rows 0..p."""
+    return p + 1
+
+
+def prefill_position(r: int) -> int:
+    """Position of packed prefill query row r of a sequence: queries and keys index the same prompt."""
+    return r
+
+
+def decode_position(n: int) -> int:
+    """Position of the decode query once its own row is appended: the last of n valid rows."""
+    return n - 1
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """s[r, j] = scale * <q[r], k[j]>  (q: [r, d], k: [n, d])."""
+    return scale * (q @ k.T)
+
+
+def softmax_weights(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Row-wise softmax pieces of s (masked entries are -inf).
+
+    Returns (w, m, z): m = max_j s_j, w_j = exp(s_j - m), z = sum_j w_j, so that
+    softmax(s)_j = w_j / z and log-sum-exp(s) = m + log z.
+    """
+    m = np.max(s, axis=-1, keepdims=True)
+    w = np.exp(s - m)
+    z = np.sum(w, axis=-1, keepdims=True)
+    return w, m, z
+
+
+def log_sum_exp(m: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """log sum_j exp(s_j) from the softmax pieces: m + log z."""
+    return m + np.log(z)
+
+
+def attend_rows(q: np.ndarray, positions: np.ndarray, k: np.ndarray, v: np.ndarray,
+                scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Causal attention of query rows q [r, d] at `positions` [r] to rows k, v [n, d].
+
+    Row i of the result is sum_j softmax_j(scale q_i.k_j, j <= p_i) v_j and its LSE.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    r = q.shape[0]
+    out = np.zeros((r, v.shape[1]), dtype=np.float64)
+    lse = np.full((r,), -np.inf, dtype=np.float64)
+    if r == 0:
+        return out, lse
+    n_vis = max(visible_rows(int(p)) for p in positions)
+    kk = np.asarray(k[:n_vis], dtype=np.float64)
+    vv = np.asarray(v[:n_vis], dtype=np.float64)
+    s = scores(q, kk, scale)
+    j = np.arange(n_vis)[None, :]
+    lim = np.array([visible_rows(int(p)) for p in positions])[:, None]
+    s = np.where(j < lim, s, -np.inf)
+    w, m, z = softmax_weights(s)
+    out = (w @ vv) / z
+    lse = log_sum_exp(m, z)[:, 0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# The three operations of the path, on the pool layout.
+# ---------------------------------------------------------------------------
+
+def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start: Sequence[int],
+                seq_len: Sequence[int], cu_seqlens: Sequence[int], scale: float,
+                rows: Optional[Dict[int, Iterable[int]]] = None, block: int = 512
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """Causal cross-attention of every packed query row to its sequence's shared rows.
+
+    q: [total_q, Hq, d]; k_pool, v_pool: [rows, Hkv, d]. Query row r of sequence b
+    (packed row cu_seqlens[b] + r) sits at position r and sees cache rows
+    seq_start[b] + 0 .. seq_start[b] + r. Requires q_len[b] == seq_len[b].
+    `rows` (optional) restricts the work to {b: [r, ...]}; rows not computed are NaN.
+    Returns out [total_q, Hq, d] and lse [Hq, total_q] (float64).
+    """
+    total_q, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    out = np.full((total_q, hq, d), np.nan if rows is not None else 0.0, dtype=np.float64)
+    lse = np.full((hq, total_q), np.nan if rows is not None else -np.inf, dtype=np.float64)
+    nseq = len(seq_len)
+    for b in range(nseq):
+        n = int(seq_len[b])
+        q0 = int(cu_seqlens[b])
+        if int(cu_seqlens[b + 1]) - q0 != n:
+            raise ValueError("prefill oracle needs q_len == seq_len for every sequence")
+        want = np.arange(n) if rows is None else np.asarray(sorted(set(rows.get(b, ()))), dtype=np.int64)
+        if want.size == 0:
+            continue
+        s0 = int(seq_start[b])
+        for h in range(hq):
+            kh = kv_head_of(h, hq, hkv)
+            kb = k_pool[s0:s0 + n, kh, :]
+            vb = v_pool[s0:s0 + n, kh, :]
+            for i in range(0, want.size, block):
+                r = want[i:i + block]
+                pos = np.array([prefill_position(int(x)) for x in r], dtype=np.int64)
+                o, l = attend_rows(q[q0 + r, h, :], pos, kb, vb, scale)
+                out[q0 + r, h, :] = o
+                lse[h, q0 + r] = l
+    return out, lse
+
+
+def decode_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start: Sequence[int],
+               seq_len: Sequence[int], scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One query per sequence at position seq_len[b] - 1, against rows 0..seq_len[b]-1.
+
+    q: [B, Hq, d]. Returns out [B, Hq, d] and lse [B, Hq] (float64). A sequence with
+    no rows gives out = 0 and lse = -inf.
+    """
+    bsz, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    out = np.zeros((bsz, hq, d), dtype=np.float64)
+    lse = np.full((bsz, hq), -np.inf, dtype=np.float64)
+    for b in range(bsz):
+        n = int(seq_len[b])
+        if n == 0:
+            continue
+        s0 = int(seq_start[b])
+        for kh in range(hkv):
+            kb = np.asarray(k_pool[s0:s0 + n, kh, :], dtype=np.float64)
+            vb = np.asarray(v_pool[s0:s0 + n, kh, :], dtype=np.float64)
+            for h in range(hq):
+                if kv_head_of(h, hq, hkv) != kh:
+                    continue
+                o, l = attend_rows(q[b, h:h + 1, :], np.array([decode_position(n)]), kb, vb, scale)
+                out[b, h] = o[0]
+                lse[b, h] = l[0]
+    return out, lse
+
+
+def kv_append_ref(k_pool: np.ndarray, v_pool: np.ndarray, seq_start: Sequence[int],
+                  seq_len: Sequence[int], seq_cap: Sequence[int], k_new: np.ndarray,
+                  v_new: np.ndarray):
+    """Write each sequence's new K̂,V̂ row at its next free row; one more valid row.
+
+    A sequence whose cache is full keeps its pool rows and length and raises the
+    overflow flag. Returns (k_pool', v_pool', seq_len', overflow) as new arrays.
+    """
+    k2 = np.array(k_pool, copy=True)
+    v2 = np.array(v_pool, copy=True)
+    lens = np.array(seq_len, dtype=np.int64, copy=True)
+    overflow = 0
+    for b in range(len(lens)):
+        if lens[b] >= int(seq_cap[b]):
+            overflow = 1
+            continue
+        row = int(seq_start[b]) + int(lens[b])
+        k2[row] = k_new[b]
+        v2[row] = v_new[b]
+        lens[b] += 1
+    return k2, v2, lens, overflow

@@ -1,0 +1,258 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each ``check_*`` function raises AssertionError (or any exception) when the
+oracle disagrees with what the pages and the mathematics fix. They are plain
+functions so that the mutation tests can run them against an oracle with a
+planted mistake and require that at least one of them fails.
+
+What pins what:
+
+* brute force: pure-Python scalar loops (math.exp / math.fsum, no max
+  subtraction) on tiny shapes -- the definition of causal softmax attention
+  with contiguous GQA groups, written independently of NumPy;
+* torch's scaled_dot_product_attention in float64 on the CPU with
+  is_causal=True and enable_gqa=True -- a library routine for the square
+  (queries = keys) causal GQA case;
+* closed forms: K = 0 gives the prefix mean of V and LSE = log(p + 1); V = c
+  gives c; one row gives V[0]; a planted needle gives that row; a hand-worked
+  two-key case from tests/golden/;
+* invariants: decode at p equals prefill row p; rows past p do not matter;
+  shifting every key by u leaves O and moves LSE by scale*q.u; GQA equals MHA
+  with repeated KV heads; packed sequences equal separate calls; (cQ, s/c)
+  equals (Q, s); softmax weights sum to 1;
+* append: the new row lands at seq_start + seq_len, overflow leaves all alone.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle.xattn as ox
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _pool_case(rng, lens, hq, hkv, d, junk=3):
+    """Packed queries + pool with `junk` finite capacity rows after each sequence."""
+    caps = [n + junk for n in lens]
+    starts = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64)
+    rows = int(sum(caps))
+    k = rng.standard_normal((rows, hkv, d))
+    v = rng.standard_normal((rows, hkv, d))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q = rng.standard_normal((int(cu[-1]), hq, d))
+    return q, k, v, starts, np.asarray(lens, dtype=np.int64), cu
+
+
+# ---------------------------------------------------------------------------
+# brute force
+# ---------------------------------------------------------------------------
+
+def _brute_prefill(q, k, v, starts, lens, cu, scale):
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    out = [[[0.0] * d for _ in range(hq)] for _ in range(total)]
+    lse = [[0.0] * total for _ in range(hq)]
+    for b in range(len(lens)):
+        for r in range(int(lens[b])):
+            row = int(cu[b]) + r
+            for h in range(hq):
+                kh = h // g
+                e = []
+                for j in range(r + 1):
+                    key = k[int(starts[b]) + j, kh]
+                    dot = math.fsum(float(q[row, h, t]) * float(key[t]) for t in range(d))
+                    e.append(math.exp(scale * dot))
+                z = math.fsum(e)
+                for t in range(d):
+                    out[row][h][t] = math.fsum(e[j] * float(v[int(starts[b]) + j, kh, t])
+                                               for j in range(r + 1)) / z
+                lse[h][row] = math.log(z)
+    return np.array(out), np.array(lse)
+
+
+def check_bruteforce():
+    rng = _rng(11)
+    for lens, hq, hkv, d, scale in [((5,), 2, 1, 3, 0.7), ((4, 7), 4, 2, 4, 0.5), ((9,), 4, 1, 8, 0.35),
+                                    ((1, 3, 6), 2, 2, 2, 1.3), ((12,), 8, 2, 5, 0.45)]:
+        q, k, v, st, ln, cu = _pool_case(rng, lens, hq, hkv, d)
+        o, l = ox.prefill_ref(q, k, v, st, ln, cu, scale)
+        ob, lb = _brute_prefill(q, k, v, st, ln, cu, scale)
+        assert np.max(np.abs(o - ob)) <= 1e-13, ("brute force out", lens, np.max(np.abs(o - ob)))
+        assert np.max(np.abs(l - lb)) <= 1e-13, ("brute force lse", lens)
+        # decode of the last row of each sequence = brute-force row
+        qd = np.stack([q[int(cu[b + 1]) - 1] for b in range(len(lens))])
+        od, ld = ox.decode_ref(qd, k, v, st, ln, scale)
+        for b in range(len(lens)):
+            row = int(cu[b + 1]) - 1
+            assert np.max(np.abs(od[b] - ob[row])) <= 1e-13, ("brute force decode", lens, b)
+            assert np.max(np.abs(ld[b] - lb[:, row])) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# library special case
+# ---------------------------------------------------------------------------
+
+def check_sdpa():
+    import torch.nn.functional as F
+    rng = _rng(12)
+    for n, hq, hkv, d in [(33, 4, 1, 16), (70, 8, 2, 32), (130, 6, 3, 8), (64, 4, 4, 64)]:
+        q, k, v, st, ln, cu = _pool_case(rng, (n,), hq, hkv, d, junk=0)
+        scale = 1.0 / math.sqrt(d)
+        o, _ = ox.prefill_ref(q, k, v, st, ln, cu, scale)
+        tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+        tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+        tv = torch.from_numpy(v).permute(1, 0, 2)[None]
+        ts = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True, scale=scale)
+        ref = ts[0].permute(1, 0, 2).numpy()
+        assert np.max(np.abs(o - ref)) <= 1e-12, ("sdpa", n, hq, hkv, np.max(np.abs(o - ref)))
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def check_closed_forms():
+    rng = _rng(13)
+    n, hq, hkv, d = 40, 4, 2, 6
+    q, k, v, st, ln, cu = _pool_case(rng, (n,), hq, hkv, d, junk=2)
+    # K = 0 (inside the sequence): every visible row weighs the same
+    kz = k.copy()
+    kz[:n] = 0.0
+    o, l = ox.prefill_ref(q, kz, v, st, ln, cu, 0.9)
+    for h in range(hq):
+        kh = h // (hq // hkv)
+        prefix_mean = np.cumsum(v[:n, kh], axis=0) / np.arange(1, n + 1)[:, None]
+        assert np.max(np.abs(o[:, h] - prefix_mean)) <= 1e-13, "K=0 prefix mean"
+        assert np.max(np.abs(l[h] - np.log(np.arange(1, n + 1)))) <= 1e-13, "K=0 lse"
+    # Q = 0 likewise
+    o, _ = ox.prefill_ref(np.zeros_like(q), k, v, st, ln, cu, 0.9)
+    for h in range(hq):
+        kh = h // (hq // hkv)
+        prefix_mean = np.cumsum(v[:n, kh], axis=0) / np.arange(1, n + 1)[:, None]
+        assert np.max(np.abs(o[:, h] - prefix_mean)) <= 1e-13, "Q=0 prefix mean"
+    # V = c per KV head: the weights sum to one
+    c = rng.standard_normal((hkv, d))
+    vc = v.copy()
+    vc[:n] = c[None]
+    o, _ = ox.prefill_ref(q, k, vc, st, ln, cu, 0.9)
+    for h in range(hq):
+        assert np.max(np.abs(o[:, h] - c[h // (hq // hkv)][None])) <= 1e-13, "V=c"
+    # single row: O = V[0], LSE = scale q.k0
+    q1, k1, v1, st1, ln1, cu1 = _pool_case(rng, (1,), 4, 1, 5, junk=4)
+    o, l = ox.prefill_ref(q1, k1, v1, st1, ln1, cu1, 0.6)
+    assert np.max(np.abs(o[0] - v1[0, 0][None])) <= 1e-15
+    assert np.max(np.abs(l[:, 0] - 0.6 * (q1[0] @ k1[0, 0]))) <= 1e-13
+    # planted needle: row 17 aligned with the query, far above all others
+    n2, d2 = 64, 16
+    q2, k2, v2, st2, ln2, cu2 = _pool_case(rng, (n2,), 1, 1, d2, junk=1)
+    k2 *= 0.01
+    qn = q2[n2 - 1, 0] / np.linalg.norm(q2[n2 - 1, 0])
+    k2[17, 0] = 60.0 * qn
+    od, _ = ox.decode_ref(q2[n2 - 1][None] / np.linalg.norm(q2[n2 - 1, 0]), k2, v2, st2, ln2, 1.0)
+    assert np.max(np.abs(od[0, 0] - v2[17, 0])) <= 1e-20 + 64 * math.exp(-55) * np.max(np.abs(v2)), "needle"
+    # hand-worked fixtures
+    with open(os.path.join(GOLDEN, "hand_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for cs in cases:
+        qh = np.array(cs["q"], dtype=np.float64)
+        kh_ = np.array(cs["k"], dtype=np.float64)
+        vh = np.array(cs["v"], dtype=np.float64)
+        nn = kh_.shape[0]
+        o, l = ox.prefill_ref(qh, kh_, vh, [0], [nn], [0, nn], cs["scale"])
+        exp_o = np.array(cs["expected_out"], dtype=np.float64)
+        exp_l = np.array(cs["expected_lse"], dtype=np.float64)
+        assert np.max(np.abs(o - exp_o)) <= 1e-14, ("hand case", cs["name"], o, exp_o)
+        assert np.max(np.abs(l - exp_l)) <= 1e-14, ("hand case lse", cs["name"], l, exp_l)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def check_invariants():
+    rng = _rng(14)
+    lens = (23, 9, 31)
+    hq, hkv, d = 6, 2, 8
+    q, k, v, st, ln, cu = _pool_case(rng, lens, hq, hkv, d, junk=4)
+    scale = 0.4
+    o, l = ox.prefill_ref(q, k, v, st, ln, cu, scale)
+    # decode at p = prefill row p, for every p of every sequence
+    for b, n in enumerate(lens):
+        for p in range(n):
+            lens_p = np.array(ln)
+            lens_p[b] = p + 1
+            qd = np.zeros((len(lens), hq, d))
+            qd[b] = q[int(cu[b]) + p]
+            od, ld = ox.decode_ref(qd, k, v, st, lens_p, scale)
+            assert np.max(np.abs(od[b] - o[int(cu[b]) + p])) <= 1e-14, ("decode = prefill row", b, p)
+            assert np.max(np.abs(ld[b] - l[:, int(cu[b]) + p])) <= 1e-14
+    # causal-mask invariance: rows past p, perturbed with finite values, change nothing
+    b, p = 2, 12
+    k2, v2 = k.copy(), v.copy()
+    s0 = int(st[b])
+    k2[s0 + p + 1:s0 + lens[b] + 4] += 5.0 * rng.standard_normal(k2[s0 + p + 1:s0 + lens[b] + 4].shape)
+    v2[s0 + p + 1:s0 + lens[b] + 4] -= 7.0
+    o2, l2 = ox.prefill_ref(q, k2, v2, st, ln, cu, scale)
+    rows = slice(int(cu[b]), int(cu[b]) + p + 1)
+    assert np.array_equal(o2[rows], o[rows]) and np.array_equal(l2[:, rows], l[:, rows]), "causal invariance"
+    assert np.max(np.abs(o2[int(cu[b]) + p + 1:int(cu[b + 1])] - o[int(cu[b]) + p + 1:int(cu[b + 1])])) > 1e-3
+    # shift of every key by u: O unchanged, LSE moves by scale * q.u
+    u = rng.standard_normal((hkv, d))
+    o3, l3 = ox.prefill_ref(q, k + u[None], v, st, ln, cu, scale)
+    assert np.max(np.abs(o3 - o)) <= 1e-12, "key shift leaves O"
+    g = hq // hkv
+    for h in range(hq):
+        shift = scale * (q[:, h, :] @ u[h // g])
+        assert np.max(np.abs(l3[h] - l[h] - shift)) <= 1e-12, "key shift moves LSE"
+    # GQA = MHA on repeated KV heads
+    kr = np.repeat(k, g, axis=1)
+    vr = np.repeat(v, g, axis=1)
+    o4, l4 = ox.prefill_ref(q, kr, vr, st, ln, cu, scale)
+    assert np.max(np.abs(o4 - o)) <= 1e-14 and np.max(np.abs(l4 - l)) <= 1e-14, "GQA = MHA repeat"
+    # packed sequences = separate calls
+    for b, n in enumerate(lens):
+        s0 = int(st[b])
+        ob, lb = ox.prefill_ref(q[int(cu[b]):int(cu[b + 1])], k[s0:s0 + n], v[s0:s0 + n], [0], [n], [0, n], scale)
+        assert np.max(np.abs(ob - o[int(cu[b]):int(cu[b + 1])])) <= 1e-14, "varlen = separate"
+        assert np.max(np.abs(lb - l[:, int(cu[b]):int(cu[b + 1])])) <= 1e-14
+    # (c Q, scale / c) = (Q, scale)
+    o5, l5 = ox.prefill_ref(4.0 * q, k, v, st, ln, cu, scale / 4.0)
+    assert np.max(np.abs(o5 - o)) <= 1e-12 and np.max(np.abs(l5 - l)) <= 1e-12, "scale covariance"
+    # softmax weights of any masked score row sum to one
+    s = rng.standard_normal((5, 9))
+    s[:, 6:] = -np.inf
+    w, m, z = ox.softmax_weights(s)
+    assert np.max(np.abs((w / z).sum(axis=1) - 1.0)) <= 1e-15 and np.all(w[:, 6:] == 0.0)
+    # empty decode sequence: O = 0, LSE = -inf
+    od, ld = ox.decode_ref(np.ones((1, 2, 3)), np.ones((4, 1, 3)), np.ones((4, 1, 3)), [0], [0], 1.0)
+    assert np.all(od == 0.0) and np.all(np.isneginf(ld))
+
+
+def check_append():
+    rng = _rng(15)
+    k = rng.standard_normal((24, 2, 4))
+    v = rng.standard_normal((24, 2, 4))
+    st, ln, cap = [0, 8, 14], [3, 6, 6], [8, 6, 8]
+    kn = rng.standard_normal((3, 2, 4))
+    vn = rng.standard_normal((3, 2, 4))
+    k2, v2, ln2, ov = ox.kv_append_ref(k, v, st, ln, cap, kn, vn)
+    assert list(ln2) == [4, 6, 7] and ov == 1, (list(ln2), ov)
+    assert np.array_equal(k2[3], kn[0]) and np.array_equal(v2[3], vn[0])
+    assert np.array_equal(k2[20], kn[2]) and np.array_equal(v2[20], vn[2])
+    changed = [i for i in range(24) if not np.array_equal(k2[i], k[i]) or not np.array_equal(v2[i], v[i])]
+    assert changed == [3, 20], changed
+    _, _, ln3, ov3 = ox.kv_append_ref(k, v, [0], [2], [3], kn[:1], vn[:1])
+    assert list(ln3) == [3] and ov3 == 0
+
+
+ALL_PINS = [check_bruteforce, check_sdpa, check_closed_forms, check_invariants, check_append]

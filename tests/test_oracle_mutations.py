@@ -1,0 +1,88 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one pin.
+
+Every mutation replaces one step of the oracle with a plausible wrong version:
+a wrong head map, an off-by-one or missing causal limit, a dropped or doubled
+scale, a sign flip, a transposed operand, a missing normalisation, a dropped
+max term in the LSE, a wrong decode or prefill position, an append at the wrong
+row or without the overflow check.
+"""
+import numpy as np
+import pytest
+
+import oracle.xattn as ox
+import pinlib
+
+
+def _append_wrong_row(k_pool, v_pool, seq_start, seq_len, seq_cap, k_new, v_new):
+    k2, v2 = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    lens = np.array(seq_len, dtype=np.int64, copy=True)
+    ov = 0
+    for b in range(len(lens)):
+        if lens[b] >= int(seq_cap[b]):
+            ov = 1
+            continue
+        row = int(seq_start[b]) + int(lens[b]) - 1
+        k2[row], v2[row] = k_new[b], v_new[b]
+        lens[b] += 1
+    return k2, v2, lens, ov
+
+
+def _append_no_cap(k_pool, v_pool, seq_start, seq_len, seq_cap, k_new, v_new):
+    k2, v2 = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    lens = np.array(seq_len, dtype=np.int64, copy=True)
+    for b in range(len(lens)):
+        row = int(seq_start[b]) + int(lens[b])
+        k2[row], v2[row] = k_new[b], v_new[b]
+        lens[b] += 1
+    return k2, v2, lens, 0
+
+
+def _softmax_no_exp(s):
+    m = np.max(s, axis=-1, keepdims=True)
+    w = np.where(np.isfinite(s), s - m + 10.0, 0.0)
+    return w, m, np.sum(w, axis=-1, keepdims=True)
+
+
+def _softmax_unnormalised_sum(s):
+    m = np.max(s, axis=-1, keepdims=True)
+    w = np.exp(s - m)
+    return w, m, np.ones_like(m)
+
+
+MUTATIONS = {
+    "head_map_interleaved": ("kv_head_of", lambda h, hq, hkv: h % hkv),
+    "head_map_zero": ("kv_head_of", lambda h, hq, hkv: 0),
+    "mask_excludes_diagonal": ("visible_rows", lambda p: p),
+    "mask_one_too_many": ("visible_rows", lambda p: p + 2),
+    "no_scale": ("scores", lambda q, k, scale: q @ k.T),
+    "scale_squared": ("scores", lambda q, k, scale: scale * scale * (q @ k.T)),
+    "sqrt_scale": ("scores", lambda q, k, scale: np.sqrt(scale) * (q @ k.T)),
+    "negated_scores": ("scores", lambda q, k, scale: -scale * (q @ k.T)),
+    "no_exp": ("softmax_weights", _softmax_no_exp),
+    "no_normalisation": ("softmax_weights", _softmax_unnormalised_sum),
+    "lse_drops_max": ("log_sum_exp", lambda m, z: np.log(z)),
+    "lse_log2": ("log_sum_exp", lambda m, z: m + np.log2(z)),
+    "prefill_position_shift": ("prefill_position", lambda r: r + 1),
+    "decode_position_before_append": ("decode_position", lambda n: n - 2),
+    "decode_position_past_end": ("decode_position", lambda n: n),
+    "append_wrong_row": ("kv_append_ref", _append_wrong_row),
+    "append_ignores_capacity": ("kv_append_ref", _append_no_cap),
+}
+
+
+def test_unmutated_oracle_passes_all_pins():
+    for check in pinlib.ALL_PINS:
+        check()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, repl = MUTATIONS[name]
+    monkeypatch.setattr(ox, attr, repl)
+    caught = []
+    for check in pinlib.ALL_PINS:
+        try:
+            check()
+        except Exception:  # noqa: BLE001 - any failure of a pin counts
+            caught.append(check.__name__)
+    assert caught, f"mutation {name} passed every pin"
