@@ -1,0 +1,21 @@
+"""MI355X-native shared-KV cross-attention (YOCO Cross-Decoder hot path).
+
+The compute lives in the HIP library ``lib/libyoco_xattn.so`` (C ABI in
+``include/yoco_xattn.h``); this package is its thin Python binding. Nothing
+here falls back to another implementation: calls raise if the library is
+missing or rejects its arguments.
+"""
+from .xattn import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    SharedKV,
+    YocoError,
+    alloc_workspace,
+    decode_splits,
+    kv_append,
+    load_library,
+    make_dims,
+    workspace_size,
+    xattn_decode,
+    xattn_prefill,
+)

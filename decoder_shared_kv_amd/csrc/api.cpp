@@ -1,0 +1,212 @@
+// C ABI entry points: host-side argument checks, launch planning, dispatch.
+//
+// Every check runs before the first launch, so a call that returns an error has
+// launched nothing. All launches go to the caller's stream; nothing here
+// synchronises, allocates or keeps state between calls.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/yoco_xattn.h"
+#include "internal.h"
+
+namespace {
+
+using yoco::AttnParams;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kDecodeKeysPerIter = 128;  // rows one decode workgroup consumes per iteration
+constexpr int kDecodeTargetWgs = 1024;   // split-K target: ~4 workgroups per CU
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_size(int dtype) { return dtype == YOCO_DTYPE_BF16 ? 2 : 4; }
+
+yoco_status check_dims(const yoco_dims* d) {
+  if (d == nullptr) return YOCO_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return YOCO_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return YOCO_ERR_INVALID_ARG;
+  if (!std::isfinite(d->scale)) return YOCO_ERR_INVALID_ARG;
+  if (d->dtype != YOCO_DTYPE_F32 && d->dtype != YOCO_DTYPE_BF16) return YOCO_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return YOCO_ERR_UNSUPPORTED;
+  return YOCO_OK;
+}
+
+yoco_status check_cache(const yoco_kv_cache* c) {
+  if (c == nullptr) return YOCO_ERR_INVALID_ARG;
+  if (c->k == nullptr || c->v == nullptr || !aligned16(c->k) || !aligned16(c->v)) return YOCO_ERR_INVALID_ARG;
+  if (c->seq_start == nullptr || c->seq_len == nullptr || c->seq_cap == nullptr) return YOCO_ERR_INVALID_ARG;
+  if (!aligned4(c->seq_len) || !aligned4(c->seq_cap) || (reinterpret_cast<uintptr_t>(c->seq_start) & 7u))
+    return YOCO_ERR_INVALID_ARG;
+  if (c->pool_rows < 0) return YOCO_ERR_INVALID_ARG;
+  return YOCO_OK;
+}
+
+int head_chunks(const yoco_dims* d) {
+  const int g = d->num_q_heads / d->num_kv_heads;
+  return (g + 15) / 16;
+}
+
+void plan_decode(const yoco_dims* d, int32_t max_kv_len, int32_t* splits, int32_t* rows) {
+  const int64_t units = (int64_t)d->batch * d->num_kv_heads * head_chunks(d);
+  int64_t want = (kDecodeTargetWgs + units - 1) / units;
+  if (want < 1) want = 1;
+  int64_t n = max_kv_len > 0 ? max_kv_len : 1;
+  int64_t r = (n + want - 1) / want;
+  r = (r + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter * kDecodeKeysPerIter;
+  if (r < kDecodeKeysPerIter) r = kDecodeKeysPerIter;
+  *rows = (int32_t)r;
+  *splits = (int32_t)((n + r - 1) / r);
+}
+
+size_t decode_ml_offset(const yoco_dims* d, int32_t splits) {
+  const size_t o = (size_t)d->batch * d->num_q_heads * splits * d->head_dim * sizeof(float);
+  return (o + 255) & ~(size_t)255;
+}
+
+size_t decode_workspace(const yoco_dims* d, int32_t splits) {
+  return decode_ml_offset(d, splits) + (size_t)d->batch * d->num_q_heads * splits * 2 * sizeof(float);
+}
+
+AttnParams base_params(const yoco_dims* d, const yoco_kv_cache* c) {
+  AttnParams p{};
+  p.k = c->k;
+  p.v = c->v;
+  p.seq_start = c->seq_start;
+  p.seq_len = c->seq_len;
+  p.seq_cap = c->seq_cap;
+  p.pool_rows = c->pool_rows;
+  p.batch = d->batch;
+  p.hq = d->num_q_heads;
+  p.hkv = d->num_kv_heads;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.scale_log2 = d->scale * kLog2e;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+yoco_status yoco_kv_append(const yoco_dims* dims, const yoco_kv_cache* cache, const void* k_new,
+                           const void* v_new, int32_t* overflow_flag, void* stream) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || !aligned16(k_new) || !aligned16(v_new)) return YOCO_ERR_INVALID_ARG;
+  if (overflow_flag != nullptr && !aligned4(overflow_flag)) return YOCO_ERR_INVALID_ARG;
+  yoco::AppendParams p{};
+  p.k = cache->k;
+  p.v = cache->v;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.seq_start = cache->seq_start;
+  p.seq_len = cache->seq_len;
+  p.seq_cap = cache->seq_cap;
+  p.overflow = overflow_flag;
+  p.pool_rows = cache->pool_rows;
+  p.row_bytes = dims->num_kv_heads * dims->head_dim * elem_size(dims->dtype);
+  if (yoco::launch_kv_append(p, dims->batch, static_cast<hipStream_t>(stream)) != hipSuccess) return YOCO_ERR_HIP;
+  return YOCO_OK;
+}
+
+yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
+                               const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q, void* out,
+                               float* lse, void* stream) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr) return YOCO_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned4(cu_seqlens_q)) return YOCO_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned4(lse)) return YOCO_ERR_INVALID_ARG;
+  if (max_q_len < 0 || total_q < 0) return YOCO_ERR_INVALID_ARG;
+  if (total_q == 0) return YOCO_OK;
+  AttnParams p = base_params(dims, cache);
+  p.q = q;
+  p.out = out;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens_q;
+  p.total_q = total_q;
+  const int64_t len = max_q_len > 0 ? max_q_len : 1;
+  hipError_t err;
+  if (dims->dtype == YOCO_DTYPE_BF16) {
+    const int ppw = yoco::prefill_positions_per_wg(p.group);
+    const int64_t units = (int64_t)dims->batch * dims->num_kv_heads * (p.group / yoco::prefill_heads_per_wg(p.group));
+    const int64_t blocks = (len + ppw - 1) / ppw;
+    if (blocks * units > INT32_MAX) return YOCO_ERR_UNSUPPORTED;
+    p.pos_blocks = (int32_t)blocks;
+    err = yoco::launch_prefill_bf16(p, dims->head_dim, (int)(blocks * units), static_cast<hipStream_t>(stream));
+  } else {
+    const int64_t units = (int64_t)dims->batch * dims->num_q_heads;
+    const int64_t blocks = (len + yoco::kPrefillF32Rows - 1) / yoco::kPrefillF32Rows;
+    if (blocks * units > INT32_MAX) return YOCO_ERR_UNSUPPORTED;
+    p.pos_blocks = (int32_t)blocks;
+    err = yoco::launch_prefill_f32(p, dims->head_dim, (int)(blocks * units), static_cast<hipStream_t>(stream));
+  }
+  return err == hipSuccess ? YOCO_OK : YOCO_ERR_HIP;
+}
+
+yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len, int32_t* splits,
+                                     int32_t* rows_per_split) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  if (splits == nullptr || rows_per_split == nullptr || max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
+  plan_decode(dims, max_kv_len, splits, rows_per_split);
+  return YOCO_OK;
+}
+
+yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  if (bytes == nullptr || max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
+  int32_t splits, rows;
+  plan_decode(dims, max_kv_len, &splits, &rows);
+  *bytes = decode_workspace(dims, splits);
+  return YOCO_OK;
+}
+
+yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
+                              int32_t max_kv_len, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return YOCO_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned4(lse)) return YOCO_ERR_INVALID_ARG;
+  if (max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
+  int32_t splits, rows;
+  plan_decode(dims, max_kv_len, &splits, &rows);
+  const size_t need = decode_workspace(dims, splits);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return YOCO_ERR_WORKSPACE;
+  AttnParams p = base_params(dims, cache);
+  p.q = q;
+  p.out = out;
+  p.lse = lse;
+  p.splits = splits;
+  p.split_rows = rows;
+  p.head_chunks = head_chunks(dims);
+  p.part_o = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ml_offset(dims, splits));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dims->dtype == YOCO_DTYPE_BF16 ? yoco::launch_decode_split_bf16(p, dims->head_dim, s)
+                                                  : yoco::launch_decode_split_f32(p, dims->head_dim, s);
+  if (err != hipSuccess) return YOCO_ERR_HIP;
+  if (yoco::launch_decode_merge(p, dims->head_dim, dims->dtype, s) != hipSuccess) return YOCO_ERR_HIP;
+  return YOCO_OK;
+}
+
+const char* yoco_status_string(yoco_status status) {
+  switch (status) {
+    case YOCO_OK: return "ok";
+    case YOCO_ERR_INVALID_ARG: return "invalid argument";
+    case YOCO_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
+    case YOCO_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case YOCO_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

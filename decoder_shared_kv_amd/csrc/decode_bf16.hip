@@ -1,0 +1,281 @@
+// Decode split pass, bf16 storage, MFMA for both contractions.
+//
+// Every Cross-Decoder layer re-reads the whole shared cache once per decode
+// step (page "YOCO", section "KV Cache 与计算量分析": repeated reads of the
+// shared KV make its bandwidth the critical path), so this kernel is bound by
+// HBM reads of K^ and V^. Design points:
+//  * one workgroup = (row split, KV head, sequence); it reads each cache row of
+//    its split exactly once, for ALL query heads of the KV group (<= 16 per
+//    workgroup), so GQA costs no extra traffic;
+//  * K^ rows go straight from HBM into MFMA A operands (16 B per lane, no LDS):
+//    S^T[key][head] = K^ . Q^T with v_mfma_f32_16x16x32_bf16, query heads padded
+//    to 16 columns;
+//  * the accumulator layout of S^T (lane = head, 4 consecutive keys per lane)
+//    is exactly the B-operand layout of v_mfma_f32_16x16x16_bf16 over those
+//    16 keys, so P^T never moves between lanes; V^ is transposed once through a
+//    small wave-private LDS tile to become the A operand (V^T);
+//  * online softmax in the base-2 domain, per lane, with two cross-lane max
+//    reductions per iteration; the partial (max, sum, unnormalised O) of the
+//    split is merged by decode_merge.
+#include <hip/hip_bf16.h>
+
+#include "internal.h"
+
+namespace yoco {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDecWaves = 4;
+constexpr int kVtStride = 20;  // 16 keys + 4 pad (bf16 elements) per transposed V^ row
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 c = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, c) << 16);
+}
+
+__device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
+
+// Per-lane register tile of one iteration: U blocks of 16 keys.
+template <int D, int U>
+struct DecRegs {
+  uint4 k[U][D / 32];       // A operand of S^T: key (lane & 15), 8 dims at 32*kk + 8*(lane >> 4)
+  uint32_t v[U][4][D / 32]; // 4 consecutive keys x D/16 dims (as D/32 dwords) for the V^ transpose
+};
+
+template <int D, int U>
+__device__ __forceinline__ void dec_load(DecRegs<D, U>& r, const __bf16* kbase, const __bf16* vbase,
+                                         int64_t row_stride, int base, int last, int lane) {
+  const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int key = base + 16 * u + col;
+    key = key < last ? key : last;
+    const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)key * row_stride + 8 * grp);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) r.k[u][kk] = src[kk * 4];  // 32 dims = 4 uint4 apart
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int vkey = base + 16 * u + 4 * grp + i;
+      vkey = vkey < last ? vkey : last;
+      const __bf16* vs = vbase + (int64_t)vkey * row_stride + col * (D / 16);
+      if constexpr (D == 128) {
+        const uint4 x = *reinterpret_cast<const uint4*>(vs);
+        r.v[u][i][0] = x.x; r.v[u][i][1] = x.y; r.v[u][i][2] = x.z; r.v[u][i][3] = x.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(vs);
+        r.v[u][i][0] = x.x; r.v[u][i][1] = x.y;
+      }
+    }
+  }
+}
+
+template <int D, int U>
+__global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
+  const int split = blockIdx.x;
+  const int kh = blockIdx.y / p.head_chunks;
+  const int hc = blockIdx.y % p.head_chunks;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // LDS: per-wave transposed V^ tiles; reused for the cross-wave combine at the end
+  constexpr int kVtBytes = kDecWaves * U * D * kVtStride * 2;
+  constexpr int kCombBytes = kDecWaves * 16 * (D + 2) * 4;
+  constexpr int kLdsBytes = kVtBytes > kCombBytes ? kVtBytes : kCombBytes;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __bf16* vt = reinterpret_cast<__bf16*>(lds) + wave * (U * D * kVtStride);
+
+  int64_t start;
+  const int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
+  const int j0 = split * p.split_rows;
+  int j1 = (split == p.splits - 1) ? n_kv : j0 + p.split_rows;
+  if (j1 > n_kv) j1 = n_kv;
+
+  const int h0 = kh * p.group + hc * 16;
+  const int nh = p.group - hc * 16 < 16 ? p.group - hc * 16 : 16;
+
+  // Q^T as the B operand: head column `col`, dims 32*kk + 8*grp .. +8
+  bf16x8 qf[D / 32];
+  {
+    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.hq + h0 + (col < nh ? col : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint4 x = *reinterpret_cast<const uint4*>(qsrc + 32 * kk);
+      if (col >= nh) x = make_uint4(0, 0, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  const int64_t row_stride = (int64_t)p.hkv * D;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + start * row_stride + (int64_t)kh * D;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + start * row_stride + (int64_t)kh * D;
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // running max of the base-2 scores of head `col` (same on its 4 lanes)
+  float l = 0.f;        // this lane's share of the running sum of weights
+
+  constexpr int kStep = kDecWaves * U * 16;
+  int base = j0 + wave * U * 16;
+  DecRegs<D, U> cur;
+  if (base < j1) dec_load<D, U>(cur, kbase, vbase, row_stride, base, j1 - 1, lane);
+  for (; base < j1; base += kStep) {
+    DecRegs<D, U> nxt;
+    const bool more = base + kStep < j1;
+    if (more) dec_load<D, U>(nxt, kbase, vbase, row_stride, base + kStep, j1 - 1, lane);
+
+    // S^T = K^ . Q^T, 16 keys x 16 heads per block
+    f32x4 s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[u][kk]), qf[kk], s[u], 0, 0, 0);
+    }
+    // scale to base 2, mask rows past the split end, block max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = base + 16 * u + 4 * grp + r;
+        const float t = key < j1 ? s[u][r] * p.scale_log2 : -INFINITY;
+        s[u][r] = t;
+        mx = fmaxf(mx, t);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+    m = m_new;
+    float psum = 0.f;
+    s16x4 pf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e[r] = exp2f(s[u][r] - m_use);
+        psum += e[r];
+      }
+      const uint32_t w0 = pack_bf16x2(e[0], e[1]);
+      const uint32_t w1 = pack_bf16x2(e[2], e[3]);
+      pf[u] = s16x4{(short)lo16(w0), (short)hi16(w0), (short)lo16(w1), (short)hi16(w1)};
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[t] *= alpha;
+
+    // V^ block -> wave-private LDS, transposed: vt[u][d][key]
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int w = 0; w < D / 32; ++w) {
+        const uint32_t a0 = cur.v[u][0][w], a1 = cur.v[u][1][w], a2 = cur.v[u][2][w], a3 = cur.v[u][3][w];
+        const int d = col * (D / 16) + 2 * w;
+        uint2 even, odd;
+        even.x = lo16(a0) | (lo16(a1) << 16);
+        even.y = lo16(a2) | (lo16(a3) << 16);
+        odd.x = hi16(a0) | (hi16(a1) << 16);
+        odd.y = hi16(a2) | (hi16(a3) << 16);
+        *reinterpret_cast<uint2*>(vt + (u * D + d) * kVtStride + 4 * grp) = even;
+        *reinterpret_cast<uint2*>(vt + (u * D + d + 1) * kVtStride + 4 * grp) = odd;
+      }
+    }
+    // the LDS tile is private to this wave: LDS executes a wave's accesses in
+    // order, so only compiler reordering must be prevented here
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // O^T += V^T . P^T, 16 dims x 16 heads per tile, 16 keys per block
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const uint2 a = *reinterpret_cast<const uint2*>(vt + (u * D + 16 * t + col) * kVtStride + 4 * grp);
+        const s16x4 av = s16x4{(short)lo16(a.x), (short)hi16(a.x), (short)lo16(a.y), (short)hi16(a.y)};
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pf[u], acc[t], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (more) cur = nxt;
+  }
+
+  // combine the four waves of this split
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  __syncthreads();  // every wave is done with its V^ tile before the LDS is reused
+  float* wo = reinterpret_cast<float*>(lds);              // [wave][16 heads][D]
+  float* wml = wo + kDecWaves * 16 * D;                   // [wave][16 heads][2]
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wo[(wave * 16 + col) * D + 16 * t + 4 * grp + r] = acc[t][r];
+  }
+  if (grp == 0) {
+    wml[(wave * 16 + col) * 2 + 0] = m;
+    wml[(wave * 16 + col) * 2 + 1] = l;
+  }
+  __syncthreads();
+  {
+    const int hh = threadIdx.x >> 4;               // head of the chunk
+    const int d0 = (threadIdx.x & 15) * (D / 16);  // D/16 dims per thread
+    float mw[kDecWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      mw[w] = wml[(w * 16 + hh) * 2];
+      M = fmaxf(M, mw[w]);
+    }
+    float sc[kDecWaves];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      sc[w] = M == -INFINITY ? 0.f : exp2f(mw[w] - M);
+      L = fmaf(wml[(w * 16 + hh) * 2 + 1], sc[w], L);
+    }
+    if (hh < nh) {
+      const int64_t slot = ((int64_t)b * p.hq + h0 + hh) * p.splits + split;
+      float* po = p.part_o + slot * D + d0;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) o = fmaf(wo[(w * 16 + hh) * D + d0 + i], sc[w], o);
+        po[i] = o;
+      }
+      if ((threadIdx.x & 15) == 0) {
+        p.part_ml[2 * slot + 0] = M;
+        p.part_ml[2 * slot + 1] = L;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream) {
+  const dim3 grid((unsigned)p.splits, (unsigned)(p.hkv * p.head_chunks), (unsigned)p.batch);
+  if (head_dim == 64)
+    hipLaunchKernelGGL((decode_split_bf16_kernel<64, 2>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_bf16_kernel<128, 2>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

@@ -1,0 +1,85 @@
+// Internal launch parameters and device helpers shared by the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace yoco {
+
+// Everything a kernel needs, by value (kernel argument).
+struct AttnParams {
+  const void* q;
+  void* out;
+  float* lse;
+  const void* k;
+  const void* v;
+  const int64_t* seq_start;
+  const int32_t* seq_len;
+  const int32_t* seq_cap;
+  const int32_t* cu_seqlens;  // prefill only
+  int64_t pool_rows;
+  int64_t total_q;            // prefill: rows of q/out, columns of lse
+  int32_t batch;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;              // hq / hkv
+  float scale_log2;           // scale * log2(e): scores are kept in the base-2 domain
+  // prefill grid
+  int32_t pos_blocks;         // position blocks covering max_q_len
+  // decode split plan
+  int32_t splits;
+  int32_t split_rows;
+  int32_t head_chunks;        // query-head chunks of <= 16 per KV head (decode)
+  float* part_o;              // [B, Hq, splits, D] unnormalised partial outputs
+  float* part_ml;             // [B, Hq, splits, 2] (running max in base 2, sum of weights)
+};
+
+struct AppendParams {
+  void* k;
+  void* v;
+  const void* k_new;
+  const void* v_new;
+  const int64_t* seq_start;
+  int32_t* seq_len;
+  const int32_t* seq_cap;
+  int32_t* overflow;
+  int64_t pool_rows;
+  int32_t row_bytes;          // Hkv * head_dim * element size (multiple of 16)
+};
+
+// Host launchers (one per kernel family); each returns the hipGetLastError code.
+hipError_t launch_kv_append(const AppendParams& p, int batch, hipStream_t stream);
+hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_prefill_f32(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_split_f32(const AttnParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hipStream_t stream);
+
+// Prefill tiling shared between the planner and the kernels.
+constexpr int kPrefillRowsPerWave = 32;
+constexpr int kPrefillWaves = 4;
+// heads of one KV group that one prefill workgroup serves (4, 2 or 1, dividing the group)
+__host__ __device__ inline int prefill_heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+__host__ __device__ inline int prefill_positions_per_wg(int group) {
+  return kPrefillRowsPerWave * (kPrefillWaves / prefill_heads_per_wg(group));
+}
+
+// fp32 prefill: one thread per query row, 64 rows per workgroup
+constexpr int kPrefillF32Rows = 64;
+
+// Readable rows of sequence b: min(seq_len, seq_cap), limited to the pool.
+__device__ __forceinline__ int32_t readable_rows(const int64_t* seq_start, const int32_t* seq_len,
+                                                 const int32_t* seq_cap, int64_t pool_rows, int b,
+                                                 int64_t* start_out) {
+  int64_t s = seq_start[b];
+  int64_t n = seq_len[b];
+  int64_t c = seq_cap[b];
+  if (n > c) n = c;
+  if (s < 0 || s > pool_rows) s = 0, n = 0;
+  if (n > pool_rows - s) n = pool_rows - s;
+  if (n < 0) n = 0;
+  *start_out = s;
+  return (int32_t)n;
+}
+
+}  // namespace yoco

@@ -1,0 +1,40 @@
+// kv_append: one new K^,V^ row per sequence into the shared cache.
+//
+// The new token's row exists before any Cross-Decoder layer reads the cache
+// (page "YOCO", section "Decode：新 token 仍需经过两部分"). One workgroup per
+// sequence copies the row with 16-byte vector stores, then bumps seq_len.
+#include "internal.h"
+
+namespace yoco {
+
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
+  const int b = blockIdx.x;
+  const int64_t start = p.seq_start[b];
+  const int32_t len = p.seq_len[b];
+  const int32_t cap = p.seq_cap[b];
+  const bool ok = len >= 0 && len < cap && start >= 0 && start + len < p.pool_rows;
+  if (!ok) {
+    if (threadIdx.x == 0 && p.overflow != nullptr) p.overflow[0] = 1;
+    return;
+  }
+  const int64_t row = start + len;
+  const int n16 = p.row_bytes / 16;
+  const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(p.k_new) + (int64_t)b * p.row_bytes);
+  const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(p.v_new) + (int64_t)b * p.row_bytes);
+  uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(p.k) + row * p.row_bytes);
+  uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(p.v) + row * p.row_bytes);
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+  // every thread has read seq_len above; the increment comes after all of them
+  __syncthreads();
+  if (threadIdx.x == 0) p.seq_len[b] = len + 1;
+}
+
+hipError_t launch_kv_append(const AppendParams& p, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL(kv_append_kernel, dim3(batch), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

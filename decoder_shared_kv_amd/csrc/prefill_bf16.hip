@@ -1,0 +1,302 @@
+// Prefill: causal cross-attention of every prompt row, bf16 storage, MFMA.
+//
+// Attn_l = softmax(Q^l K^T * scale + M_causal) V^ over the whole prompt (page
+// "YOCO", section "Cross-Decoder", Attn_l equation; causal rule j <= i from
+// section "架构总览"). A dense contraction: both products run on
+// v_mfma_f32_32x32x16_bf16.
+//
+// Workgroup = 4 waves x 32 query rows. The rows of one workgroup belong to one
+// KV head: up to 4 query heads of its group at the same 32 positions (or fewer
+// heads over more positions), so every K^/V^ tile staged in LDS serves all of
+// them. Per 64-key tile and per wave:
+//   S^T[key][query] = K^ . Q^T      A = K^ rows from LDS, B = Q^T in registers
+//   online softmax on S^T           one query per lane pair (lane, lane ^ 32)
+//   O^T[dim][query] += V^T . P^T    B = P^T straight from the S^T registers,
+//                                   A = V^T from an LDS tile stored transposed
+// The accumulator layout of a 32x32 MFMA gives lane l the keys
+// 8*(r/4) + 4*(l/32) + (r%4) of query l%32; taking registers 8c..8c+7 as the
+// B operand of the PV step c means the step's k-slot e of lane half h is key
+// 16c + 8*(e/4) + 4h + (e%4). The V^T tile stores key k at column k with bits
+// 2 and 3 swapped, which makes those eight keys one contiguous 16-byte read.
+// Tiles wholly above the diagonal are never loaded; diagonal tiles are masked.
+// Grid: one workgroup per (position block, sequence, KV head, head chunk),
+// position blocks longest first, and the (sequence, KV head) index varying
+// fastest so that workgroups dispatched round-robin to the 8 XCDs keep one KV
+// head per XCD when there are 4 or 8 of them.
+#include <hip/hip_bf16.h>
+
+#include "internal.h"
+
+namespace yoco {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBN = 64;          // keys per tile
+constexpr int kKPad = 8;         // bf16 padding per K^ row in LDS
+constexpr int kVPad = 8;         // bf16 padding per V^T row in LDS
+
+__device__ __forceinline__ int swap_bits_2_3(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 c = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, c) << 16);
+}
+
+template <int D>
+struct TileRegs {
+  static constexpr int kChunks = (kBN * D / 8 + 255) / 256;   // 16-byte K^ chunks per thread
+  static constexpr int kVBlocks = ((kBN / 4) * (D / 8) + 255) / 256;  // 4-key x 8-dim V^ blocks per thread
+  uint4 k[kChunks];
+  uint4 v[kVBlocks][4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const __bf16* kbase, const __bf16* vbase,
+                                          int64_t row_stride, int key0, int last) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
+    const int c = t + 256 * i;
+    if (c < kBN * D / 8) {
+      int key = key0 + c / (D / 8);
+      key = key < last ? key : last;
+      r.k[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * row_stride + 8 * (c % (D / 8)));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
+    const int c = t + 256 * i;
+    if (c < (kBN / 4) * (D / 8)) {
+      const int kg = c / (D / 8);
+      const int dc = c % (D / 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int key = key0 + 4 * kg + j;
+        key = key < last ? key : last;
+        r.v[i][j] = *reinterpret_cast<const uint4*>(vbase + (int64_t)key * row_stride + 8 * dc);
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __bf16* vts) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
+    const int c = t + 256 * i;
+    if (c < kBN * D / 8)
+      *reinterpret_cast<uint4*>(ks + (c / (D / 8)) * (D + kKPad) + 8 * (c % (D / 8))) = r.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
+    const int c = t + 256 * i;
+    if (c < (kBN / 4) * (D / 8)) {
+      const int kg = c / (D / 8);
+      const int dc = c % (D / 8);
+      const int kcol = swap_bits_2_3(4 * kg);   // 4 consecutive keys stay consecutive
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&r.v[i][0]);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&r.v[i][1]);
+      const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&r.v[i][2]);
+      const uint32_t* a3 = reinterpret_cast<const uint32_t*>(&r.v[i][3]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint2 even, odd;
+        even.x = (a0[w] & 0xffffu) | (a1[w] << 16);
+        even.y = (a2[w] & 0xffffu) | (a3[w] << 16);
+        odd.x = (a0[w] >> 16) | (a1[w] & 0xffff0000u);
+        odd.y = (a2[w] >> 16) | (a3[w] & 0xffff0000u);
+        const int d = 8 * dc + 2 * w;
+        *reinterpret_cast<uint2*>(vts + d * (kBN + kVPad) + kcol) = even;
+        *reinterpret_cast<uint2*>(vts + (d + 1) * (kBN + kVPad) + kcol) = odd;
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 ks_lds[2][kBN * (D + kKPad)];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * (kBN + kVPad)];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int qj = lane & 31;   // query column of this lane in S^T / O^T tiles
+  const int hf = lane >> 5;   // lane half
+
+  const int hpw = prefill_heads_per_wg(p.group);
+  const int ppw = kPrefillWaves / hpw;
+  const int hchunks = p.group / hpw;
+  const int units = p.batch * p.hkv * hchunks;
+  const int unit = blockIdx.x % units;
+  const int rank = blockIdx.x / units;
+  const int hc = unit % hchunks;
+  const int kh = (unit / hchunks) % p.hkv;
+  const int b = unit / (hchunks * p.hkv);
+  const int h = kh * p.group + hc * hpw + wave % hpw;   // this wave's query head
+  const int pbl = wave / hpw;                          // this wave's position block inside the WG
+  const int pos_per_wg = kPrefillRowsPerWave * ppw;
+
+  int64_t start;
+  const int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
+  int64_t q0 = p.cu_seqlens[b];
+  int64_t q1 = p.cu_seqlens[b + 1];
+  if (q1 > p.total_q) q1 = p.total_q;
+  if (q0 < 0 || q0 > q1) return;
+  const int32_t n_q = (int32_t)(q1 - q0);
+  const int32_t offset = n_kv > n_q ? n_kv - n_q : 0;
+
+  const int64_t row_stride = (int64_t)p.hkv * D;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + start * row_stride + (int64_t)kh * D;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + start * row_stride + (int64_t)kh * D;
+  const __bf16* qbase = static_cast<const __bf16*>(p.q);
+
+  for (int pw = p.pos_blocks - 1 - rank; pw >= 0 && pw * pos_per_wg < n_q; pw += p.pos_blocks) {
+    const int r0 = pw * pos_per_wg + pbl * kPrefillRowsPerWave;   // first row of this wave
+    const int wg_last_row = min(n_q, (pw + 1) * pos_per_wg) - 1;
+    const int wg_last_key = min(wg_last_row + offset, n_kv - 1);
+    const int n_tiles = wg_last_key >= 0 ? wg_last_key / kBN + 1 : 0;
+    const bool wave_active = r0 < n_q;
+    const int wave_min_pos = r0 + offset;
+    const int wave_max_pos = min(r0 + kPrefillRowsPerWave, n_q) - 1 + offset;
+    const int my_row = min(r0 + qj, n_q - 1);
+    const int my_pos = r0 + qj + offset;
+
+    // Q^T as the B operand: query my_row, dims 16*kk + 8*hf .. +8
+    bf16x8 qf[D / 16];
+    {
+      const __bf16* qsrc = qbase + ((q0 + (my_row > 0 ? my_row : 0)) * p.hq + h) * D + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qsrc + 16 * kk));
+    }
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+
+    TileRegs<D> regs;
+    if (n_tiles > 0) {
+      load_tile<D>(regs, kbase, vbase, row_stride, 0, n_kv - 1);
+      store_tile<D>(regs, ks_lds[0], vt_lds[0]);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < n_tiles; ++kt) {
+      const int buf = kt & 1;
+      const bool more = kt + 1 < n_tiles;
+      if (more) load_tile<D>(regs, kbase, vbase, row_stride, (kt + 1) * kBN, n_kv - 1);
+      const int key0 = kt * kBN;
+      if (wave_active && key0 <= wave_max_pos) {
+        const __bf16* ks = ks_lds[buf];
+        const __bf16* vts = vt_lds[buf];
+        // S^T = K^ . Q^T for two 32-key blocks
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+          const __bf16* krow = ks + (kb * 32 + qj) * (D + kKPad) + 8 * hf;
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+          }
+        }
+        // base-2 scores; mask keys past this query or past the readable rows
+        const bool need_mask = key0 + kBN - 1 > wave_min_pos || key0 + kBN > n_kv;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float t = s[kb][r] * p.scale_log2;
+            if (need_mask) {
+              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (key > my_pos || key >= n_kv) t = -INFINITY;
+            }
+            s[kb][r] = t;
+            mx = fmaxf(mx, t);
+          }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m - m_use);
+        m = m_new;
+        float psum = 0.f;
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            uint4 w;
+            float e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              e[i] = exp2f(s[kb][8 * c + i] - m_use);
+              psum += e[i];
+            }
+            w.x = pack2(e[0], e[1]);
+            w.y = pack2(e[2], e[3]);
+            w.z = pack2(e[4], e[5]);
+            w.w = pack2(e[6], e[7]);
+            pf[kb][c] = __builtin_bit_cast(bf16x8, w);
+          }
+        }
+        l = l * alpha + psum;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+        // O^T += V^T . P^T
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          const __bf16* vrow = vts + (32 * t + qj) * (kBN + kVPad) + 8 * hf;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + 16 * c);
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][c], acc[t], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (more) store_tile<D>(regs, ks_lds[buf ^ 1], vt_lds[buf ^ 1]);
+      __syncthreads();
+    }
+
+    // normalise and store: lane holds dims 32t + 8*(r/4) + 4*hf + (r%4) of query qj
+    const float l_tot = l + __shfl_xor(l, 32);
+    if (wave_active && r0 + qj < n_q) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* dst = static_cast<__bf16*>(p.out) + ((q0 + r0 + qj) * p.hq + h) * D;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint2 w;
+          w.x = pack2(acc[t][4 * g4 + 0] * inv, acc[t][4 * g4 + 1] * inv);
+          w.y = pack2(acc[t][4 * g4 + 2] * inv, acc[t][4 * g4 + 3] * inv);
+          *reinterpret_cast<uint2*>(dst + 32 * t + 8 * g4 + 4 * hf) = w;
+        }
+      }
+      if (hf == 0 && p.lse != nullptr)
+        p.lse[(int64_t)h * p.total_q + q0 + r0 + qj] =
+            l_tot > 0.f ? (m + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream) {
+  if (head_dim == 64)
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

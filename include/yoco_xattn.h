@@ -1,0 +1,152 @@
+/*
+ * yoco_xattn.h -- C ABI of the shared-KV cross-attention library for MI355X (gfx950).
+ *
+ * The operation: YOCO's Cross-Decoder layers each send their own queries Q^l
+ * against ONE shared pair K^, V^ that the Self-Decoder output produced once
+ * (page "YOCO", zdszero.github.io: section "架构总览" (architecture overview),
+ * equations for K^, V^ and Q^l; section "Cross-Decoder：共享 KV，但不共享 Query",
+ * the Attn_l equation):
+ *
+ *     Attn_l = softmax(Q^l K^T * scale + M_causal) V^
+ *
+ * M_causal lets the query at position i see cache rows j <= i (same page, end of
+ * "架构总览"). Several query heads share one KV head (page "YOCO 深度技术分析",
+ * liuhc.cn, section 2.1, Cross-Decoder bullets): query head h reads KV head
+ * h / (Hq / Hkv). No positional transform is applied inside these calls.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers marked [device] are device (HBM) addresses; [host] are host memory.
+ *  - Tensors are dense, row-major, head_dim contiguous:
+ *      shared cache  K, V   : [pool_rows, Hkv, head_dim]
+ *      prefill queries/out  : [total_q, Hq, head_dim], sequences packed back to back
+ *      decode queries/out   : [batch, Hq, head_dim]
+ *  - Q, K, V, O share one storage dtype (fp32 or bf16); scores, softmax and
+ *    accumulation are fp32; O is rounded once (round-to-nearest-even) on store.
+ *    LSE (natural log of the sum of exp of the scaled scores) is fp32.
+ *  - Every call is asynchronous on `stream` (a hipStream_t, NULL = the null
+ *    stream); nothing is synchronised inside the library. Host-side argument
+ *    checks run before any launch: a call that returns an error launched
+ *    nothing and touched no output.
+ *  - The library allocates and frees nothing and keeps no global state: all
+ *    buffers belong to the caller. Calls are re-entrant.
+ *  - Device-side sequence metadata is clamped, never trusted, for memory
+ *    safety: a sequence's readable rows are seq_start[b] .. seq_start[b] +
+ *    min(seq_len[b], seq_cap[b]) - 1, further limited to the pool. Metadata
+ *    outside these limits yields clamped results, never an out-of-bounds access.
+ *  - Pointers to Q, K, V, O and the appended rows must be 16-byte aligned.
+ */
+#ifndef YOCO_XATTN_H
+#define YOCO_XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  YOCO_OK = 0,
+  YOCO_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or count */
+  YOCO_ERR_UNSUPPORTED = 2,  /* valid but not built: dtype, head_dim */
+  YOCO_ERR_WORKSPACE = 3,    /* workspace missing or smaller than yoco_xattn_workspace_size */
+  YOCO_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError after launch) */
+} yoco_status;
+
+typedef enum { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1 } yoco_dtype;
+
+/* [host] Problem dimensions. */
+typedef struct {
+  int32_t batch;         /* B >= 1: sequences */
+  int32_t num_q_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t dtype;         /* yoco_dtype of Q, K, V, O */
+  float scale;           /* softmax scale, finite; 1/sqrt(head_dim) for the usual d_k reading */
+} yoco_dims;
+
+/* [host] Descriptor of the ONE shared K^,V^ cache read by every layer. */
+typedef struct {
+  void* k;                   /* [device] [pool_rows, Hkv, head_dim] */
+  void* v;                   /* [device] same layout as k */
+  int64_t pool_rows;         /* rows allocated in k and v (bounds every access) */
+  const int64_t* seq_start;  /* [device] [B] first pool row of sequence b */
+  int32_t* seq_len;          /* [device] [B] valid rows of sequence b (kv_append increments) */
+  const int32_t* seq_cap;    /* [device] [B] rows reserved for sequence b */
+} yoco_kv_cache;
+
+/*
+ * yoco_kv_append -- write each sequence's new K^,V^ row into the shared cache.
+ *
+ * Decode order on the pages: the new token passes the Self-Decoder, which yields
+ * its K^,V^ row, before any Cross-Decoder layer reads the cache (page "YOCO",
+ * section "Decode：新 token 仍需经过两部分"). For each b: if seq_len[b] <
+ * seq_cap[b] (and the row lies inside the pool) the row k_new[b], v_new[b] is
+ * copied to pool row seq_start[b] + seq_len[b] and seq_len[b] is incremented;
+ * otherwise nothing of sequence b changes and *overflow_flag is set to 1 (the
+ * flag is never cleared by the library; NULL disables it).
+ *   k_new, v_new  [device] [B, Hkv, head_dim], same dtype as the cache.
+ */
+yoco_status yoco_kv_append(const yoco_dims* dims, const yoco_kv_cache* cache,
+                           const void* k_new, const void* v_new,
+                           int32_t* overflow_flag, void* stream);
+
+/*
+ * yoco_xattn_prefill -- causal cross-attention of every packed query row.
+ *
+ * Sequence b's queries are packed rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of
+ * q. With n = its readable cache rows and m = its query rows, query row r sits
+ * at position r + max(n - m, 0) (r itself when m == n, the full-prompt case)
+ * and attends rows 0 .. that position. Rows of queries whose position has no
+ * readable row (n == 0) get O = 0 and LSE = -inf.
+ *   q          [device] [total_q, Hq, head_dim]
+ *   cu_seqlens_q [device] int32 [B+1], non-decreasing, cu_seqlens_q[B] <= total_q
+ *   max_q_len  [host] sizing hint for the grid (longer sequences are still
+ *              computed in full, by more passes)
+ *   total_q    [host] rows of q, out and columns of lse
+ *   out        [device] [total_q, Hq, head_dim]
+ *   lse        [device] fp32 [Hq, total_q] or NULL
+ * No workspace is needed.
+ */
+yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache,
+                               const void* q, const int32_t* cu_seqlens_q,
+                               int32_t max_q_len, int64_t total_q,
+                               void* out, float* lse, void* stream);
+
+/*
+ * yoco_xattn_decode -- one query per sequence against the whole shared cache.
+ *
+ * Call after yoco_kv_append: sequence b's query sits at position seq_len[b]-1
+ * and attends rows 0 .. seq_len[b]-1 (every Cross-Decoder layer re-reads the
+ * shared cache: page "YOCO", section "KV Cache 与计算量分析", cost table).
+ * Rows are split across workgroups (split-K) and merged by log-sum-exp.
+ *   q          [device] [B, Hq, head_dim]
+ *   max_kv_len [host] sizing hint for the split plan; longer sequences are still
+ *              computed in full (the last split takes the remainder)
+ *   out        [device] [B, Hq, head_dim]; a sequence with no rows gets O = 0
+ *   lse        [device] fp32 [B, Hq] or NULL; -inf for a sequence with no rows
+ *   workspace  [device] >= yoco_xattn_workspace_size(dims, max_kv_len) bytes,
+ *              16-byte aligned; contents need no initialisation and are
+ *              overwritten. Calls that share a workspace must be serialised.
+ */
+yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache,
+                              const void* q, int32_t max_kv_len,
+                              void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len. */
+yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes);
+
+/* [host] Number of row splits yoco_xattn_decode uses (for reports and tests). */
+yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len,
+                                     int32_t* splits, int32_t* rows_per_split);
+
+/* Static description of a status code; never NULL. */
+const char* yoco_status_string(yoco_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* YOCO_XATTN_H */

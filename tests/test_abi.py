@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments on the host, before any launch (no GPU needed: no call here reaches
+a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decoder_shared_kv_amd as dk
+from decoder_shared_kv_amd import xattn as X
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(yoco_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dk.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(X.EXPORTS) <= set(names), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.yoco_status_string(s)
+    assert lib.yoco_status_string(99) == b"unknown status"
+
+
+FAKE = 1 << 20  # a 16-byte aligned fake device address; never dereferenced on the host
+
+
+def _cache(**kw):
+    d = dict(k=FAKE, v=FAKE, pool_rows=100, seq_start=FAKE, seq_len=FAKE, seq_cap=FAKE)
+    d.update(kw)
+    return X.KvCache(**d)
+
+
+def _dims(**kw):
+    d = dict(batch=1, num_q_heads=4, num_kv_heads=2, head_dim=128, dtype=1, scale=0.1)
+    d.update(kw)
+    return X.Dims(**d)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(batch=0), 1), (dict(num_q_heads=3, num_kv_heads=2), 1), (dict(num_kv_heads=0), 1),
+    (dict(head_dim=96), 2), (dict(dtype=7), 2), (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+])
+def test_dims_rejected_everywhere(lib, bad, code):
+    dims, cache = _dims(**bad), _cache()
+    ws = ctypes.c_size_t(0)
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 10, ctypes.byref(ws)) == code
+    assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None) == code
+    assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, FAKE, None, FAKE, 1 << 30,
+                                 None) == code
+    assert lib.yoco_kv_append(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, None, None) == code
+
+
+@pytest.mark.parametrize("bad", [dict(k=None), dict(v=None), dict(k=FAKE + 2), dict(seq_start=None),
+                                 dict(seq_len=None), dict(seq_cap=None), dict(pool_rows=-1), dict(seq_start=FAKE + 4)])
+def test_cache_rejected(lib, bad):
+    dims, cache = _dims(), _cache(**bad)
+    assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None) == 1
+    assert lib.yoco_kv_append(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, None, None) == 1
+    assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, FAKE, None, FAKE, 1 << 30,
+                                 None) == 1
+
+
+def test_null_structs(lib):
+    cache, dims = _cache(), _dims()
+    assert lib.yoco_xattn_prefill(None, ctypes.byref(cache), FAKE, FAKE, 1, 1, FAKE, None, None) == 1
+    assert lib.yoco_xattn_prefill(ctypes.byref(dims), None, FAKE, FAKE, 1, 1, FAKE, None, None) == 1
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5, None) == 1
+
+
+def test_prefill_argument_checks(lib):
+    dims, cache = _dims(), _cache()
+    P = lambda *a: lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    assert P(None, FAKE, 10, 10, FAKE, None, None) == 1          # q
+    assert P(FAKE, None, 10, 10, FAKE, None, None) == 1          # cu_seqlens
+    assert P(FAKE, FAKE, 10, 10, None, None, None) == 1          # out
+    assert P(FAKE + 8, FAKE, 10, 10, FAKE, None, None) == 1      # misaligned q
+    assert P(FAKE, FAKE, 10, 10, FAKE + 8, None, None) == 1      # misaligned out
+    assert P(FAKE, FAKE, 10, 10, FAKE, FAKE + 2, None) == 1      # misaligned lse
+    assert P(FAKE, FAKE, -1, 10, FAKE, None, None) == 1          # max_q_len
+    assert P(FAKE, FAKE, 10, -5, FAKE, None, None) == 1          # total_q
+    assert P(FAKE, FAKE, 10, 0, FAKE, None, None) == 0           # nothing to do, nothing launched
+
+
+def test_decode_workspace_checks(lib):
+    dims, cache = _dims(batch=2), _cache()
+    need = ctypes.c_size_t(0)
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5000, ctypes.byref(need)) == 0
+    assert need.value > 0
+    D = lambda *a: lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    assert D(FAKE, 5000, FAKE, None, None, need.value, None) == 3
+    assert D(FAKE, 5000, FAKE, None, FAKE, need.value - 1, None) == 3
+    assert D(FAKE, 5000, FAKE, None, FAKE + 4, need.value, None) == 3
+    assert D(FAKE, -1, FAKE, None, FAKE, need.value, None) == 1
+    assert D(None, 5000, FAKE, None, FAKE, need.value, None) == 1
+    assert D(FAKE, 5000, FAKE + 8, None, FAKE, need.value, None) == 1
+
+
+def test_append_argument_checks(lib):
+    dims, cache = _dims(), _cache()
+    A = lambda *a: lib.yoco_kv_append(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    assert A(None, FAKE, None, None) == 1
+    assert A(FAKE, None, None, None) == 1
+    assert A(FAKE + 2, FAKE, None, None) == 1
+    assert A(FAKE, FAKE, FAKE + 1, None) == 1
+
+
+def test_split_plan():
+    # decode: 8 x 131072 rows, Hkv=2 -> 16 (sequence, KV head) units, ~1024 workgroups in total
+    s, r = dk.decode_splits(8, 16, 2, 128, X.torch.bfloat16, 131072)
+    assert s * r >= 131072 and r % 128 == 0 and 512 <= s * 16 <= 2048
+    s, r = dk.decode_splits(1, 16, 2, 128, X.torch.bfloat16, 1048640)
+    assert s * r >= 1048640 and (s - 1) * r < 1048640 and 512 <= s * 2 <= 2048
+    s, r = dk.decode_splits(1, 4, 1, 64, X.torch.float32, 1)
+    assert s == 1 and r == 128
+    s, r = dk.decode_splits(3, 32, 1, 128, X.torch.bfloat16, 0)
+    assert s == 1
