@@ -1,0 +1,341 @@
+"""Benchmark of the shared-KV cross-attention hot path on one MI355X.
+
+One step = one pass of the whole path over seeded synthetic input resident in HBM:
+  * prefill: 16 Cross-Decoder layers, each a causal prefill of its own queries
+    [32768, 16 heads, 128] against one shared K^,V^ [32768, 4 KV heads, 128] (bf16);
+  * decode: one appended K^,V^ row per sequence, then 16 layer queries against the
+    shared cache of 8 sequences x 131072 rows, 2 KV heads, 16 query heads (bf16).
+`value` is the prefill rate (algorithmic causal flops 4*d*Hq*N(N+1)/2 per layer
+over the measured time); the decode rate (K^ and V^ bytes read once per call plus
+Q and O, over the measured call time) is reported beside it in `decode`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --workload decode_1m     (long-context decode, 64 steps x 16 layers)
+       python bench.py --copy-probe             (plain copy kernel of known size, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "decode HBM GB/s (% peak) @128K-1M; prefill TFLOP/s (% MFMA peak) @32K"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops(lens, hq, d):
+    return sum(4.0 * d * hq * n * (n + 1) / 2.0 for n in lens)
+
+
+def decode_bytes(lens, hkv, hq, d, elem=2):
+    return sum(n * hkv * d * elem * 2 for n in lens) + len(lens) * hq * d * elem * 2
+
+
+def make_prefill(dk, synth, dev, w):
+    c = synth.make_prefill_case(list(w.seq_lens), w.q_heads, w.kv_heads, w.head_dim, w.layers, w.dtype, w.seed,
+                                w.value_std)
+    cache = dk.SharedKV(c.k_pool.to(dev), c.v_pool.to(dev), c.seq_start.to(dev), c.seq_len.to(dev), c.seq_cap.to(dev))
+    qs = [q.to(dev) for q in c.q]
+    return c, cache, qs
+
+
+def make_decode(dk, synth, dev, w, extra_steps):
+    steps = max(w.decode_steps, 1)
+    c = synth.make_decode_case(list(w.seq_lens), w.q_heads, w.kv_heads, w.head_dim, w.layers, steps, w.dtype,
+                               w.seed, w.value_std, cap_extra=extra_steps)
+    cache = dk.SharedKV(c.k_pool.to(dev), c.v_pool.to(dev), c.seq_start.to(dev), c.seq_len.to(dev).clone(),
+                        c.seq_cap.to(dev))
+    return c, cache
+
+
+def cpu_baseline(synth, oracle, w, budget_s=12.0):
+    """The oracle as it stands, on the host cores, over a bounded sample of the
+    prefill workload: blocks of the last query rows of layer 0, all heads."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    c = synth.make_prefill_case(list(w.seq_lens), w.q_heads, w.kv_heads, w.head_dim, 1, w.dtype, w.seed,
+                                w.value_std)
+    q = synth.to_f64(c.q[0])
+    k = synth.to_f32(c.k_pool)
+    v = synth.to_f32(c.v_pool)
+    n = int(w.seq_lens[0])
+    done_rows = []
+    flops = 0.0
+    t0 = time.perf_counter()
+    hi = n
+    while time.perf_counter() - t0 < budget_s and hi > 0:
+        lo = max(0, hi - 128)
+        rows = list(range(lo, hi))
+        oracle.prefill_ref(q, k, v, c.seq_start.numpy(), c.seq_len.numpy(), c.cu_seqlens.numpy(), c.scale,
+                           rows={0: rows})
+        flops += sum(4.0 * w.head_dim * w.q_heads * (r + 1) for r in rows)
+        done_rows.append((lo, hi))
+        hi = lo
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, prefill layer 0 of the 32K workload, query rows "
+                      f"{done_rows[-1][0]}..{n - 1} (all {w.q_heads} heads), {dt:.1f} s; "
+                      f"rate = causal flops of those rows / time"}
+
+
+def copy_probe(torch, dev):
+    """A plain device copy of known size: its FETCH_SIZE/WRITE_SIZE calibrate the counters."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="default", choices=["default", "decode_1m", "ragged"])
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--skip", default="", help="comma list of modes to leave out: prefill,decode (profiling only)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decoder_shared_kv_amd as dk
+    import synth
+
+    dev = torch.device("cuda:0")
+    dk.load_library()
+    if args.copy_probe:
+        copy_probe(torch, dev)
+        return
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} CUs={props.multi_processor_count}")
+
+    if args.workload == "decode_1m":
+        return bench_decode_1m(args, torch, dk, synth, dev)
+    if args.workload == "ragged":
+        return bench_ragged(args, torch, dk, synth, dev)
+
+    skip = set(x for x in args.skip.split(",") if x)
+    wp = synth.WORKLOADS["prefill_32k"]
+    wd = synth.WORKLOADS["decode_128k"]
+    t = time.perf_counter()
+    pc, pcache, qs = make_prefill(dk, synth, dev, wp)
+    dc, dcache = make_decode(dk, synth, dev, wd, args.steps + args.warmup + 1)
+    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
+    n = int(wp.seq_lens[0])
+    cu = pc.cu_seqlens.to(dev)
+    out_p = torch.empty_like(qs[0])
+    lse_p = torch.empty(wp.q_heads, n, device=dev, dtype=torch.float32)
+    max_dec = int(dc.seq_len.max()) + args.steps + args.warmup + 1
+    ws = dk.alloc_workspace(dcache, wd.q_heads, max_dec)
+    out_d = torch.empty(wd.batch, wd.q_heads, wd.head_dim, device=dev, dtype=torch.bfloat16)
+    lse_d = torch.empty(wd.batch, wd.q_heads, device=dev, dtype=torch.float32)
+    qd = dc.q[0].to(dev)               # [layers, B, Hq, d]
+    kn = dc.k_new[0].to(dev)
+    vn = dc.v_new[0].to(dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    lens_now = [int(x) for x in dc.seq_len]
+
+    def step(record):
+        if "prefill" not in skip:
+            if record:
+                ev[0].record()
+            for layer in range(wp.layers):
+                dk.xattn_prefill(pcache, qs[layer], cu, n, pc.scale, out=out_p, lse=lse_p)
+            if record:
+                ev[1].record()
+        if "decode" not in skip:
+            dk.kv_append(dcache, kn, vn, flag)
+            if record:
+                ev[2].record()
+            cur = max(lens_now) + 1
+            for layer in range(wd.layers):
+                dk.xattn_decode(dcache, qd[layer], cur, dc.scale, ws, out=out_d, lse=lse_d)
+            if record:
+                ev[3].record()
+        for b in range(len(lens_now)):
+            lens_now[b] += 1 if "decode" not in skip else 0
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    pre_ms, dec_ms = 0.0, 0.0
+    dec_bytes = 0.0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        if "decode" not in skip:
+            dec_bytes += wd.layers * decode_bytes(lens_now, wd.kv_heads, wd.q_heads, wd.head_dim)
+        ev[3 if "decode" not in skip else 1].synchronize()
+        if "prefill" not in skip:
+            pre_ms += ev[0].elapsed_time(ev[1])
+        if "decode" not in skip:
+            dec_ms += ev[2].elapsed_time(ev[3])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(flag.item()) == 0, "append overflowed"
+
+    flops_layer = prefill_flops(wp.seq_lens, wp.q_heads, wp.head_dim)
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1)/sqrt(128) bf16)",
+           "config": {"workload": "prefill: B=1 N=32768 Hq=16 Hkv=4 d=128 causal, 16 layers on one shared K,V; "
+                                  "decode: B=8 N=131072 Hq=16 Hkv=2 d=128, append + 16 layers",
+                      "global_batch": 1, "seq_len": n, "parallelism": "none (1 GPU)"}}
+    if "prefill" not in skip:
+        layer_s = pre_ms / 1e3 / (args.steps * wp.layers)
+        tflops = flops_layer / layer_s / 1e12
+        res.update({"value": tflops, "unit": "TFLOP/s"})
+        res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tflops / BF16_DENSE_PEAK_TFLOPS, "traffic": None,
+                           "kernel": "prefill_bf16_kernel<128>", "avg_launch_ms": layer_s * 1e3,
+                           "algorithmic_per_launch": flops_layer}
+    if "decode" not in skip:
+        calls = args.steps * wd.layers
+        call_s = dec_ms / 1e3 / calls
+        gbs = dec_bytes / (dec_ms / 1e3) / 1e9
+        res["decode"] = {"value": gbs, "unit": "GB/s", "avg_call_ms": call_s * 1e3,
+                         "algorithmic_bytes_per_call": dec_bytes / calls,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                      "kernel": "decode_split_bf16_kernel<128,2> + decode_merge_kernel"}}
+        if "prefill" in skip:
+            res.update({"value": gbs, "unit": "GB/s"})
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(synth, oracle, wp)
+    print(json.dumps(res), flush=True)
+
+
+def bench_decode_1m(args, torch, dk, synth, dev):
+    w = synth.WORKLOADS["decode_1m"]
+    t = time.perf_counter()
+    c, cache = make_decode(dk, synth, dev, w, 0)
+    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
+    q = c.q.to(dev)
+    kn, vn = c.k_new.to(dev), c.v_new.to(dev)
+    max_len = int(c.seq_len.max()) + w.decode_steps
+    ws = dk.alloc_workspace(cache, w.q_heads, max_len)
+    out = torch.empty(w.batch, w.q_heads, w.head_dim, device=dev, dtype=torch.bfloat16)
+    lse = torch.empty(w.batch, w.q_heads, device=dev, dtype=torch.float32)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    # warm-up on a copy of the metadata so that the timed run starts from the initial cache
+    saved = cache.seq_len.clone()
+    for _ in range(min(args.warmup, 2)):
+        dk.kv_append(cache, kn[0], vn[0], flag)
+        dk.xattn_decode(cache, q[0, 0], max_len, c.scale, ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    cache.seq_len.copy_(saved)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lens = [int(x) for x in c.seq_len]
+    nbytes = 0.0
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(w.decode_steps):
+        dk.kv_append(cache, kn[s], vn[s], flag)
+        lens = [x + 1 for x in lens]
+        for layer in range(w.layers):
+            dk.xattn_decode(cache, q[s, layer], max_len, c.scale, ws, out=out, lse=lse)
+            nbytes += decode_bytes(lens, w.kv_heads, w.q_heads, w.head_dim)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    assert int(flag.item()) == 0
+    gbs = nbytes / (ms / 1e3) / 1e9
+    calls = w.decode_steps * w.layers
+    print(json.dumps({
+        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": w.decode_steps, "warmup": 2,
+        "ms_per_step": wall * 1e3 / w.decode_steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1)/sqrt(128) bf16)",
+        "config": {"workload": "decode: B=1 N=1048576 (+64 appends) Hq=16 Hkv=2 d=128, 64 steps x 16 layers",
+                   "global_batch": 1, "seq_len": 1048576, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "decode_split_bf16_kernel<128,2> + decode_merge_kernel",
+                     "avg_call_ms": ms / calls, "algorithmic_bytes_per_call": nbytes / calls},
+        "total_ms": ms}), flush=True)
+
+
+def bench_ragged(args, torch, dk, synth, dev):
+    w = synth.WORKLOADS["ragged"]
+    t = time.perf_counter()
+    pc = synth.make_prefill_case(list(w.seq_lens), w.q_heads, w.kv_heads, w.head_dim, 1, w.dtype, w.seed,
+                                 w.value_std, cap_extra=w.decode_steps)
+    dc = synth.make_decode_case([1] * w.batch, w.q_heads, w.kv_heads, w.head_dim, 1, w.decode_steps, w.dtype,
+                                w.seed, w.value_std)
+    cache = dk.SharedKV(pc.k_pool.to(dev), pc.v_pool.to(dev), pc.seq_start.to(dev), pc.seq_len.to(dev).clone(),
+                        pc.seq_cap.to(dev))
+    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
+    q = pc.q[0].to(dev)
+    cu = pc.cu_seqlens.to(dev)
+    maxq = max(w.seq_lens)
+    out = torch.empty_like(q)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(args.warmup):
+        dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out)
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(args.steps):
+        dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out)
+    e[1].record()
+    torch.cuda.synchronize()
+    pre_ms = e[0].elapsed_time(e[1]) / args.steps
+    flops = prefill_flops(w.seq_lens, w.q_heads, w.head_dim)
+    qd = dc.q.to(dev)
+    kn, vn = dc.k_new.to(dev), dc.v_new.to(dev)
+    ws = dk.alloc_workspace(cache, w.q_heads, maxq + w.decode_steps)
+    outd = torch.empty(w.batch, w.q_heads, w.head_dim, device=dev, dtype=torch.bfloat16)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    lens = list(w.seq_lens)
+    nbytes = 0.0
+    e[2].record()
+    for s in range(w.decode_steps):
+        dk.kv_append(cache, kn[s], vn[s], flag)
+        lens = [x + 1 for x in lens]
+        dk.xattn_decode(cache, qd[s, 0], maxq + w.decode_steps, pc.scale, ws, out=outd)
+        nbytes += decode_bytes(lens, w.kv_heads, w.q_heads, w.head_dim)
+    e[3].record()
+    torch.cuda.synchronize()
+    dms = e[2].elapsed_time(e[3])
+    assert int(flag.item()) == 0
+    tfl = flops / (pre_ms / 1e3) / 1e12
+    gbs = nbytes / (dms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": METRIC, "value": tfl, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": pre_ms + dms / w.decode_steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1)/sqrt(128) bf16)",
+        "config": {"workload": f"ragged: 16 seqs L={list(w.seq_lens)} Hq=32 Hkv=8 d=128; prefill + 32 decode steps",
+                   "global_batch": 16, "seq_len": maxq, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": tfl, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tfl / BF16_DENSE_PEAK_TFLOPS, "traffic": None, "avg_launch_ms": pre_ms},
+        "decode": {"value": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "avg_call_ms": dms / w.decode_steps}}),
+        flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,16 +47,30 @@ int head_chunks(const yoco_dims* d) {
   return (g + 15) / 16;
 }
 
-void plan_decode(const yoco_dims* d, int32_t max_kv_len, int32_t* splits, int32_t* rows) {
+int64_t decode_split_target(const yoco_dims* d) {
   const int64_t units = (int64_t)d->batch * d->num_kv_heads * head_chunks(d);
-  int64_t want = (kDecodeTargetWgs + units - 1) / units;
-  if (want < 1) want = 1;
-  int64_t n = max_kv_len > 0 ? max_kv_len : 1;
+  const int64_t want = (kDecodeTargetWgs + units - 1) / units;
+  return want < 1 ? 1 : want;
+}
+
+// rows per split: a multiple of the workgroup's iteration, at least one iteration;
+// never more than decode_split_target splits
+void plan_decode(const yoco_dims* d, int32_t max_kv_len, int32_t* splits, int32_t* rows) {
+  const int64_t want = decode_split_target(d);
+  const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
   int64_t r = (n + want - 1) / want;
   r = (r + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter * kDecodeKeysPerIter;
-  if (r < kDecodeKeysPerIter) r = kDecodeKeysPerIter;
   *rows = (int32_t)r;
   *splits = (int32_t)((n + r - 1) / r);
+}
+
+// An upper bound of the splits of every plan with max_kv_len <= n (monotone in n),
+// so a workspace sized for n serves every shorter call.
+int32_t decode_split_bound(const yoco_dims* d, int32_t max_kv_len) {
+  const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
+  const int64_t by_rows = (n + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter;
+  const int64_t want = decode_split_target(d);
+  return (int32_t)(by_rows < want ? by_rows : want);
 }
 
 size_t decode_ml_offset(const yoco_dims* d, int32_t splits) {
@@ -161,9 +175,7 @@ yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len,
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
   if (bytes == nullptr || max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
-  int32_t splits, rows;
-  plan_decode(dims, max_kv_len, &splits, &rows);
-  *bytes = decode_workspace(dims, splits);
+  *bytes = decode_workspace(dims, decode_split_bound(dims, max_kv_len));
   return YOCO_OK;
 }
 

@@ -40,9 +40,16 @@ def errors(out, ref):
 
 
 def check(out, ref, dtype, discriminating=False, what=""):
-    """Raise AssertionError unless out matches ref to the bounds for dtype."""
+    """Raise AssertionError unless out matches ref to the bounds for dtype.
+
+    Acceptance inputs (discriminating=False): the max-abs bound. Discriminating
+    inputs (unit-spread logits, outputs of magnitude ~1 or more): the row-relative
+    bound, which scales with the output like bf16 rounding does; fp32 keeps the
+    max-abs bound as well.
+    """
     e = errors(out, ref)
-    assert e["max_abs"] <= MAX_ABS[dtype], f"{what}: max-abs {e['max_abs']:.3e} > {MAX_ABS[dtype]}"
+    if not discriminating or dtype == "f32":
+        assert e["max_abs"] <= MAX_ABS[dtype], f"{what}: max-abs {e['max_abs']:.3e} > {MAX_ABS[dtype]}"
     if discriminating:
         assert e["row_rel"] <= ROW_REL[dtype], f"{what}: row-relative {e['row_rel']:.3e} > {ROW_REL[dtype]}"
     return e

@@ -135,3 +135,13 @@ def test_split_plan():
     assert s == 1 and r == 128
     s, r = dk.decode_splits(3, 32, 1, 128, X.torch.bfloat16, 0)
     assert s == 1
+
+
+def test_workspace_is_monotone_in_max_kv_len():
+    import torch
+    prev = 0
+    for n in [0, 1, 127, 128, 129, 1000, 4096, 65535, 131071, 131072, 131085, 131200, 1 << 20, (1 << 20) + 64]:
+        ws = dk.workspace_size(8, 16, 2, 128, torch.bfloat16, n)
+        s, r = dk.decode_splits(8, 16, 2, 128, torch.bfloat16, n)
+        assert ws >= prev and ws >= 8 * 16 * s * (128 + 2) * 4, (n, ws, s)
+        prev = ws
