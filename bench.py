@@ -140,24 +140,26 @@ def main():
     wp = synth.WORKLOADS["prefill_32k"]
     wd = synth.WORKLOADS["decode_128k"]
     t = time.perf_counter()
-    pc, pcache, qs = make_prefill(dk, synth, dev, wp)
-    dc, dcache = make_decode(dk, synth, dev, wd, args.steps + args.warmup + 1)
-    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
     n = int(wp.seq_lens[0])
-    cu = pc.cu_seqlens.to(dev)
-    out_p = torch.empty_like(qs[0])
-    lse_p = torch.empty(wp.q_heads, n, device=dev, dtype=torch.float32)
-    max_dec = int(dc.seq_len.max()) + args.steps + args.warmup + 1
-    ws = dk.alloc_workspace(dcache, wd.q_heads, max_dec)
-    out_d = torch.empty(wd.batch, wd.q_heads, wd.head_dim, device=dev, dtype=torch.bfloat16)
-    lse_d = torch.empty(wd.batch, wd.q_heads, device=dev, dtype=torch.float32)
-    qd = dc.q[0].to(dev)               # [layers, B, Hq, d]
-    kn = dc.k_new[0].to(dev)
-    vn = dc.v_new[0].to(dev)
+    if "prefill" not in skip:
+        pc, pcache, qs = make_prefill(dk, synth, dev, wp)
+        cu = pc.cu_seqlens.to(dev)
+        out_p = torch.empty_like(qs[0])
+        lse_p = torch.empty(wp.q_heads, n, device=dev, dtype=torch.float32)
+    if "decode" not in skip:
+        dc, dcache = make_decode(dk, synth, dev, wd, args.steps + args.warmup + 1)
+        max_dec = int(dc.seq_len.max()) + args.steps + args.warmup + 1
+        ws = dk.alloc_workspace(dcache, wd.q_heads, max_dec)
+        out_d = torch.empty(wd.batch, wd.q_heads, wd.head_dim, device=dev, dtype=torch.bfloat16)
+        lse_d = torch.empty(wd.batch, wd.q_heads, device=dev, dtype=torch.float32)
+        qd = dc.q[0].to(dev)               # [layers, B, Hq, d]
+        kn = dc.k_new[0].to(dev)
+        vn = dc.v_new[0].to(dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    lens_now = [int(x) for x in dc.seq_len]
+    lens_now = [int(x) for x in dc.seq_len] if "decode" not in skip else []
 
     def step(record):
         if "prefill" not in skip:

@@ -26,7 +26,7 @@ yoco_status check_dims(const yoco_dims* d) {
   if (d == nullptr) return YOCO_ERR_INVALID_ARG;
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return YOCO_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return YOCO_ERR_INVALID_ARG;
-  if (!std::isfinite(d->scale)) return YOCO_ERR_INVALID_ARG;
+  if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return YOCO_ERR_INVALID_ARG;
   if (d->dtype != YOCO_DTYPE_F32 && d->dtype != YOCO_DTYPE_BF16) return YOCO_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return YOCO_ERR_UNSUPPORTED;
   return YOCO_OK;

@@ -13,49 +13,81 @@ namespace yoco {
 
 namespace {
 
+constexpr int kMergeThreads = 256;
+
+// One workgroup per (sequence, query head). The split maxima are reduced by the
+// whole workgroup; then 256/D groups of D threads each sum a strided subset of
+// the splits (independent loads in flight), and the groups are added in LDS.
 template <int D, typename OutT>
-__global__ __launch_bounds__(D) void decode_merge_kernel(AttnParams p) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams p) {
+  constexpr int G = kMergeThreads / D;
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float part_o[G][D];
+  __shared__ float part_l[G];
   const int bh = blockIdx.x;  // b * hq + h
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const int64_t base = (int64_t)bh * p.splits;
   const float* ml = p.part_ml + 2 * base;
+
   float mx = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, ml[2 * s]);
-  float lsum = 0.f, o = 0.f;
-  if (mx != -INFINITY) {
+  for (int s = tid; s < p.splits; s += kMergeThreads) mx = fmaxf(mx, ml[2 * s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
+
+  const int g = tid / D;
+  const int d = tid % D;
+  float o = 0.f, lsum = 0.f;
+  if (M != -INFINITY) {
     const float* po = p.part_o + base * D + d;
-    for (int s = 0; s < p.splits; ++s) {
+#pragma unroll 8
+    for (int s = g; s < p.splits; s += G) {
       const float ms = ml[2 * s];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - mx);
+      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
       lsum = fmaf(ml[2 * s + 1], w, lsum);
       o = fmaf(po[(int64_t)s * D], w, o);
     }
   }
-  const float res = lsum > 0.f ? o / lsum : 0.f;
-  OutT* dst = static_cast<OutT*>(p.out) + (int64_t)bh * D + d;
-  if constexpr (sizeof(OutT) == 2) {
-    *dst = __float2bfloat16(res);
-  } else {
-    *dst = res;
+  part_o[g][d] = o;
+  if (d == 0) part_l[g] = lsum;
+  __syncthreads();
+  if (tid < D) {
+    float os = 0.f, ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      os += part_o[i][tid];
+      ls += part_l[i];
+    }
+    const float res = ls > 0.f ? os / ls : 0.f;
+    OutT* dst = static_cast<OutT*>(p.out) + (int64_t)bh * D + tid;
+    if constexpr (sizeof(OutT) == 2) {
+      *dst = __float2bfloat16(res);
+    } else {
+      *dst = res;
+    }
+    if (tid == 0 && p.lse != nullptr) p.lse[bh] = ls > 0.f ? (M + log2f(ls)) * 0.6931471805599453f : -INFINITY;
   }
-  if (d == 0 && p.lse != nullptr) p.lse[bh] = lsum > 0.f ? (mx + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hipStream_t stream) {
   const dim3 grid((unsigned)(p.batch * p.hq));
+  const dim3 block(kMergeThreads);
   if (dtype == 1) {
     if (head_dim == 64)
-      hipLaunchKernelGGL((decode_merge_kernel<64, __hip_bfloat16>), grid, dim3(64), 0, stream, p);
+      hipLaunchKernelGGL((decode_merge_kernel<64, __hip_bfloat16>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<128, __hip_bfloat16>), grid, dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((decode_merge_kernel<128, __hip_bfloat16>), grid, block, 0, stream, p);
   } else {
     if (head_dim == 64)
-      hipLaunchKernelGGL((decode_merge_kernel<64, float>), grid, dim3(64), 0, stream, p);
+      hipLaunchKernelGGL((decode_merge_kernel<64, float>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<128, float>), grid, dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((decode_merge_kernel<128, float>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

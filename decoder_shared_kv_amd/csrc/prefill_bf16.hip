@@ -33,6 +33,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 64;          // keys per tile
 constexpr int kKPad = 8;         // bf16 padding per K^ row in LDS
@@ -83,6 +84,10 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const __bf16* kbase, c
   }
 }
 
+// XOR swizzle of the 16-byte units of a V^T row: rows d and d+8 land in different
+// banks when 16 lanes store 16 consecutive 8-dim blocks of one key group.
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 3) & 7; }
+
 template <int D>
 __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __bf16* vts) {
   const int t = threadIdx.x;
@@ -110,9 +115,86 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __b
         even.y = (a2[w] & 0xffffu) | (a3[w] << 16);
         odd.x = (a0[w] >> 16) | (a1[w] & 0xffff0000u);
         odd.y = (a2[w] >> 16) | (a3[w] & 0xffff0000u);
-        const int d = 8 * dc + 2 * w;
-        *reinterpret_cast<uint2*>(vts + d * (kBN + kVPad) + kcol) = even;
-        *reinterpret_cast<uint2*>(vts + (d + 1) * (kBN + kVPad) + kcol) = odd;
+        const int d = 8 * dc + 2 * w;   // d and d + 1 share d >> 3
+        const int col = (((kcol >> 3) ^ vt_swz(d)) << 3) | (kcol & 7);
+        *reinterpret_cast<uint2*>(vts + d * (kBN + kVPad) + col) = even;
+        *reinterpret_cast<uint2*>(vts + (d + 1) * (kBN + kVPad) + col) = odd;
+      }
+    }
+  }
+}
+
+// Running-max slack (base 2): the O accumulator is rescaled only when a tile's
+// max exceeds the reference by more than this, so P <= 2^8 between rescales.
+constexpr float kRescaleSlack = 8.0f;
+
+// One 64-key tile for one wave: S^T = K^ Q^T, online softmax, O^T += V^T P^T.
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_step(const __bf16* ks, const __bf16* vts, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&acc)[D / 32], float& m, float& l, int key0, int my_pos,
+                                          int n_kv, float c, int qj, int hf) {
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16{};
+    const __bf16* krow = ks + (kb * 32 + qj) * (D + kKPad) + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (MASK) {
+        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key > my_pos || key >= n_kv) s[kb][r] = -INFINITY;
+      }
+      mx = fmaxf(mx, s[kb][r]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mx2 = mx * c;  // c > 0: the max commutes with the scale
+  if (__builtin_amdgcn_ballot_w64(mx2 > m + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(m, mx2);
+    const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+  }
+  const float neg_m = m == -INFINITY ? 0.f : -m;
+  bf16x8 pf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i], c, neg_m));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i + 1], c, neg_m));
+        w[i] = pack2(e0, e1);
+        l += e0 + e1;   // fp32 sum of the unrounded weights keeps the LSE fp32-accurate
+      }
+      pf[kb][cc] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int d = 32 * t + qj;
+    const __bf16* vrow = vts + d * (kBN + kVPad);
+    const int swz = vt_swz(d);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int unit = 4 * kb + 2 * cc + hf;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + ((unit ^ swz) << 3));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][cc], acc[t], 0, 0, 0);
       }
     }
   }
@@ -140,6 +222,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
   const int h = kh * p.group + hc * hpw + wave % hpw;   // this wave's query head
   const int pbl = wave / hpw;                          // this wave's position block inside the WG
   const int pos_per_wg = kPrefillRowsPerWave * ppw;
+  const float c = p.scale_log2;
 
   int64_t start;
   const int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
@@ -163,13 +246,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
     const bool wave_active = r0 < n_q;
     const int wave_min_pos = r0 + offset;
     const int wave_max_pos = min(r0 + kPrefillRowsPerWave, n_q) - 1 + offset;
+    // tiles [0, full_tiles) are visible to every row of the wave: no mask
+    const int full_tiles = min((wave_min_pos + 1) / kBN, n_kv / kBN);
     const int my_row = min(r0 + qj, n_q - 1);
     const int my_pos = r0 + qj + offset;
 
     // Q^T as the B operand: query my_row, dims 16*kk + 8*hf .. +8
     bf16x8 qf[D / 16];
     {
-      const __bf16* qsrc = qbase + ((q0 + (my_row > 0 ? my_row : 0)) * p.hq + h) * D + 8 * hf;
+      const __bf16* qsrc = qbase + ((q0 + my_row) * p.hq + h) * D + 8 * hf;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qsrc + 16 * kk));
     }
@@ -191,101 +276,50 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
       if (more) load_tile<D>(regs, kbase, vbase, row_stride, (kt + 1) * kBN, n_kv - 1);
       const int key0 = kt * kBN;
       if (wave_active && key0 <= wave_max_pos) {
-        const __bf16* ks = ks_lds[buf];
-        const __bf16* vts = vt_lds[buf];
-        // S^T = K^ . Q^T for two 32-key blocks
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = f32x16{};
-          const __bf16* krow = ks + (kb * 32 + qj) * (D + kKPad) + 8 * hf;
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-          }
-        }
-        // base-2 scores; mask keys past this query or past the readable rows
-        const bool need_mask = key0 + kBN - 1 > wave_min_pos || key0 + kBN > n_kv;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float t = s[kb][r] * p.scale_log2;
-            if (need_mask) {
-              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-              if (key > my_pos || key >= n_kv) t = -INFINITY;
-            }
-            s[kb][r] = t;
-            mx = fmaxf(mx, t);
-          }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m - m_use);
-        m = m_new;
-        float psum = 0.f;
-        bf16x8 pf[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            uint4 w;
-            float e[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              e[i] = exp2f(s[kb][8 * c + i] - m_use);
-              psum += e[i];
-            }
-            w.x = pack2(e[0], e[1]);
-            w.y = pack2(e[2], e[3]);
-            w.z = pack2(e[4], e[5]);
-            w.w = pack2(e[6], e[7]);
-            pf[kb][c] = __builtin_bit_cast(bf16x8, w);
-          }
-        }
-        l = l * alpha + psum;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-        // O^T += V^T . P^T
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const __bf16* vrow = vts + (32 * t + qj) * (kBN + kVPad) + 8 * hf;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + 16 * c);
-              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][c], acc[t], 0, 0, 0);
-            }
-          }
-        }
+        if (kt < full_tiles)
+          tile_step<D, false>(ks_lds[buf], vt_lds[buf], qf, acc, m, l, key0, my_pos, n_kv, c, qj, hf);
+        else
+          tile_step<D, true>(ks_lds[buf], vt_lds[buf], qf, acc, m, l, key0, my_pos, n_kv, c, qj, hf);
       }
       if (more) store_tile<D>(regs, ks_lds[buf ^ 1], vt_lds[buf ^ 1]);
       __syncthreads();
     }
 
-    // normalise and store: lane holds dims 32t + 8*(r/4) + 4*hf + (r%4) of query qj
+    // Epilogue: normalise, stage the wave's 32 x D output tile in LDS (the K^
+    // tiles are no longer read), then store whole rows with 16-byte writes.
     const float l_tot = l + __shfl_xor(l, 32);
-    if (wave_active && r0 + qj < n_q) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      __bf16* dst = static_cast<__bf16*>(p.out) + ((q0 + r0 + qj) * p.hq + h) * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    constexpr int kOStride = D + 8;
+    __bf16* ot = &ks_lds[0][0] + wave * (kPrefillRowsPerWave * kOStride);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
+    for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          uint2 w;
-          w.x = pack2(acc[t][4 * g4 + 0] * inv, acc[t][4 * g4 + 1] * inv);
-          w.y = pack2(acc[t][4 * g4 + 2] * inv, acc[t][4 * g4 + 3] * inv);
-          *reinterpret_cast<uint2*>(dst + 32 * t + 8 * g4 + 4 * hf) = w;
-        }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint2 w;
+        w.x = pack2(acc[t][4 * g4 + 0] * inv, acc[t][4 * g4 + 1] * inv);
+        w.y = pack2(acc[t][4 * g4 + 2] * inv, acc[t][4 * g4 + 3] * inv);
+        *reinterpret_cast<uint2*>(ot + qj * kOStride + 32 * t + 8 * g4 + 4 * hf) = w;
       }
-      if (hf == 0 && p.lse != nullptr)
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (wave_active) {
+      __bf16* obase = static_cast<__bf16*>(p.out);
+#pragma unroll
+      for (int i = 0; i < kPrefillRowsPerWave * (D / 8) / 64; ++i) {
+        const int ci = lane + 64 * i;
+        const int row = ci / (D / 8);
+        const int c8 = ci % (D / 8);
+        if (r0 + row < n_q)
+          *reinterpret_cast<uint4*>(obase + ((q0 + r0 + row) * p.hq + h) * D + 8 * c8) =
+              *reinterpret_cast<const uint4*>(ot + row * kOStride + 8 * c8);
+      }
+      if (hf == 0 && p.lse != nullptr && r0 + qj < n_q)
         p.lse[(int64_t)h * p.total_q + q0 + r0 + qj] =
             l_tot > 0.f ? (m + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     }
+    __syncthreads();  // the output staging area is the next pass's K^ tile buffer
   }
 }
 

@@ -63,7 +63,7 @@ typedef struct {
   int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */
   int32_t head_dim;      /* 64 or 128 */
   int32_t dtype;         /* yoco_dtype of Q, K, V, O */
-  float scale;           /* softmax scale, finite; 1/sqrt(head_dim) for the usual d_k reading */
+  float scale;           /* softmax scale, finite and > 0; 1/sqrt(head_dim) for the usual d_k reading */
 } yoco_dims;
 
 /* [host] Descriptor of the ONE shared K^,V^ cache read by every layer. */

@@ -60,6 +60,7 @@ def _dims(**kw):
 @pytest.mark.parametrize("bad,code", [
     (dict(batch=0), 1), (dict(num_q_heads=3, num_kv_heads=2), 1), (dict(num_kv_heads=0), 1),
     (dict(head_dim=96), 2), (dict(dtype=7), 2), (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+    (dict(scale=0.0), 1), (dict(scale=-0.5), 1),
 ])
 def test_dims_rejected_everywhere(lib, bad, code):
     dims, cache = _dims(**bad), _cache()
