@@ -158,9 +158,12 @@ __device__ __forceinline__ void tile_step(const __bf16* ks, const __bf16* vts, c
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float mx2 = mx * c;  // c > 0: the max commutes with the scale
-  if (__builtin_amdgcn_ballot_w64(mx2 > m + kRescaleSlack) != 0) {
-    const float m_new = fmaxf(m, mx2);
-    const float alpha = __builtin_amdgcn_exp2f(m - (m_new == -INFINITY ? 0.f : m_new));
+  const bool grow = mx2 > m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    // only the lanes whose own max grew move their reference: every row's
+    // arithmetic stays independent of the other rows in the wave
+    const float m_new = grow ? mx2 : m;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;  // exp2(-inf) = 0 on the first tile
     m = m_new;
     l *= alpha;
 #pragma unroll
