@@ -319,7 +319,7 @@ def bench_ragged(args, torch, dk, synth, dev):
     for s in range(w.decode_steps):
         dk.kv_append(cache, kn[s], vn[s], flag)
         lens = [x + 1 for x in lens]
-        dk.xattn_decode(cache, qd[s, 0], maxq + w.decode_steps, pc.scale, ws, out=outd)
+        dk.xattn_decode(cache, qd[s, 0], maxq + w.decode_steps, pc.scale, ws, out=outd, total_kv_len=sum(lens))
         nbytes += decode_bytes(lens, w.kv_heads, w.q_heads, w.head_dim)
     e[3].record()
     torch.cuda.synchronize()

@@ -14,8 +14,14 @@ namespace {
 using yoco::AttnParams;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kDecodeKeysPerIter = 128;  // rows one decode workgroup consumes per iteration
-constexpr int kDecodeTargetWgs = 1024;   // split-K target: ~4 workgroups per CU
+#ifndef YOCO_DEC_U
+#define YOCO_DEC_U 2
+#endif
+#ifndef YOCO_DECODE_TARGET_WGS
+#define YOCO_DECODE_TARGET_WGS 1024
+#endif
+constexpr int kDecodeKeysPerIter = 4 * 16 * YOCO_DEC_U;  // rows one decode workgroup consumes per iteration
+constexpr int kDecodeTargetWgs = YOCO_DECODE_TARGET_WGS;  // split-K target
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -47,30 +53,36 @@ int head_chunks(const yoco_dims* d) {
   return (g + 15) / 16;
 }
 
-int64_t decode_split_target(const yoco_dims* d) {
-  const int64_t units = (int64_t)d->batch * d->num_kv_heads * head_chunks(d);
-  const int64_t want = (kDecodeTargetWgs + units - 1) / units;
-  return want < 1 ? 1 : want;
+// Split plan: rows per split are sized so that the (sequence, KV head, head
+// chunk, split) workgroups holding rows number about kDecodeTargetWgs, counting
+// the rows of every sequence (total_kv_len, at least max_kv_len); a multiple of
+// one workgroup iteration, at least one. The splits cover max_kv_len.
+int64_t rows_per_split(const yoco_dims* d, int32_t max_kv_len, int64_t total_kv_len) {
+  const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
+  int64_t total = total_kv_len > 0 ? total_kv_len : (int64_t)d->batch * n;
+  if (total < n) total = n;
+  const int64_t per_row = (int64_t)d->num_kv_heads * head_chunks(d);
+  int64_t r = (total * per_row + kDecodeTargetWgs - 1) / kDecodeTargetWgs;
+  r = (r + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter * kDecodeKeysPerIter;
+  return r < kDecodeKeysPerIter ? kDecodeKeysPerIter : r;
 }
 
-// rows per split: a multiple of the workgroup's iteration, at least one iteration;
-// never more than decode_split_target splits
-void plan_decode(const yoco_dims* d, int32_t max_kv_len, int32_t* splits, int32_t* rows) {
-  const int64_t want = decode_split_target(d);
+void plan_decode(const yoco_dims* d, int32_t max_kv_len, int64_t total_kv_len, int32_t* splits, int32_t* rows) {
   const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
-  int64_t r = (n + want - 1) / want;
-  r = (r + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter * kDecodeKeysPerIter;
+  const int64_t r = rows_per_split(d, max_kv_len, total_kv_len);
   *rows = (int32_t)r;
   *splits = (int32_t)((n + r - 1) / r);
 }
 
-// An upper bound of the splits of every plan with max_kv_len <= n (monotone in n),
-// so a workspace sized for n serves every shorter call.
+// An upper bound of the splits of every plan with max_kv_len <= n and any
+// total_kv_len (monotone in n): rows >= n * per_row / target and rows >= one
+// iteration, so splits <= min(ceil(target / per_row), ceil(n / iteration)).
 int32_t decode_split_bound(const yoco_dims* d, int32_t max_kv_len) {
   const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
   const int64_t by_rows = (n + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter;
-  const int64_t want = decode_split_target(d);
-  return (int32_t)(by_rows < want ? by_rows : want);
+  const int64_t per_row = (int64_t)d->num_kv_heads * head_chunks(d);
+  const int64_t by_target = (kDecodeTargetWgs + per_row - 1) / per_row;
+  return (int32_t)(by_rows < by_target ? by_rows : by_target);
 }
 
 size_t decode_ml_offset(const yoco_dims* d, int32_t splits) {
@@ -149,9 +161,10 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
     const int ppw = yoco::prefill_positions_per_wg(p.group);
     const int64_t units = (int64_t)dims->batch * dims->num_kv_heads * (p.group / yoco::prefill_heads_per_wg(p.group));
     const int64_t blocks = (len + ppw - 1) / ppw;
-    if (blocks * units > INT32_MAX) return YOCO_ERR_UNSUPPORTED;
+    if (blocks * units > INT32_MAX / 2 || units > INT32_MAX) return YOCO_ERR_UNSUPPORTED;
     p.pos_blocks = (int32_t)blocks;
-    err = yoco::launch_prefill_bf16(p, dims->head_dim, (int)(blocks * units), static_cast<hipStream_t>(stream));
+    const int64_t grid = yoco::prefill_grid((int)units, (int)blocks);
+    err = yoco::launch_prefill_bf16(p, dims->head_dim, (int)grid, static_cast<hipStream_t>(stream));
   } else {
     const int64_t units = (int64_t)dims->batch * dims->num_q_heads;
     const int64_t blocks = (len + yoco::kPrefillF32Rows - 1) / yoco::kPrefillF32Rows;
@@ -162,12 +175,12 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
   return err == hipSuccess ? YOCO_OK : YOCO_ERR_HIP;
 }
 
-yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len, int32_t* splits,
-                                     int32_t* rows_per_split) {
+yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len, int64_t total_kv_len,
+                                     int32_t* splits, int32_t* rows_per_split) {
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
-  if (splits == nullptr || rows_per_split == nullptr || max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
-  plan_decode(dims, max_kv_len, splits, rows_per_split);
+  if (splits == nullptr || rows_per_split == nullptr || max_kv_len < 0 || total_kv_len < 0) return YOCO_ERR_INVALID_ARG;
+  plan_decode(dims, max_kv_len, total_kv_len, splits, rows_per_split);
   return YOCO_OK;
 }
 
@@ -180,7 +193,7 @@ yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len,
 }
 
 yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
-                              int32_t max_kv_len, void* out, float* lse, void* workspace,
+                              int32_t max_kv_len, int64_t total_kv_len, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream) {
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
@@ -188,9 +201,9 @@ yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache,
   if (st != YOCO_OK) return st;
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return YOCO_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned4(lse)) return YOCO_ERR_INVALID_ARG;
-  if (max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
+  if (max_kv_len < 0 || total_kv_len < 0) return YOCO_ERR_INVALID_ARG;
   int32_t splits, rows;
-  plan_decode(dims, max_kv_len, &splits, &rows);
+  plan_decode(dims, max_kv_len, total_kv_len, &splits, &rows);
   const size_t need = decode_workspace(dims, splits);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return YOCO_ERR_WORKSPACE;
   AttnParams p = base_params(dims, cache);

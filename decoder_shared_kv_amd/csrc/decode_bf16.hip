@@ -16,7 +16,8 @@
 //    small wave-private LDS tile to become the A operand (V^T);
 //  * online softmax in the base-2 domain, per lane, with two cross-lane max
 //    reductions per iteration; the partial (max, sum, unnormalised O) of the
-//    split is merged by decode_merge.
+//    split is merged by decode_merge;
+//  * nontemporal 16-byte loads: the cache is streamed once per call.
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
@@ -28,8 +29,42 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Tuning knobs (measured on MI355X at 8 x 131072 and 1 x 1048576 rows): two
+// 16-key blocks per wave and iteration, no register double buffer (the freed
+// registers buy occupancy, which keeps more loads in flight), nontemporal loads.
+#ifndef YOCO_DEC_U
+#define YOCO_DEC_U 2
+#endif
+#ifndef YOCO_DEC_PREFETCH
+#define YOCO_DEC_PREFETCH 0
+#endif
+#ifndef YOCO_DEC_NT
+#define YOCO_DEC_NT 1
+#endif
 
 constexpr int kDecWaves = 4;
+
+// The cache is streamed once per call and is far larger than the 256 MB
+// Infinity Cache: nontemporal loads keep it from evicting useful lines.
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+#if YOCO_DEC_NT
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+__device__ __forceinline__ uint2 stream_load8(const void* p) {
+#if YOCO_DEC_NT
+  const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(t.x, t.y);
+#else
+  return *reinterpret_cast<const uint2*>(p);
+#endif
+}
 constexpr int kVtStride = 20;  // 16 keys + 4 pad (bf16 elements) per transposed V^ row
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -56,19 +91,19 @@ __device__ __forceinline__ void dec_load(DecRegs<D, U>& r, const __bf16* kbase, 
   for (int u = 0; u < U; ++u) {
     int key = base + 16 * u + col;
     key = key < last ? key : last;
-    const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)key * row_stride + 8 * grp);
+    const __bf16* src = kbase + (int64_t)key * row_stride + 8 * grp;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) r.k[u][kk] = src[kk * 4];  // 32 dims = 4 uint4 apart
+    for (int kk = 0; kk < D / 32; ++kk) r.k[u][kk] = stream_load16(src + 32 * kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int vkey = base + 16 * u + 4 * grp + i;
       vkey = vkey < last ? vkey : last;
       const __bf16* vs = vbase + (int64_t)vkey * row_stride + col * (D / 16);
       if constexpr (D == 128) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vs);
+        const uint4 x = stream_load16(vs);
         r.v[u][i][0] = x.x; r.v[u][i][1] = x.y; r.v[u][i][2] = x.z; r.v[u][i][3] = x.w;
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(vs);
+        const uint2 x = stream_load8(vs);
         r.v[u][i][0] = x.x; r.v[u][i][1] = x.y;
       }
     }
@@ -127,11 +162,17 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
   constexpr int kStep = kDecWaves * U * 16;
   int base = j0 + wave * U * 16;
   DecRegs<D, U> cur;
+#if YOCO_DEC_PREFETCH
   if (base < j1) dec_load<D, U>(cur, kbase, vbase, row_stride, base, j1 - 1, lane);
+#endif
   for (; base < j1; base += kStep) {
+#if YOCO_DEC_PREFETCH
     DecRegs<D, U> nxt;
     const bool more = base + kStep < j1;
     if (more) dec_load<D, U>(nxt, kbase, vbase, row_stride, base + kStep, j1 - 1, lane);
+#else
+    dec_load<D, U>(cur, kbase, vbase, row_stride, base, j1 - 1, lane);
+#endif
 
     // S^T = K^ . Q^T, 16 keys x 16 heads per block
     f32x4 s[U];
@@ -213,7 +254,9 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#if YOCO_DEC_PREFETCH
     if (more) cur = nxt;
+#endif
   }
 
   // combine the four waves of this split
@@ -272,9 +315,9 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
 hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid((unsigned)p.splits, (unsigned)(p.hkv * p.head_chunks), (unsigned)p.batch);
   if (head_dim == 64)
-    hipLaunchKernelGGL((decode_split_bf16_kernel<64, 2>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_bf16_kernel<64, YOCO_DEC_U>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_split_bf16_kernel<128, 2>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_bf16_kernel<128, YOCO_DEC_U>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

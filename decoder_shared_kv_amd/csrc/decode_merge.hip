@@ -14,17 +14,20 @@ namespace yoco {
 namespace {
 
 constexpr int kMergeThreads = 256;
+constexpr int kMergeDims = 16;                            // dims per workgroup
+constexpr int kMergeGroups = kMergeThreads / kMergeDims;  // split groups per workgroup
 
-// One workgroup per (sequence, query head). The split maxima are reduced by the
-// whole workgroup; then 256/D groups of D threads each sum a strided subset of
-// the splits (independent loads in flight), and the groups are added in LDS.
+// One workgroup per (sequence, query head, 16-dim chunk): many workgroups even
+// for one long sequence. The split maxima are reduced by the whole workgroup;
+// then 16 groups of 16 threads each sum a strided subset of the splits (with
+// independent loads in flight), and the groups are added in LDS.
 template <int D, typename OutT>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams p) {
-  constexpr int G = kMergeThreads / D;
   __shared__ float red[kMergeThreads / 64];
-  __shared__ float part_o[G][D];
-  __shared__ float part_l[G];
+  __shared__ float part_o[kMergeGroups][kMergeDims];
+  __shared__ float part_l[kMergeGroups];
   const int bh = blockIdx.x;  // b * hq + h
+  const int d0 = blockIdx.y * kMergeDims;
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)bh * p.splits;
   const float* ml = p.part_ml + 2 * base;
@@ -39,13 +42,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams 
 #pragma unroll
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
 
-  const int g = tid / D;
-  const int d = tid % D;
+  const int g = tid / kMergeDims;
+  const int d = tid % kMergeDims;
   float o = 0.f, lsum = 0.f;
   if (M != -INFINITY) {
-    const float* po = p.part_o + base * D + d;
+    const float* po = p.part_o + base * D + d0 + d;
 #pragma unroll 8
-    for (int s = g; s < p.splits; s += G) {
+    for (int s = g; s < p.splits; s += kMergeGroups) {
       const float ms = ml[2 * s];
       const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
       lsum = fmaf(ml[2 * s + 1], w, lsum);
@@ -55,28 +58,29 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams 
   part_o[g][d] = o;
   if (d == 0) part_l[g] = lsum;
   __syncthreads();
-  if (tid < D) {
+  if (tid < kMergeDims) {
     float os = 0.f, ls = 0.f;
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
+    for (int i = 0; i < kMergeGroups; ++i) {
       os += part_o[i][tid];
       ls += part_l[i];
     }
     const float res = ls > 0.f ? os / ls : 0.f;
-    OutT* dst = static_cast<OutT*>(p.out) + (int64_t)bh * D + tid;
+    OutT* dst = static_cast<OutT*>(p.out) + (int64_t)bh * D + d0 + tid;
     if constexpr (sizeof(OutT) == 2) {
       *dst = __float2bfloat16(res);
     } else {
       *dst = res;
     }
-    if (tid == 0 && p.lse != nullptr) p.lse[bh] = ls > 0.f ? (M + log2f(ls)) * 0.6931471805599453f : -INFINITY;
+    if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr)
+      p.lse[bh] = ls > 0.f ? (M + log2f(ls)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.batch * p.hq));
+  const dim3 grid((unsigned)(p.batch * p.hq), (unsigned)(head_dim / kMergeDims));
   const dim3 block(kMergeThreads);
   if (dtype == 1) {
     if (head_dim == 64)

@@ -64,6 +64,36 @@ __host__ __device__ inline int prefill_positions_per_wg(int group) {
   return kPrefillRowsPerWave * (kPrefillWaves / prefill_heads_per_wg(group));
 }
 
+// XCD-affine order of the prefill grid. Workgroup i runs on XCD i % 8. With U
+// units of P position blocks each:
+//  * U % 8 == 0: XCD x takes units x, x+8, ... one after the other, each unit's
+//    blocks longest first (grid U*P);
+//  * 8 % U == 0: the 8/U XCDs sharing unit x % U take its blocks round-robin
+//    (grid 8 * ceil(P / (8/U)); blocks past P are empty);
+//  * otherwise: unit-major order (grid U*P).
+constexpr int kXcds = 8;
+__host__ __device__ inline int64_t prefill_grid(int units, int pos_blocks) {
+  if (units % kXcds != 0 && kXcds % units == 0) {
+    const int per = kXcds / units;
+    return (int64_t)kXcds * ((pos_blocks + per - 1) / per);
+  }
+  return (int64_t)units * pos_blocks;
+}
+__host__ __device__ inline void prefill_schedule(int bid, int units, int pos_blocks, int* unit, int* rank) {
+  if (units % kXcds == 0) {
+    const int x = bid % kXcds, j = bid / kXcds;
+    *unit = x + kXcds * (j / pos_blocks);
+    *rank = j % pos_blocks;
+  } else if (kXcds % units == 0) {
+    const int x = bid % kXcds, j = bid / kXcds;
+    *unit = x % units;
+    *rank = x / units + (kXcds / units) * j;
+  } else {
+    *unit = bid / pos_blocks;
+    *rank = bid % pos_blocks;
+  }
+}
+
 // fp32 prefill: one thread per query row, 64 rows per workgroup
 constexpr int kPrefillF32Rows = 64;
 

@@ -19,10 +19,12 @@
 // 16c + 8*(e/4) + 4h + (e%4). The V^T tile stores key k at column k with bits
 // 2 and 3 swapped, which makes those eight keys one contiguous 16-byte read.
 // Tiles wholly above the diagonal are never loaded; diagonal tiles are masked.
-// Grid: one workgroup per (position block, sequence, KV head, head chunk),
-// position blocks longest first, and the (sequence, KV head) index varying
-// fastest so that workgroups dispatched round-robin to the 8 XCDs keep one KV
-// head per XCD when there are 4 or 8 of them.
+// Grid: one workgroup per (unit, position block), a unit being a (sequence, KV
+// head, head chunk); position blocks run longest first. Workgroups reach the 8
+// XCDs round-robin by index, and prefill_schedule (internal.h) orders them so
+// that each XCD walks whole units (or a share of one unit's blocks when there
+// are fewer than 8 units): the workgroups resident on one XCD then stream the
+// same K^/V^ rows through that XCD's L2.
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
@@ -217,8 +219,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
   const int ppw = kPrefillWaves / hpw;
   const int hchunks = p.group / hpw;
   const int units = p.batch * p.hkv * hchunks;
-  const int unit = blockIdx.x % units;
-  const int rank = blockIdx.x / units;
+  int unit, rank;
+  prefill_schedule(blockIdx.x, units, p.pos_blocks, &unit, &rank);
   const int hc = unit % hchunks;
   const int kh = (unit / hchunks) % p.hkv;
   const int b = unit / (hchunks * p.hkv);
@@ -226,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
   const int pbl = wave / hpw;                          // this wave's position block inside the WG
   const int pos_per_wg = kPrefillRowsPerWave * ppw;
   const float c = p.scale_log2;
+  if (rank >= p.pos_blocks) return;
 
   int64_t start;
   const int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);

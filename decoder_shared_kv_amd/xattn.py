@@ -60,9 +60,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     cache_p = ctypes.POINTER(KvCache)
     lib.yoco_kv_append.argtypes = [dims_p, cache_p, P, P, P, P]
     lib.yoco_xattn_prefill.argtypes = [dims_p, cache_p, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P]
-    lib.yoco_xattn_decode.argtypes = [dims_p, cache_p, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+    lib.yoco_xattn_decode.argtypes = [dims_p, cache_p, P, ctypes.c_int32, ctypes.c_int64, P, P, P, ctypes.c_size_t,
+                                      P]
     lib.yoco_xattn_workspace_size.argtypes = [dims_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
-    lib.yoco_xattn_decode_splits.argtypes = [dims_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+    lib.yoco_xattn_decode_splits.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                              ctypes.POINTER(ctypes.c_int32)]
     lib.yoco_status_string.argtypes = [ctypes.c_int]
     lib.yoco_status_string.restype = ctypes.c_char_p
@@ -148,11 +149,13 @@ def workspace_size(batch: int, q_heads: int, kv_heads: int, head_dim: int, dtype
     return int(n.value)
 
 
-def decode_splits(batch: int, q_heads: int, kv_heads: int, head_dim: int, dtype: torch.dtype, max_kv_len: int):
+def decode_splits(batch: int, q_heads: int, kv_heads: int, head_dim: int, dtype: torch.dtype, max_kv_len: int,
+                  total_kv_len: int = 0):
     lib = load_library()
     dims = make_dims(batch, q_heads, kv_heads, head_dim, dtype, 1.0)
     s, r = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(lib.yoco_xattn_decode_splits(ctypes.byref(dims), int(max_kv_len), ctypes.byref(s), ctypes.byref(r)),
+    _check(lib.yoco_xattn_decode_splits(ctypes.byref(dims), int(max_kv_len), int(total_kv_len), ctypes.byref(s),
+                                        ctypes.byref(r)),
            "yoco_xattn_decode_splits")
     return int(s.value), int(r.value)
 
@@ -164,15 +167,20 @@ def alloc_workspace(cache: SharedKV, q_heads: int, max_kv_len: int) -> torch.Ten
 
 
 def xattn_decode(cache: SharedKV, q: torch.Tensor, max_kv_len: int, scale: float, workspace: torch.Tensor,
-                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
-    """One query per sequence (q [B, Hq, d]) against the whole shared cache; returns out."""
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None,
+                 total_kv_len: int = 0):
+    """One query per sequence (q [B, Hq, d]) against the whole shared cache; returns out.
+
+    max_kv_len / total_kv_len are the host-side sizing hints of the split plan
+    (the longest sequence's rows, all sequences' rows; 0 = B * max_kv_len)."""
     lib = load_library()
     batch, hq, _ = q.shape
     if out is None:
         out = torch.empty_like(q)
     dims = _dims_for(cache, hq, scale, batch)
     desc = cache.descriptor()
-    _check(lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), int(max_kv_len), _ptr(out),
+    _check(lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), int(max_kv_len), int(total_kv_len),
+                                 _ptr(out),
                                  _ptr(lse), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                  _stream(stream)), "yoco_xattn_decode")
     return out

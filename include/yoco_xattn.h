@@ -122,8 +122,12 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
  * shared cache: page "YOCO", section "KV Cache 与计算量分析", cost table).
  * Rows are split across workgroups (split-K) and merged by log-sum-exp.
  *   q          [device] [B, Hq, head_dim]
- *   max_kv_len [host] sizing hint for the split plan; longer sequences are still
- *              computed in full (the last split takes the remainder)
+ *   max_kv_len [host] sizing hint for the split plan: the longest sequence's
+ *              rows; longer sequences are still computed in full (the last split
+ *              takes the remainder)
+ *   total_kv_len [host] sizing hint: the rows of all sequences together, or 0
+ *              for B * max_kv_len; rows per split are chosen so that about a
+ *              thousand workgroups hold rows, whatever the length mix
  *   out        [device] [B, Hq, head_dim]; a sequence with no rows gets O = 0
  *   lse        [device] fp32 [B, Hq] or NULL; -inf for a sequence with no rows
  *   workspace  [device] >= yoco_xattn_workspace_size(dims, max_kv_len) bytes,
@@ -131,16 +135,18 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
  *              overwritten. Calls that share a workspace must be serialised.
  */
 yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache,
-                              const void* q, int32_t max_kv_len,
+                              const void* q, int32_t max_kv_len, int64_t total_kv_len,
                               void* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
 
-/* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len. */
+/* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len (any
+ * total_kv_len, any smaller max_kv_len). */
 yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes);
 
 /* [host] Number of row splits yoco_xattn_decode uses (for reports and tests). */
 yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len,
-                                     int32_t* splits, int32_t* rows_per_split);
+                                     int64_t total_kv_len, int32_t* splits,
+                                     int32_t* rows_per_split);
 
 /* Static description of a status code; never NULL. */
 const char* yoco_status_string(yoco_status status);

@@ -28,13 +28,18 @@ def run_prefill(case: synth.PrefillCase, layer: int = 0, cache: dk.SharedKV = No
     return f64(out), (lse.cpu().numpy().astype(np.float64) if with_lse else None)
 
 
-def run_decode(cache: dk.SharedKV, q: torch.Tensor, scale: float, max_kv_len: int = None, with_lse: bool = True):
+def run_decode(cache: dk.SharedKV, q: torch.Tensor, scale: float, max_kv_len: int = None, with_lse: bool = True,
+               total_kv_len: int = None):
+    """Decode through the library; the split-plan hints default to the true
+    longest and total row counts (pass total_kv_len=0 for the B x max plan)."""
     q = q.to(DEV).contiguous()
     if max_kv_len is None:
         max_kv_len = int(cache.seq_len.max().item())
+    if total_kv_len is None:
+        total_kv_len = int(cache.seq_len.sum().item())
     ws = dk.alloc_workspace(cache, q.shape[1], max_kv_len)
     lse = torch.full(q.shape[:2], float("nan"), device=DEV) if with_lse else None
-    out = dk.xattn_decode(cache, q, max_kv_len, scale, ws, lse=lse)
+    out = dk.xattn_decode(cache, q, max_kv_len, scale, ws, lse=lse, total_kv_len=total_kv_len)
     torch.cuda.synchronize()
     return f64(out), (lse.cpu().numpy().astype(np.float64) if with_lse else None)
 

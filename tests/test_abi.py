@@ -67,7 +67,7 @@ def test_dims_rejected_everywhere(lib, bad, code):
     ws = ctypes.c_size_t(0)
     assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 10, ctypes.byref(ws)) == code
     assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None) == code
-    assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, FAKE, None, FAKE, 1 << 30,
+    assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, 0, FAKE, None, FAKE, 1 << 30,
                                  None) == code
     assert lib.yoco_kv_append(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, None, None) == code
 
@@ -78,7 +78,7 @@ def test_cache_rejected(lib, bad):
     dims, cache = _dims(), _cache(**bad)
     assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None) == 1
     assert lib.yoco_kv_append(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, None, None) == 1
-    assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, FAKE, None, FAKE, 1 << 30,
+    assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, 0, FAKE, None, FAKE, 1 << 30,
                                  None) == 1
 
 
@@ -109,12 +109,13 @@ def test_decode_workspace_checks(lib):
     assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5000, ctypes.byref(need)) == 0
     assert need.value > 0
     D = lambda *a: lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
-    assert D(FAKE, 5000, FAKE, None, None, need.value, None) == 3
-    assert D(FAKE, 5000, FAKE, None, FAKE, need.value - 1, None) == 3
-    assert D(FAKE, 5000, FAKE, None, FAKE + 4, need.value, None) == 3
-    assert D(FAKE, -1, FAKE, None, FAKE, need.value, None) == 1
-    assert D(None, 5000, FAKE, None, FAKE, need.value, None) == 1
-    assert D(FAKE, 5000, FAKE + 8, None, FAKE, need.value, None) == 1
+    assert D(FAKE, 5000, 0, FAKE, None, None, need.value, None) == 3
+    assert D(FAKE, 5000, 0, FAKE, None, FAKE, need.value - 1, None) == 3
+    assert D(FAKE, 5000, 0, FAKE, None, FAKE + 4, need.value, None) == 3
+    assert D(FAKE, -1, 0, FAKE, None, FAKE, need.value, None) == 1
+    assert D(FAKE, 5000, -3, FAKE, None, FAKE, need.value, None) == 1
+    assert D(None, 5000, 0, FAKE, None, FAKE, need.value, None) == 1
+    assert D(FAKE, 5000, 0, FAKE + 8, None, FAKE, need.value, None) == 1
 
 
 def test_append_argument_checks(lib):
@@ -130,7 +131,7 @@ def test_split_plan():
     # decode: 8 x 131072 rows, Hkv=2 -> 16 (sequence, KV head) units, ~1024 workgroups in total
     s, r = dk.decode_splits(8, 16, 2, 128, X.torch.bfloat16, 131072)
     assert s * r >= 131072 and r % 128 == 0 and 512 <= s * 16 <= 2048
-    s, r = dk.decode_splits(1, 16, 2, 128, X.torch.bfloat16, 1048640)
+    s, r = dk.decode_splits(1, 16, 2, 128, X.torch.bfloat16, 1048640, 1048640)
     assert s * r >= 1048640 and (s - 1) * r < 1048640 and 512 <= s * 2 <= 2048
     s, r = dk.decode_splits(1, 4, 1, 64, X.torch.float32, 1)
     assert s == 1 and r == 128
@@ -138,11 +139,25 @@ def test_split_plan():
     assert s == 1
 
 
-def test_workspace_is_monotone_in_max_kv_len():
+def test_workspace_is_monotone_and_bounds_every_plan():
     import torch
     prev = 0
     for n in [0, 1, 127, 128, 129, 1000, 4096, 65535, 131071, 131072, 131085, 131200, 1 << 20, (1 << 20) + 64]:
         ws = dk.workspace_size(8, 16, 2, 128, torch.bfloat16, n)
-        s, r = dk.decode_splits(8, 16, 2, 128, torch.bfloat16, n)
-        assert ws >= prev and ws >= 8 * 16 * s * (128 + 2) * 4, (n, ws, s)
+        assert ws >= prev, (n, ws)
         prev = ws
+        for total in [0, n, 2 * n + 5, 8 * n, 3 * n // 2]:
+            for m in {n, n // 2, max(n - 1, 0)}:
+                s, r = dk.decode_splits(8, 16, 2, 128, torch.bfloat16, m, total)
+                assert s * r >= max(m, 1) and ws >= 8 * 16 * s * (128 + 2) * 4, (n, m, total, s, r, ws)
+
+
+def test_split_plan_counts_all_rows():
+    import torch
+    # 16 ragged sequences: rows per split follow the total, not B x the longest
+    lens = [13257, 14478, 45818, 11785, 13140, 8156, 31001, 13071, 23276, 22166, 17936, 22454, 5776, 11113, 5199, 18047]
+    s, r = dk.decode_splits(16, 32, 8, 128, torch.bfloat16, max(lens), sum(lens))
+    busy = sum(-(-n // r) for n in lens) * 8
+    assert 768 <= busy <= 1400, (s, r, busy)
+    s0, r0 = dk.decode_splits(16, 32, 8, 128, torch.bfloat16, max(lens), 0)
+    assert r0 > r

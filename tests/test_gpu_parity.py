@@ -61,6 +61,7 @@ def test_prefill_f32(lens, hq, hkv, d):
 
 @pytest.mark.parametrize("lens,hq,hkv,d,dtype,std", [
     ((1, 100, 5000), 16, 2, 128, "bf16", 1.0),   # g=8, lengths 1 .. several splits
+    ((40000, 7, 900, 13000), 8, 2, 128, "bf16", 1.0),  # ragged lengths: splits sized by the total
     ((4097, 300), 32, 8, 128, "bf16", 1.0),      # g=4
     ((2000,), 32, 1, 128, "bf16", 1.0),          # g=32: two head chunks of 16
     ((999,), 12, 4, 64, "bf16", 1.0),            # g=3, head_dim 64
@@ -97,7 +98,7 @@ def test_decode_max_kv_len_underestimate_still_exact():
     say("decode with an under-estimated max_kv_len")
     c = synth.make_decode_case([3000], 16, 2, 128, 1, 1, "bf16", seed=4, std=1.0)
     cache = device_cache(c.k_pool, c.v_pool, c.seq_start, c.seq_len, c.seq_cap)
-    out, _ = run_decode(cache, c.q[0, 0], c.scale, max_kv_len=700)
+    out, _ = run_decode(cache, c.q[0, 0], c.scale, max_kv_len=700, total_kv_len=0)
     ref, _ = oracle.decode_ref(synth.to_f64(c.q[0, 0]), synth.to_f32(c.k_pool), synth.to_f32(c.v_pool),
                                c.seq_start.numpy(), c.seq_len.numpy(), c.scale)
     parity.check(out, ref, "bf16", discriminating=True)
