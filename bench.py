@@ -34,6 +34,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def traffic_fields(kernel, launch_s):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated
+    against a plain copy; see bench_counters.py) as a rate over the measured launch
+    time, or null when absent or taken on a different version of the kernel."""
+    from bench_counters import traffic_for
+    b = traffic_for(kernel)
+    if b is None:
+        return {"traffic": None}
+    return {"traffic": b / launch_s / 1e9, "traffic_unit": "GB/s", "traffic_bytes_per_launch": b}
+
+
 def prefill_flops(lens, hq, d):
     return sum(4.0 * d * hq * n * (n + 1) / 2.0 for n in lens)
 
@@ -212,7 +223,8 @@ def main():
         tflops = flops_layer / layer_s / 1e12
         res.update({"value": tflops, "unit": "TFLOP/s"})
         res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": tflops / BF16_DENSE_PEAK_TFLOPS, "traffic": None,
+                           "frac": tflops / BF16_DENSE_PEAK_TFLOPS,
+                           **traffic_fields("prefill_bf16_kernel<128>", layer_s),
                            "kernel": "prefill_bf16_kernel<128>", "avg_launch_ms": layer_s * 1e3,
                            "algorithmic_per_launch": flops_layer}
     if "decode" not in skip:
@@ -222,8 +234,10 @@ def main():
         res["decode"] = {"value": gbs, "unit": "GB/s", "avg_call_ms": call_s * 1e3,
                          "algorithmic_bytes_per_call": dec_bytes / calls,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                                      "kernel": "decode_split_bf16_kernel<128,2> + decode_merge_kernel"}}
+                                      "frac": gbs / HBM_PEAK_GBS, **traffic_fields("decode_split_bf16_kernel<128, 2>",
+                                                                                    call_s),
+                                      "kernel": "decode_split_bf16_kernel<128, 2> + decode_merge_kernel "
+                                                "(one call: both launches, timed together)"}}
         if "prefill" in skip:
             res.update({"value": gbs, "unit": "GB/s"})
     if not args.no_cpu_baseline:

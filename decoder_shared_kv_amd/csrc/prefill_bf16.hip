@@ -36,6 +36,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 64;          // keys per tile
 constexpr int kKPad = 8;         // bf16 padding per K^ row in LDS
@@ -53,35 +54,36 @@ template <int D>
 struct TileRegs {
   static constexpr int kChunks = (kBN * D / 8 + 255) / 256;   // 16-byte K^ chunks per thread
   static constexpr int kVBlocks = ((kBN / 4) * (D / 8) + 255) / 256;  // 4-key x 8-dim V^ blocks per thread
-  uint4 k[kChunks];
-  uint4 v[kVBlocks][4];
+  u32x4 k[kChunks];       // native vectors: HIP's uint4 struct is copied by memcpy, which
+  u32x4 v[kVBlocks][4];   // keeps an array of it out of registers
 };
 
+// Loads are unconditional (indices wrap onto valid chunks when a tile has fewer
+// chunks than threads, and only the LDS store is guarded): a conditionally
+// assigned register tile would be demoted to scratch memory.
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D>& r, const __bf16* kbase, const __bf16* vbase,
                                           int64_t row_stride, int key0, int last) {
+  constexpr int kKChunks = kBN * D / 8;
+  constexpr int kVBlocksAll = (kBN / 4) * (D / 8);
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
-    const int c = t + 256 * i;
-    if (c < kBN * D / 8) {
-      int key = key0 + c / (D / 8);
-      key = key < last ? key : last;
-      r.k[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * row_stride + 8 * (c % (D / 8)));
-    }
+    const int c = (t + 256 * i) % kKChunks;
+    int key = key0 + c / (D / 8);
+    key = key < last ? key : last;
+    r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * row_stride + 8 * (c % (D / 8)));
   }
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
-    const int c = t + 256 * i;
-    if (c < (kBN / 4) * (D / 8)) {
-      const int kg = c / (D / 8);
-      const int dc = c % (D / 8);
+    const int c = (t + 256 * i) % kVBlocksAll;
+    const int kg = c / (D / 8);
+    const int dc = c % (D / 8);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int key = key0 + 4 * kg + j;
-        key = key < last ? key : last;
-        r.v[i][j] = *reinterpret_cast<const uint4*>(vbase + (int64_t)key * row_stride + 8 * dc);
-      }
+    for (int j = 0; j < 4; ++j) {
+      int key = key0 + 4 * kg + j;
+      key = key < last ? key : last;
+      r.v[i][j] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * row_stride + 8 * dc);
     }
   }
 }
@@ -97,7 +99,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __b
   for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
     const int c = t + 256 * i;
     if (c < kBN * D / 8)
-      *reinterpret_cast<uint4*>(ks + (c / (D / 8)) * (D + kKPad) + 8 * (c % (D / 8))) = r.k[i];
+      *reinterpret_cast<u32x4*>(ks + (c / (D / 8)) * (D + kKPad) + 8 * (c % (D / 8))) = r.k[i];
   }
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
@@ -106,10 +108,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __b
       const int kg = c / (D / 8);
       const int dc = c % (D / 8);
       const int kcol = swap_bits_2_3(4 * kg);   // 4 consecutive keys stay consecutive
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&r.v[i][0]);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&r.v[i][1]);
-      const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&r.v[i][2]);
-      const uint32_t* a3 = reinterpret_cast<const uint32_t*>(&r.v[i][3]);
+      // element access on register vectors (a pointer cast would force the tile to scratch)
+      const u32x4 a0 = r.v[i][0], a1 = r.v[i][1], a2 = r.v[i][2], a3 = r.v[i][3];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint2 even, odd;
