@@ -67,10 +67,12 @@ __device__ __forceinline__ uint2 stream_load8(const void* p) {
 }
 constexpr int kVtStride = 20;  // 16 keys + 4 pad (bf16 elements) per transposed V^ row
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;
-  const __bf16 c = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, c) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 __device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }

@@ -18,6 +18,8 @@
 // B operand of the PV step c means the step's k-slot e of lane half h is key
 // 16c + 8*(e/4) + 4h + (e%4). The V^T tile stores key k at column k with bits
 // 2 and 3 swapped, which makes those eight keys one contiguous 16-byte read.
+// LDS rows are padded by 16 bytes, so that the 16-byte reads of 8 (or 16)
+// consecutive lanes from 8 (16) consecutive rows hit distinct banks.
 // Tiles wholly above the diagonal are never loaded; diagonal tiles are masked.
 // Grid: one workgroup per (unit, position block), a unit being a (sequence, KV
 // head, head chunk); position blocks run longest first. Workgroups reach the 8
@@ -44,10 +46,11 @@ constexpr int kVPad = 8;         // bf16 padding per V^T row in LDS
 
 __device__ __forceinline__ int swap_bits_2_3(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;
-  const __bf16 c = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, c) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 template <int D>
@@ -77,8 +80,8 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const __bf16* kbase, c
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
     const int c = (t + 256 * i) % kVBlocksAll;
-    const int kg = c / (D / 8);
-    const int dc = c % (D / 8);
+    const int kg = c % (kBN / 4);   // key group fastest: see store_tile
+    const int dc = c / (kBN / 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int key = key0 + 4 * kg + j;
@@ -87,10 +90,6 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const __bf16* kbase, c
     }
   }
 }
-
-// XOR swizzle of the 16-byte units of a V^T row: rows d and d+8 land in different
-// banks when 16 lanes store 16 consecutive 8-dim blocks of one key group.
-__device__ __forceinline__ int vt_swz(int d) { return (d >> 3) & 7; }
 
 template <int D>
 __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __bf16* vts) {
@@ -105,8 +104,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __b
   for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
     const int c = t + 256 * i;
     if (c < (kBN / 4) * (D / 8)) {
-      const int kg = c / (D / 8);
-      const int dc = c % (D / 8);
+      // 16 consecutive lanes hold the 16 key groups of one 8-dim block: each
+      // 8-byte store of theirs fills one 128-byte V^T row without bank conflicts
+      const int kg = c % (kBN / 4);
+      const int dc = c / (kBN / 4);
       const int kcol = swap_bits_2_3(4 * kg);   // 4 consecutive keys stay consecutive
       // element access on register vectors (a pointer cast would force the tile to scratch)
       const u32x4 a0 = r.v[i][0], a1 = r.v[i][1], a2 = r.v[i][2], a3 = r.v[i][3];
@@ -117,10 +118,9 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __b
         even.y = (a2[w] & 0xffffu) | (a3[w] << 16);
         odd.x = (a0[w] >> 16) | (a1[w] & 0xffff0000u);
         odd.y = (a2[w] >> 16) | (a3[w] & 0xffff0000u);
-        const int d = 8 * dc + 2 * w;   // d and d + 1 share d >> 3
-        const int col = (((kcol >> 3) ^ vt_swz(d)) << 3) | (kcol & 7);
-        *reinterpret_cast<uint2*>(vts + d * (kBN + kVPad) + col) = even;
-        *reinterpret_cast<uint2*>(vts + (d + 1) * (kBN + kVPad) + col) = odd;
+        const int d = 8 * dc + 2 * w;
+        *reinterpret_cast<uint2*>(vts + d * (kBN + kVPad) + kcol) = even;
+        *reinterpret_cast<uint2*>(vts + (d + 1) * (kBN + kVPad) + kcol) = odd;
       }
     }
   }
@@ -190,15 +190,12 @@ __device__ __forceinline__ void tile_step(const __bf16* ks, const __bf16* vts, c
   }
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
-    const int d = 32 * t + qj;
-    const __bf16* vrow = vts + d * (kBN + kVPad);
-    const int swz = vt_swz(d);
+    const __bf16* vrow = vts + (32 * t + qj) * (kBN + kVPad) + 8 * hf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int unit = 4 * kb + 2 * cc + hf;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + ((unit ^ swz) << 3));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 32 * kb + 16 * cc);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][cc], acc[t], 0, 0, 0);
       }
     }
