@@ -50,16 +50,26 @@ struct AppendParams {
 // Host launchers (one per kernel family); each returns the hipGetLastError code.
 hipError_t launch_kv_append(const AppendParams& p, int batch, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_prefill_bf16_dma(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_prefill_f32(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_split_f32(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hipStream_t stream);
 
 // Prefill tiling shared between the planner and the kernels.
+#ifndef YOCO_PREFILL_WAVES
+#define YOCO_PREFILL_WAVES 8
+#endif
 constexpr int kPrefillRowsPerWave = 32;
-constexpr int kPrefillWaves = 4;
-// heads of one KV group that one prefill workgroup serves (4, 2 or 1, dividing the group)
-__host__ __device__ inline int prefill_heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+constexpr int kPrefillWaves = YOCO_PREFILL_WAVES;
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
+// heads of one KV group that one prefill workgroup serves: the largest power of
+// two that divides the group and does not exceed the waves of a workgroup
+__host__ __device__ inline int prefill_heads_per_wg(int group) {
+  int h = kPrefillWaves;
+  while (h > 1 && group % h != 0) h >>= 1;
+  return h;
+}
 __host__ __device__ inline int prefill_positions_per_wg(int group) {
   return kPrefillRowsPerWave * (kPrefillWaves / prefill_heads_per_wg(group));
 }

@@ -5,8 +5,8 @@
 // section "架构总览"). A dense contraction: both products run on
 // v_mfma_f32_32x32x16_bf16.
 //
-// Workgroup = 4 waves x 32 query rows. The rows of one workgroup belong to one
-// KV head: up to 4 query heads of its group at the same 32 positions (or fewer
+// Workgroup = W waves x 32 query rows. The rows of one workgroup belong to one
+// KV head: up to W query heads of its group at the same 32 positions (or fewer
 // heads over more positions), so every K^/V^ tile staged in LDS serves all of
 // them. Per 64-key tile and per wave:
 //   S^T[key][query] = K^ . Q^T      A = K^ rows from LDS, B = Q^T in registers
@@ -55,8 +55,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 template <int D>
 struct TileRegs {
-  static constexpr int kChunks = (kBN * D / 8 + 255) / 256;   // 16-byte K^ chunks per thread
-  static constexpr int kVBlocks = ((kBN / 4) * (D / 8) + 255) / 256;  // 4-key x 8-dim V^ blocks per thread
+  static constexpr int kChunks = (kBN * D / 8 + kPrefillThreads - 1) / kPrefillThreads;  // 16-byte K^ chunks per thread
+  static constexpr int kVBlocks = ((kBN / 4) * (D / 8) + kPrefillThreads - 1) / kPrefillThreads;  // 4-key x 8-dim V^ blocks
   u32x4 k[kChunks];       // native vectors: HIP's uint4 struct is copied by memcpy, which
   u32x4 v[kVBlocks][4];   // keeps an array of it out of registers
 };
@@ -72,14 +72,14 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const __bf16* kbase, c
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
-    const int c = (t + 256 * i) % kKChunks;
+    const int c = (t + kPrefillThreads * i) % kKChunks;
     int key = key0 + c / (D / 8);
     key = key < last ? key : last;
     r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * row_stride + 8 * (c % (D / 8)));
   }
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
-    const int c = (t + 256 * i) % kVBlocksAll;
+    const int c = (t + kPrefillThreads * i) % kVBlocksAll;
     const int kg = c % (kBN / 4);   // key group fastest: see store_tile
     const int dc = c / (kBN / 4);
 #pragma unroll
@@ -96,13 +96,13 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, __bf16* ks, __b
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
-    const int c = t + 256 * i;
+    const int c = t + kPrefillThreads * i;
     if (c < kBN * D / 8)
       *reinterpret_cast<u32x4*>(ks + (c / (D / 8)) * (D + kKPad) + 8 * (c % (D / 8))) = r.k[i];
   }
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::kVBlocks; ++i) {
-    const int c = t + 256 * i;
+    const int c = t + kPrefillThreads * i;
     if (c < (kBN / 4) * (D / 8)) {
       // 16 consecutive lanes hold the 16 key groups of one 8-dim block: each
       // 8-byte store of theirs fills one 128-byte V^T row without bank conflicts
@@ -203,9 +203,15 @@ __device__ __forceinline__ void tile_step(const __bf16* ks, const __bf16* vts, c
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 ks_lds[2][kBN * (D + kKPad)];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * (kBN + kVPad)];
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnParams p) {
+  // two K^ tiles then two V^T tiles; the output staging of the epilogue reuses the start
+  constexpr int kKTile = kBN * (D + kKPad);
+  constexpr int kVTile = D * (kBN + kVPad);
+  constexpr int kOStride = D + 8;
+  static_assert(kPrefillWaves * kPrefillRowsPerWave * kOStride <= 2 * (kKTile + kVTile), "staging fits");
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (kKTile + kVTile)];
+  auto ks_lds = [&](int b) { return smem + b * kKTile; };
+  auto vt_lds = [&](int b) { return smem + 2 * kKTile + b * kVTile; };
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
     TileRegs<D> regs;
     if (n_tiles > 0) {
       load_tile<D>(regs, kbase, vbase, row_stride, 0, n_kv - 1);
-      store_tile<D>(regs, ks_lds[0], vt_lds[0]);
+      store_tile<D>(regs, ks_lds(0), vt_lds(0));
     }
     __syncthreads();
     for (int kt = 0; kt < n_tiles; ++kt) {
@@ -280,11 +286,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
       const int key0 = kt * kBN;
       if (wave_active && key0 <= wave_max_pos) {
         if (kt < full_tiles)
-          tile_step<D, false>(ks_lds[buf], vt_lds[buf], qf, acc, m, l, key0, my_pos, n_kv, c, qj, hf);
+          tile_step<D, false>(ks_lds(buf), vt_lds(buf), qf, acc, m, l, key0, my_pos, n_kv, c, qj, hf);
         else
-          tile_step<D, true>(ks_lds[buf], vt_lds[buf], qf, acc, m, l, key0, my_pos, n_kv, c, qj, hf);
+          tile_step<D, true>(ks_lds(buf), vt_lds(buf), qf, acc, m, l, key0, my_pos, n_kv, c, qj, hf);
       }
-      if (more) store_tile<D>(regs, ks_lds[buf ^ 1], vt_lds[buf ^ 1]);
+      if (more) store_tile<D>(regs, ks_lds(buf ^ 1), vt_lds(buf ^ 1));
       __syncthreads();
     }
 
@@ -292,8 +298,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
     // tiles are no longer read), then store whole rows with 16-byte writes.
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    constexpr int kOStride = D + 8;
-    __bf16* ot = &ks_lds[0][0] + wave * (kPrefillRowsPerWave * kOStride);
+    __bf16* ot = smem + wave * (kPrefillRowsPerWave * kOStride);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
@@ -330,9 +335,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnParams p) {
 
 hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream) {
   if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(kPrefillThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(kPrefillThreads), 0, stream, p);
   return hipGetLastError();
 }
 
