@@ -14,9 +14,6 @@ namespace {
 using yoco::AttnParams;
 
 constexpr float kLog2e = 1.4426950408889634f;
-#ifndef YOCO_PREFILL_DMA
-#define YOCO_PREFILL_DMA 1
-#endif
 #ifndef YOCO_DEC_U
 #define YOCO_DEC_U 2
 #endif
@@ -167,11 +164,7 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
     if (blocks * units > INT32_MAX / 2 || units > INT32_MAX) return YOCO_ERR_UNSUPPORTED;
     p.pos_blocks = (int32_t)blocks;
     const int64_t grid = yoco::prefill_grid((int)units, (int)blocks);
-#if YOCO_PREFILL_DMA
-    err = yoco::launch_prefill_bf16_dma(p, dims->head_dim, (int)grid, static_cast<hipStream_t>(stream));
-#else
     err = yoco::launch_prefill_bf16(p, dims->head_dim, (int)grid, static_cast<hipStream_t>(stream));
-#endif
   } else {
     const int64_t units = (int64_t)dims->batch * dims->num_q_heads;
     const int64_t blocks = (len + yoco::kPrefillF32Rows - 1) / yoco::kPrefillF32Rows;

@@ -50,7 +50,6 @@ struct AppendParams {
 // Host launchers (one per kernel family); each returns the hipGetLastError code.
 hipError_t launch_kv_append(const AppendParams& p, int batch, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
-hipError_t launch_prefill_bf16_dma(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_prefill_f32(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_split_f32(const AttnParams& p, int head_dim, hipStream_t stream);
