@@ -28,8 +28,9 @@ Readings where the pages are silent (each is listed in the design notes):
 * d_k is the head dimension; the scale is passed explicitly.
 * The query head h reads KV head h // (Hq / Hkv) (contiguous groups).
 * The mask is inclusive (j <= i) and exact (masked rows carry zero weight).
-* Prefill queries and keys index the same positions; a decode query sits at
-  position seq_len - 1 after its row was appended.
+* Prefill queries and keys index the same positions; a chunk of m new query
+  rows after n cached rows (m <= n) sits at the last m positions; a decode
+  query sits at position seq_len - 1 after its row was appended.
 * No positional transform inside the cross-attention.
 * LSE is the natural-log log-sum-exp of the scaled scores; an empty sequence
   yields O = 0 and LSE = -inf.
@@ -73,9 +74,15 @@ def visible_rows(p: int) -> int:
     return p + 1
 
 
-def prefill_position(r: int) -> int:
-    """Position of packed prefill query row r of a sequence: queries and keys index the same prompt."""
-    return r
+def prefill_position(r: int, n_q: int, n_kv: int) -> int:
+    """Position of query row r when a sequence has n_q query rows and n_kv cache rows.
+
+    The queries are the last n_q positions of the sequence (a full prompt when
+    n_q == n_kv; a chunk of new tokens after the cached ones otherwise); with
+    more queries than rows they start at position 0 and those past the last row
+    see every row.
+    """
+    return min(r + max(n_kv - n_q, 0), n_kv - 1)
 
 
 def decode_position(n: int) -> int:
@@ -142,8 +149,9 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start
     """Causal cross-attention of every packed query row to its sequence's shared rows.
 
     q: [total_q, Hq, d]; k_pool, v_pool: [rows, Hkv, d]. Query row r of sequence b
-    (packed row cu_seqlens[b] + r) sits at position r and sees cache rows
-    seq_start[b] + 0 .. seq_start[b] + r. Requires q_len[b] == seq_len[b].
+    (packed row cu_seqlens[b] + r) sits at position prefill_position(r, m, n) (m
+    query rows, n = seq_len[b] cache rows: r itself for a full prompt) and sees
+    cache rows seq_start[b] + 0 .. seq_start[b] + that position (at most n rows).
     `rows` (optional) restricts the work to {b: [r, ...]}; rows not computed are NaN.
     Returns out [total_q, Hq, d] and lse [Hq, total_q] (float64).
     """
@@ -155,10 +163,9 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start
     for b in range(nseq):
         n = int(seq_len[b])
         q0 = int(cu_seqlens[b])
-        if int(cu_seqlens[b + 1]) - q0 != n:
-            raise ValueError("prefill oracle needs q_len == seq_len for every sequence")
-        want = np.arange(n) if rows is None else np.asarray(sorted(set(rows.get(b, ()))), dtype=np.int64)
-        if want.size == 0:
+        m = int(cu_seqlens[b + 1]) - q0
+        want = np.arange(m) if rows is None else np.asarray(sorted(set(rows.get(b, ()))), dtype=np.int64)
+        if want.size == 0 or n == 0:
             continue
         s0 = int(seq_start[b])
         for h in range(hq):
@@ -167,7 +174,7 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start
             vb = v_pool[s0:s0 + n, kh, :]
             for i in range(0, want.size, block):
                 r = want[i:i + block]
-                pos = np.array([prefill_position(int(x)) for x in r], dtype=np.int64)
+                pos = np.array([prefill_position(int(x), m, n) for x in r], dtype=np.int64)
                 o, l = attend_rows(q[q0 + r, h, :], pos, kb, vb, scale)
                 out[q0 + r, h, :] = o
                 lse[h, q0 + r] = l

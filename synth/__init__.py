@@ -10,6 +10,7 @@ from .inputs import (  # noqa: F401
     PrefillCase,
     DecodeCase,
     make_prefill_case,
+    make_chunk_case,
     make_decode_case,
     to_f64,
     to_f32,

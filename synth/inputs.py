@@ -107,6 +107,22 @@ def make_prefill_case(lens: Sequence[int], q_heads: int, kv_heads: int, head_dim
                        float(scale if scale is not None else head_dim ** -0.5), dtype)
 
 
+def make_chunk_case(kv_lens: Sequence[int], q_lens: Sequence[int], q_heads: int, kv_heads: int, head_dim: int,
+                    dtype: str, seed: int, std: float, scale: Optional[float] = None,
+                    cap_extra: int = 0) -> PrefillCase:
+    """Cache rows kv_lens[b] per sequence and q_lens[b] query rows (a chunk of new
+    tokens after the cached ones), packed like a prefill."""
+    rngs = _streams(seed)
+    caps = [int(n) + cap_extra for n in kv_lens]
+    k, v, start, seq_len, cap = _pool(rngs, kv_lens, caps, kv_heads, head_dim, std, dtype)
+    total_q = int(sum(q_lens))
+    q = _draw(rngs[2], (total_q, q_heads, head_dim), std, dtype)
+    cu = np.zeros(len(q_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(q_lens, dtype=np.int64))
+    return PrefillCase([q], k, v, start, seq_len, cap, torch.from_numpy(cu),
+                       float(scale if scale is not None else head_dim ** -0.5), dtype)
+
+
 def make_decode_case(lens: Sequence[int], q_heads: int, kv_heads: int, head_dim: int, layers: int,
                      steps: int, dtype: str, seed: int, std: float, scale: Optional[float] = None,
                      cap_extra: int = 0, q_std: Optional[float] = None, k_std: Optional[float] = None,

@@ -238,6 +238,57 @@ def check_invariants():
     assert np.all(od == 0.0) and np.all(np.isneginf(ld))
 
 
+def _chunk_case(rng, lens, chunks, hq, hkv, d, junk=2):
+    """Cache rows lens[b]; the last chunks[b] positions of each sequence get queries."""
+    caps = [n + junk for n in lens]
+    starts = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64)
+    k = rng.standard_normal((int(sum(caps)), hkv, d))
+    v = rng.standard_normal((int(sum(caps)), hkv, d))
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
+    q = rng.standard_normal((int(cu[-1]), hq, d))
+    return q, k, v, starts, np.asarray(lens, dtype=np.int64), cu
+
+
+def check_chunked_prefill():
+    """A chunk of m queries after n - m cached rows: bottom-right causal alignment.
+
+    Pinned by (i) the full prefill of a prompt whose last m query rows are the
+    chunk's (rows before the chunk do not matter to the chunk), (ii) decode for
+    m = 1, (iii) torch SDPA in fp64 with an explicit lower-right causal mask."""
+    import torch.nn.functional as F
+    rng = _rng(16)
+    lens, chunks = (40, 17, 33), (9, 1, 33)
+    hq, hkv, d = 4, 2, 8
+    q, k, v, st, ln, cu = _chunk_case(rng, lens, chunks, hq, hkv, d)
+    o, l = ox.prefill_ref(q, k, v, st, ln, cu, 0.45)
+    for b, (n, m) in enumerate(zip(lens, chunks)):
+        # (i) full-prompt prefill with random earlier rows and this chunk as the last rows
+        qf = rng.standard_normal((n, hq, d))
+        qf[n - m:] = q[cu[b]:cu[b + 1]]
+        s0 = int(st[b])
+        of, lf = ox.prefill_ref(qf, k[s0:s0 + n], v[s0:s0 + n], [0], [n], [0, n], 0.45)
+        assert np.max(np.abs(of[n - m:] - o[cu[b]:cu[b + 1]])) <= 1e-14, ("chunk = last rows of prefill", b)
+        assert np.max(np.abs(lf[:, n - m:] - l[:, cu[b]:cu[b + 1]])) <= 1e-14
+        # (iii) SDPA with a lower-right aligned causal mask
+        mask = np.arange(n)[None, :] <= (np.arange(m)[:, None] + n - m)
+        tq = torch.from_numpy(np.ascontiguousarray(q[cu[b]:cu[b + 1]])).permute(1, 0, 2)[None]
+        tk = torch.from_numpy(np.ascontiguousarray(k[s0:s0 + n])).permute(1, 0, 2)[None]
+        tv = torch.from_numpy(np.ascontiguousarray(v[s0:s0 + n])).permute(1, 0, 2)[None]
+        ts = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), enable_gqa=True, scale=0.45)
+        assert np.max(np.abs(ts[0].permute(1, 0, 2).numpy() - o[cu[b]:cu[b + 1]])) <= 1e-12, ("chunk vs sdpa", b)
+    # more query rows than cache rows: rows past the last cache row see every row
+    q2, k2, v2, st2, ln2, cu2 = _chunk_case(rng, (5,), (8,), 2, 1, 4)
+    o2, _ = ox.prefill_ref(q2, k2, v2, st2, ln2, cu2, 0.7)
+    o2f, _ = ox.prefill_ref(q2[:5], k2, v2, st2, ln2, np.array([0, 5]), 0.7)
+    assert np.max(np.abs(o2[:5] - o2f)) <= 1e-14
+    for r in range(5, 8):
+        od2, _ = ox.decode_ref(q2[r:r + 1], k2, v2, st2, ln2, 0.7)
+        assert np.max(np.abs(o2[r] - od2[0])) <= 1e-14
+    # (ii) one-row chunk = decode
+    od, ld = ox.decode_ref(q[cu[1]:cu[2]], k, v, st[1:2], ln[1:2], 0.45)
+    assert np.max(np.abs(od[0] - o[cu[1]])) <= 1e-14 and np.max(np.abs(ld[0] - l[:, cu[1]])) <= 1e-14
+
+
 def check_append():
     rng = _rng(15)
     k = rng.standard_normal((24, 2, 4))
@@ -255,4 +306,4 @@ def check_append():
     assert list(ln3) == [3] and ov3 == 0
 
 
-ALL_PINS = [check_bruteforce, check_sdpa, check_closed_forms, check_invariants, check_append]
+ALL_PINS = [check_bruteforce, check_sdpa, check_closed_forms, check_invariants, check_chunked_prefill, check_append]

@@ -52,7 +52,7 @@ def test_correct_kernel_passes(case):
 
 MUTANT_ORACLE = {
     "mask_excludes_diagonal": ("visible_rows", lambda p: p if p > 0 else 1),
-    "mask_one_past": ("prefill_position", lambda r: r + 1),
+    "mask_one_past": ("prefill_position", lambda r, m, n: r + 1),
     "head_map_interleaved": ("kv_head_of", lambda h, hq, hkv: h % hkv),
     "no_scale": ("scores", lambda q, k, scale: q @ k.T),
     "double_scale": ("scores", lambda q, k, scale: 2 * scale * (q @ k.T)),

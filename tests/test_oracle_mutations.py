@@ -62,7 +62,11 @@ MUTATIONS = {
     "no_normalisation": ("softmax_weights", _softmax_unnormalised_sum),
     "lse_drops_max": ("log_sum_exp", lambda m, z: np.log(z)),
     "lse_log2": ("log_sum_exp", lambda m, z: m + np.log2(z)),
-    "prefill_position_shift": ("prefill_position", lambda r: r + 1),
+    "prefill_position_shift": ("prefill_position", lambda r, m, n: r + max(n - m, 0) + 1),
+    "prefill_position_no_clamp_to_last_row": ("prefill_position", lambda r, m, n: r + max(n - m, 0) if r < n
+                                               else n),
+    "chunk_aligned_top_left": ("prefill_position", lambda r, m, n: r),
+    "chunk_offset_off_by_one": ("prefill_position", lambda r, m, n: r + max(n - m - 1, 0)),
     "decode_position_before_append": ("decode_position", lambda n: n - 2),
     "decode_position_past_end": ("decode_position", lambda n: n),
     "append_wrong_row": ("kv_append_ref", _append_wrong_row),
