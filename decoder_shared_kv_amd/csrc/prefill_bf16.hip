@@ -23,7 +23,7 @@
 // LDS tiles are stored unpadded (the load unit writes 16 bytes per lane,
 // contiguous), with XOR swizzles of the 16-byte chunks chosen on the source
 // side: K^ row r keeps chunk c at c ^ (r mod chunks-per-row), V^ row r at
-// c ^ 2(r mod 4); both make the reads of 16 consecutive lanes bank-conflict-free.
+// c ^ v_swizzle(r mod 4); both make the reads bank-conflict-free.
 //
 // Pipeline: tile t + S - 1 is requested while tile t is computed, so a tile has
 // S - 1 tile-compute times to arrive. One workgroup barrier per tile.
@@ -93,6 +93,20 @@ struct Geom {
   static_assert(kChunks % kPrefillThreads == 0, "every thread issues the same number of loads");
 };
 
+// XOR applied to the 16-byte chunk index of V^ row r. A transposing read of one
+// wave covers 8 rows x 64 bytes; with these values its 16-lane groups (32 banks)
+// and its 32-lane halves (64 banks) both hit distinct banks (checked exhaustively
+// over the read pattern on the host).
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  if constexpr (D == 128) {
+    constexpr int t[4] = {0, 4, 10, 14};
+    return t[r & 3];
+  } else {
+    return 2 * (r & 3);
+  }
+}
+
 // Source offsets (elements, relative to the tile's first row) of this thread's
 // chunks: LDS chunk p = i * threads + t holds row p / cpr, swizzled chunk p % cpr.
 template <int D>
@@ -111,7 +125,7 @@ __device__ __forceinline__ void make_issue(Issue<D>& is) {
     const int r = p / cpr, cs = p % cpr;
     is.row[i] = r;
     is.kcol[i] = 8 * (cs ^ (r & (cpr - 1)));
-    is.vcol[i] = 8 * (cs ^ (2 * (r & 3)));
+    is.vcol[i] = 8 * (cs ^ v_swizzle<D>(r));
   }
 }
 
@@ -150,7 +164,7 @@ __device__ __forceinline__ void make_read_offs(ReadOffs<D>& ro, int lane) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
     // source row 4h + q of the 4-key group; dims 32t + 16(g%2) + 4w .. +3
-    const int chunk = (4 * t + 2 * (g & 1) + (w >> 1)) ^ (2 * q);
+    const int chunk = (4 * t + 2 * (g & 1) + (w >> 1)) ^ v_swizzle<D>(q);   // row 4h + q: r & 3 = q
     ro.v[t] = (4 * h + q) * (D * 2) + 16 * chunk + 8 * (w & 1);
   }
 }
