@@ -63,7 +63,7 @@ constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillWaves = YOCO_PREFILL_WAVES;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 // heads of one KV group that one prefill workgroup serves: the largest power of
-// two that divides the group and does not exceed the waves of a workgroup
+// two that divides the group and does not exceed the wave count
 __host__ __device__ inline int prefill_heads_per_wg(int group) {
   int h = kPrefillWaves;
   while (h > 1 && group % h != 0) h >>= 1;

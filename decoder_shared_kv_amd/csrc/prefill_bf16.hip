@@ -49,6 +49,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define YOCO_PREFILL_STAGES 4
 #endif
 constexpr int kStages = YOCO_PREFILL_STAGES;
+#ifndef YOCO_PREFILL_SCHED
+#define YOCO_PREFILL_SCHED 1
+#endif
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kRescaleSlack = 8.0f;   // base-2 growth of the running max tolerated before a rescale
 
@@ -65,7 +68,7 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// Wait until at most `ahead` tiles of L loads each are still in flight.
+// Wait until at most `ahead` (< kStages - 1) tiles of L loads each are still in flight.
 template <int L>
 __device__ __forceinline__ void wait_tiles(int ahead) {
   if (kStages >= 5 && ahead >= 3) wait_vm_lgkm0<(kStages >= 5 ? 3 * L : 0)>();
@@ -169,21 +172,60 @@ __device__ __forceinline__ void make_read_offs(ReadOffs<D>& ro, int lane) {
   }
 }
 
-// One 64-key tile for one wave.
+// Keeps the compiler's scheduler from moving instructions across this point,
+// so LDS reads stay where they are issued, ahead of the MFMAs that use them.
+__device__ __forceinline__ void sched_fence() {
+#if YOCO_PREFILL_SCHED
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+// One K^ A-operand read of QK step i: kk = i / 2, kb = i % 2.
+template <int D>
+__device__ __forceinline__ bf16x8 read_k(const YOCO_LDS char* ks, const ReadOffs<D>& ro, int i) {
+  return *reinterpret_cast<const YOCO_LDS bf16x8*>(ks + (i & 1) * 32 * (D * 2) + ro.k[i >> 1]);
+}
+
+// V^T A operand of PV step j (keys 32kb + 16cc + {0..3, 8..11} + 4h, dims of
+// tile t): two transposing reads, rows +0 and +8.
+template <int D>
+__device__ __forceinline__ bf16x8 read_v(const YOCO_LDS char* vs, const ReadOffs<D>& ro, int kb, int cc, int t) {
+  const YOCO_LDS char* base = vs + (32 * kb + 16 * cc) * (D * 2) + ro.v[t];
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(base + 8 * (D * 2)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+constexpr int kReadsAhead = 4;  // LDS operand reads kept in flight ahead of the MFMAs
+
+// One 64-key tile for one wave: S^T = K^ Q^T (16 or 8 MFMAs), online softmax,
+// O^T += V^T P^T. PV steps run with the dim tile fastest (consecutive MFMAs
+// update different accumulators); the exponentials of keys 32..63 are spread
+// between the PV MFMAs of keys 0..31, which run while they issue.
 template <int D, bool MASK>
 __device__ __forceinline__ void tile_step(const YOCO_LDS char* ks, const YOCO_LDS char* vs, const ReadOffs<D>& ro,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32], float& m, float& l,
                                           int key0, int my_pos, int n_kv, float c, int hf) {
-  f32x16 s[2];
+  constexpr int NQ = D / 8;        // QK steps
+  constexpr int NT = D / 32;       // dim tiles
+  constexpr int NV = 4 * NT;       // PV steps: (kb, cc, t)
+  constexpr int RA = kReadsAhead;
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  bf16x8 ka[NQ];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = f32x16{};
+  for (int i = 0; i < RA; ++i) ka[i] = read_k<D>(ks, ro, i);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const YOCO_LDS bf16x8*>(ks + kb * 32 * (D * 2) + ro.k[kk]);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-    }
+  for (int i = 0; i < NQ; ++i) {
+    if (i + RA < NQ) ka[i + RA] = read_k<D>(ks, ro, i + RA);
+    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+    sched_fence();
   }
+  // the first V^ operands go out before the softmax, which hides their latency
+  bf16x8 va[NV];
+#pragma unroll
+  for (int j = 0; j < RA; ++j) va[j] = read_v<D>(vs, ro, j / (2 * NT), (j / NT) & 1, j % NT);
+  sched_fence();
+
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -198,48 +240,51 @@ __device__ __forceinline__ void tile_step(const YOCO_LDS char* ks, const YOCO_LD
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float mx2 = mx * c;  // c > 0: the max commutes with the scale
+  // only the lanes whose own max grew move their reference, so every row's
+  // arithmetic stays independent of the other rows of the wave
   const bool grow = mx2 > m + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    // only the lanes whose own max grew move their reference, so every row's
-    // arithmetic stays independent of the other rows of the wave
     const float m_new = grow ? mx2 : m;
     const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;  // exp2(-inf) = 0 on the first tile
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+    for (int t = 0; t < NT; ++t) acc[t] *= alpha;
   }
   const float neg_m = m == -INFINITY ? 0.f : -m;
-  bf16x8 pf[2][2];
+
+  // P^T words: w[kb][cc][i] holds keys of S^T registers 8cc + 2i, 8cc + 2i + 1
+  uint32_t w[2][2][4];
+  auto softmax_word = [&](int kb, int cc, int i) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i], c, neg_m));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i + 1], c, neg_m));
+    w[kb][cc][i] = pack2(e0, e1);
+    l += e0 + e1;   // fp32 sum of the unrounded weights keeps the LSE fp32-accurate
+  };
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      uint32_t w[4];
+    for (int i = 0; i < 4; ++i) softmax_word(0, cc, i);
+  sched_fence();
+
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i], c, neg_m));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i + 1], c, neg_m));
-        w[i] = pack2(e0, e1);
-        l += e0 + e1;   // fp32 sum of the unrounded weights keeps the LSE fp32-accurate
-      }
-      pf[kb][cc] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  for (int j = 0; j < NV; ++j) {
+    const int kb = j / (2 * NT), cc = (j / NT) & 1, t = j % NT;
+    if (j + RA < NV) {
+      const int j2 = j + RA;
+      va[j2] = read_v<D>(vs, ro, j2 / (2 * NT), (j2 / NT) & 1, j2 % NT);
     }
-  }
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[kb][cc][0], w[kb][cc][1], w[kb][cc][2], w[kb][cc][3]));
+    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[t], 0, 0, 0);
+    // keys 32..63: 8 words over the NV / 2 MFMAs of keys 0..31
+    if (j < NV / 2) {
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        // keys 32kb + 16cc + {0..3, 8..11} + 4h: rows +0 and +8 of the transposing reads
-        const YOCO_LDS char* base = vs + (32 * kb + 16 * cc) * (D * 2) + ro.v[t];
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(base));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(base + 8 * (D * 2)));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][cc], acc[t], 0, 0, 0);
+      for (int q = 0; q < 8 / (NV / 2); ++q) {
+        const int wi = j * (8 / (NV / 2)) + q;
+        softmax_word(1, wi >> 2, wi & 3);
       }
     }
+    sched_fence();
   }
 }
 
@@ -266,6 +311,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
   const int hc = unit % hchunks;
   const int kh = (unit / hchunks) % p.hkv;
   const int b = unit / (hchunks * p.hkv);
+  // wave -> (head, position block): heads fastest
   const int h = kh * p.group + hc * hpw + wave % hpw;
   const int pbl = wave / hpw;
   const int pos_per_wg = kPrefillRowsPerWave * ppw;
@@ -292,16 +338,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
   constexpr int L = 2 * Geom<D>::kLoads;   // loads per thread and tile
 
   for (int pw = p.pos_blocks - 1 - rank; pw >= 0 && pw * pos_per_wg < n_q; pw += p.pos_blocks) {
-    const int r0 = pw * pos_per_wg + pbl * kPrefillRowsPerWave;
     const int wg_last_row = min(n_q, (pw + 1) * pos_per_wg) - 1;
     const int wg_last_key = min(wg_last_row + offset, n_kv - 1);
     const int n_tiles = wg_last_key >= 0 ? wg_last_key / kBN + 1 : 0;
-    const bool wave_active = r0 < n_q;
-    const int wave_min_pos = r0 + offset;
-    const int wave_max_pos = min(r0 + kPrefillRowsPerWave, n_q) - 1 + offset;
-    const int full_tiles = min((wave_min_pos + 1) / kBN, n_kv / kBN);
-    const int my_row = min(r0 + qj, n_q - 1);
+    const int r0 = pw * pos_per_wg + pbl * kPrefillRowsPerWave;
     const int my_pos = r0 + qj + offset;
+    const bool wave_active = r0 < n_q;
+    const int wave_max_pos = min(r0 + kPrefillRowsPerWave, n_q) - 1 + offset;
+    // tiles below full_tiles need no mask for any row of this wave
+    const int full_tiles = min((r0 + offset + 1) / kBN, n_kv / kBN);
 
     // the tiles ahead go out first: they have the longest way
 #pragma unroll
@@ -310,6 +355,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
 
     bf16x8 qf[D / 16];
     {
+      const int my_row = min(r0 + qj, n_q - 1);
       const __bf16* qsrc = qbase + ((q0 + my_row) * p.hq + h) * D + 8 * hf;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
@@ -323,9 +369,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     for (int kt = 0; kt < n_tiles; ++kt) {
       // tile kt has landed in LDS (this thread's part): at most the tiles
       // requested after it may still be in flight
-      const int ahead = min(kStages - 2, n_tiles - 1 - kt);
-      wait_tiles<L>(ahead);
-      barrier_only();  // every thread's part of tile kt is in; stage (kt-1) % S is free
+      wait_tiles<L>(min(kStages - 2, n_tiles - 1 - kt));
+      barrier_only();  // every thread's part of tile kt is in; stage (kt - 1) % S is free
       if (kt + kStages - 1 < n_tiles)
         issue_tile<D>(is, kbase, vbase, row_stride, (kt + kStages - 1) * kBN, n_kv - 1,
                       smem + ((kt + kStages - 1) % kStages) * kStage);
@@ -351,28 +396,26 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const u32x2 w = {pack2(acc[t][4 * g4 + 0] * inv, acc[t][4 * g4 + 1] * inv),
-                         pack2(acc[t][4 * g4 + 2] * inv, acc[t][4 * g4 + 3] * inv)};
-        *reinterpret_cast<YOCO_LDS u32x2*>(ot + qj * kOStride + 32 * t + 8 * g4 + 4 * hf) = w;
+        const u32x2 wv = {pack2(acc[t][4 * g4 + 0] * inv, acc[t][4 * g4 + 1] * inv),
+                          pack2(acc[t][4 * g4 + 2] * inv, acc[t][4 * g4 + 3] * inv)};
+        *reinterpret_cast<YOCO_LDS u32x2*>(ot + qj * kOStride + 32 * t + 8 * g4 + 4 * hf) = wv;
       }
     }
+    if (hf == 0 && p.lse != nullptr && r0 + qj < n_q)
+      p.lse[(int64_t)h * p.total_q + q0 + r0 + qj] =
+          l_tot > 0.f ? (m + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (wave_active) {
-      __bf16* obase = static_cast<__bf16*>(p.out);
+    __bf16* obase = static_cast<__bf16*>(p.out);
 #pragma unroll
-      for (int i = 0; i < kPrefillRowsPerWave * (D / 8) / 64; ++i) {
-        const int ci = lane + 64 * i;
-        const int row = ci / (D / 8);
-        const int c8 = ci % (D / 8);
-        if (r0 + row < n_q)
-          *reinterpret_cast<u32x4*>(obase + ((q0 + r0 + row) * p.hq + h) * D + 8 * c8) =
-              *reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8);
-      }
-      if (hf == 0 && p.lse != nullptr && r0 + qj < n_q)
-        p.lse[(int64_t)h * p.total_q + q0 + r0 + qj] =
-            l_tot > 0.f ? (m + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    for (int i = 0; i < kPrefillRowsPerWave * (D / 8) / 64; ++i) {
+      const int ci = lane + 64 * i;
+      const int row = ci / (D / 8);
+      const int c8 = ci % (D / 8);
+      if (r0 + row < n_q)
+        *reinterpret_cast<u32x4*>(obase + ((q0 + r0 + row) * p.hq + h) * D + 8 * c8) =
+            *reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8);
     }
     __syncthreads();  // the staging area is the next pass's first stage
   }
