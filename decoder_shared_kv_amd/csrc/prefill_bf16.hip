@@ -110,17 +110,19 @@ __device__ __forceinline__ int v_swizzle(int r) {
   }
 }
 
-// Source offsets (elements, relative to the tile's first row) of this thread's
-// chunks: LDS chunk p = i * threads + t holds row p / cpr, swizzled chunk p % cpr.
+// Source offsets of this thread's chunks, relative to the tile's first row:
+// LDS chunk p = i * threads + t holds row p / cpr, swizzled chunk p % cpr.
 template <int D>
 struct Issue {
   int row[Geom<D>::kLoads];
-  int kcol[Geom<D>::kLoads];  // element offset of the K^ chunk within the row
+  int kcol[Geom<D>::kLoads];       // element offset of the K^ chunk within its row
   int vcol[Geom<D>::kLoads];
+  uint32_t koff[Geom<D>::kLoads];  // byte offset of the K^ chunk from the tile's first row
+  uint32_t voff[Geom<D>::kLoads];
 };
 
 template <int D>
-__device__ __forceinline__ void make_issue(Issue<D>& is) {
+__device__ __forceinline__ void make_issue(Issue<D>& is, int64_t row_stride) {
   constexpr int cpr = Geom<D>::kCpr;
 #pragma unroll
   for (int i = 0; i < Geom<D>::kLoads; ++i) {
@@ -129,23 +131,59 @@ __device__ __forceinline__ void make_issue(Issue<D>& is) {
     is.row[i] = r;
     is.kcol[i] = 8 * (cs ^ (r & (cpr - 1)));
     is.vcol[i] = 8 * (cs ^ v_swizzle<D>(r));
+    is.koff[i] = (uint32_t)((r * row_stride + is.kcol[i]) * 2);
+    is.voff[i] = (uint32_t)((r * row_stride + is.vcol[i]) * 2);
   }
 }
+
+// 16-byte-per-lane HBM -> LDS copies by the load unit: lane l's 16 bytes land
+// at dst + 16 l (dst is wave-uniform). Written as asm so that the compiler does
+// not count them among its own LDS events (which would make it wait for every
+// LDS read to finish before the next MFMA); their completion is awaited
+// explicitly with s_waitcnt vmcnt before the workgroup barrier of their tile.
+// The s_nop covers the wait states a load-to-LDS needs after an M0 write (and
+// after a VALU write of an SGPR operand), which the compiler does not insert
+// inside asm.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else in this kernel uses it
+// per-lane 64-bit source address
+__device__ __forceinline__ void dma16(const __bf16* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+}
+// wave-uniform 64-bit base + per-lane 32-bit byte offset: no per-lane address arithmetic
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Request one K^/V^ tile into a stage. Rows past `last` repeat row `last`.
 template <int D>
 __device__ __forceinline__ void issue_tile(const Issue<D>& is, const __bf16* kbase, const __bf16* vbase,
                                            int64_t row_stride, int key0, int last, YOCO_LDS char* stage) {
-  const int wave = threadIdx.x >> 6;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)stage + wave * 64 * 16;
+  if (key0 + kBN - 1 <= last) {
+    // whole tile inside the sequence: one scalar base per matrix
+    const int64_t toff = (int64_t)key0 * row_stride;
+    const char* kt = reinterpret_cast<const char*>(kbase + toff);
+    const char* vt = reinterpret_cast<const char*>(vbase + toff);
 #pragma unroll
-  for (int i = 0; i < Geom<D>::kLoads; ++i) {
-    int key = key0 + is.row[i];
-    key = key < last ? key : last;
-    const int64_t roff = (int64_t)key * row_stride;
-    YOCO_LDS char* kd = stage + (i * kPrefillThreads + wave * 64) * 16;
-    YOCO_LDS char* vd = kd + Geom<D>::kTileBytes;
-    __builtin_amdgcn_global_load_lds((const void*)(kbase + roff + is.kcol[i]), (YOCO_LDS void*)kd, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vbase + roff + is.vcol[i]), (YOCO_LDS void*)vd, 16, 0, 0);
+    for (int i = 0; i < Geom<D>::kLoads; ++i) {
+      const uint32_t kd = lds0 + i * kPrefillThreads * 16;
+      dma16(kt, is.koff[i], kd);
+      dma16(vt, is.voff[i], kd + Geom<D>::kTileBytes);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Geom<D>::kLoads; ++i) {
+      int key = key0 + is.row[i];
+      key = key < last ? key : last;
+      const int64_t roff = (int64_t)key * row_stride;
+      const uint32_t kd = lds0 + i * kPrefillThreads * 16;
+      dma16(kbase + roff + is.kcol[i], kd);
+      dma16(vbase + roff + is.vcol[i], kd + Geom<D>::kTileBytes);
+    }
   }
 }
 
@@ -332,7 +370,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
   const __bf16* qbase = static_cast<const __bf16*>(p.q);
 
   Issue<D> is;
-  make_issue<D>(is);
+  make_issue<D>(is, row_stride);
   ReadOffs<D> ro;
   make_read_offs<D>(ro, lane);
   constexpr int L = 2 * Geom<D>::kLoads;   // loads per thread and tile
@@ -361,6 +399,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
       for (int kk = 0; kk < D / 16; ++kk)
         qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qsrc + 16 * kk));
     }
+    // Q^ (and the first tiles) in: from here on the only loads in flight are
+    // tile copies, which the loop awaits by count
+    wait_vm_lgkm0<0>();
     f32x16 acc[D / 32];
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
