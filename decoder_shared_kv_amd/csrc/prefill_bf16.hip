@@ -26,7 +26,10 @@
 // c ^ v_swizzle(r mod 4); both make the reads bank-conflict-free.
 //
 // Pipeline: tile t + S - 1 is requested while tile t is computed, so a tile has
-// S - 1 tile-compute times to arrive. One workgroup barrier per tile.
+// S - 1 tile-compute times to arrive. One workgroup barrier per tile. Within a
+// tile each wave keeps its LDS operand reads a few MFMAs ahead (scheduling
+// fences stop the compiler from sinking them to their use), and spreads half
+// of the exponentials between the PV MFMAs, which execute while they issue.
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
@@ -52,6 +55,7 @@ constexpr int kStages = YOCO_PREFILL_STAGES;
 #ifndef YOCO_PREFILL_SCHED
 #define YOCO_PREFILL_SCHED 1
 #endif
+
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kRescaleSlack = 8.0f;   // base-2 growth of the running max tolerated before a rescale
 
@@ -236,19 +240,13 @@ __device__ __forceinline__ bf16x8 read_v(const YOCO_LDS char* vs, const ReadOffs
 
 constexpr int kReadsAhead = 4;  // LDS operand reads kept in flight ahead of the MFMAs
 
-// One 64-key tile for one wave: S^T = K^ Q^T (16 or 8 MFMAs), online softmax,
-// O^T += V^T P^T. PV steps run with the dim tile fastest (consecutive MFMAs
-// update different accumulators); the exponentials of keys 32..63 are spread
-// between the PV MFMAs of keys 0..31, which run while they issue.
-template <int D, bool MASK>
-__device__ __forceinline__ void tile_step(const YOCO_LDS char* ks, const YOCO_LDS char* vs, const ReadOffs<D>& ro,
-                                          const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32], float& m, float& l,
-                                          int key0, int my_pos, int n_kv, float c, int hf) {
-  constexpr int NQ = D / 8;        // QK steps
-  constexpr int NT = D / 32;       // dim tiles
-  constexpr int NV = 4 * NT;       // PV steps: (kb, cc, t)
+// S^T = K^ Q^T of one 64-key tile for one wave (16 or 8 MFMAs, two chains).
+template <int D>
+__device__ __forceinline__ void qk_step(const YOCO_LDS char* ks, const ReadOffs<D>& ro, const bf16x8 (&qf)[D / 16],
+                                        f32x16 (&s)[2]) {
+  constexpr int NQ = D / 8;
   constexpr int RA = kReadsAhead;
-  f32x16 s[2] = {f32x16{}, f32x16{}};
+  s[0] = s[1] = f32x16{};
   bf16x8 ka[NQ];
 #pragma unroll
   for (int i = 0; i < RA; ++i) ka[i] = read_k<D>(ks, ro, i);
@@ -258,20 +256,23 @@ __device__ __forceinline__ void tile_step(const YOCO_LDS char* ks, const YOCO_LD
     s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1], s[i & 1], 0, 0, 0);
     sched_fence();
   }
-  // the first V^ operands go out before the softmax, which hides their latency
-  bf16x8 va[NV];
-#pragma unroll
-  for (int j = 0; j < RA; ++j) va[j] = read_v<D>(vs, ro, j / (2 * NT), (j / NT) & 1, j % NT);
-  sched_fence();
+}
 
+// Online-softmax bookkeeping of one tile: mask, row max, lazy rescale of the
+// running state. Returns -m for the exponentials.
+template <int D, bool MASK>
+__device__ __forceinline__ float softmax_max(f32x16 (&s)[2], f32x16 (&acc)[D / 32], float& m, float& l, int key0,
+                                             int my_pos, int n_kv, float c, int hf) {
+  // register r of chain kb holds key key0 + 32kb + 8(r/4) + 4hf + r%4; keys past
+  // min(my_pos, n_kv - 1) are masked: one compare with a constant per register
+  const int lim = min(my_pos, n_kv - 1) - key0 - 4 * hf;
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       if constexpr (MASK) {
-        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key > my_pos || key >= n_kv) s[kb][r] = -INFINITY;
+        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
       }
       mx = fmaxf(mx, s[kb][r]);
     }
@@ -287,30 +288,64 @@ __device__ __forceinline__ void tile_step(const YOCO_LDS char* ks, const YOCO_LD
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+    for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
   }
-  const float neg_m = m == -INFINITY ? 0.f : -m;
+  return m == -INFINITY ? 0.f : -m;
+}
 
-  // P^T words: w[kb][cc][i] holds keys of S^T registers 8cc + 2i, 8cc + 2i + 1
+// P^T word w[kb][cc][i]: the weights of S^T registers 8cc + 2i and 8cc + 2i + 1
+// of chain kb, as two bf16; adds them (unrounded) to the row sum.
+__device__ __forceinline__ void softmax_word(const f32x16 (&s)[2], uint32_t (&w)[2][2][4], float& l, float c,
+                                             float neg_m, int kb, int cc, int i) {
+  const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i], c, neg_m));
+  const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i + 1], c, neg_m));
+  w[kb][cc][i] = pack2(e0, e1);
+  l += e0 + e1;   // fp32 sum of the unrounded weights keeps the LSE fp32-accurate
+}
+
+// PV step j of a tile: (kb, cc, t) with the dim tile t fastest, so consecutive
+// MFMAs update different accumulators.
+template <int D>
+__device__ __forceinline__ void pv_index(int j, int& kb, int& cc, int& t) {
+  constexpr int NT = D / 32;
+  kb = j / (2 * NT);
+  cc = (j / NT) & 1;
+  t = j % NT;
+}
+
+// Softmax and O^T += V^T P^T of one tile whose S^T is in s. The exponentials
+// of keys 32..63 are spread between the PV MFMAs of keys 0..31, which run
+// while they issue.
+template <int D, bool MASK>
+__device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<D>& ro, f32x16 (&s)[2],
+                                        f32x16 (&acc)[D / 32], float& m, float& l, int key0, int my_pos, int n_kv,
+                                        float c, int hf) {
+  constexpr int NV = D / 8;        // PV steps: (kb, cc, t)
+  constexpr int RA = kReadsAhead;
+  // the first V^ operands go out before the softmax, which hides their latency
+  bf16x8 va[NV];
+#pragma unroll
+  for (int j = 0; j < RA; ++j) {
+    int kb, cc, t;
+    pv_index<D>(j, kb, cc, t);
+    va[j] = read_v<D>(vs, ro, kb, cc, t);
+  }
+  sched_fence();
+  const float neg_m = softmax_max<D, MASK>(s, acc, m, l, key0, my_pos, n_kv, c, hf);
   uint32_t w[2][2][4];
-  auto softmax_word = [&](int kb, int cc, int i) {
-    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i], c, neg_m));
-    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i + 1], c, neg_m));
-    w[kb][cc][i] = pack2(e0, e1);
-    l += e0 + e1;   // fp32 sum of the unrounded weights keeps the LSE fp32-accurate
-  };
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) softmax_word(0, cc, i);
+    for (int i = 0; i < 4; ++i) softmax_word(s, w, l, c, neg_m, 0, cc, i);
   sched_fence();
-
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int kb = j / (2 * NT), cc = (j / NT) & 1, t = j % NT;
+    int kb, cc, t;
+    pv_index<D>(j, kb, cc, t);
     if (j + RA < NV) {
-      const int j2 = j + RA;
-      va[j2] = read_v<D>(vs, ro, j2 / (2 * NT), (j2 / NT) & 1, j2 % NT);
+      int kb2, cc2, t2;
+      pv_index<D>(j + RA, kb2, cc2, t2);
+      va[j + RA] = read_v<D>(vs, ro, kb2, cc2, t2);
     }
     const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[kb][cc][0], w[kb][cc][1], w[kb][cc][2], w[kb][cc][3]));
     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[t], 0, 0, 0);
@@ -319,7 +354,7 @@ __device__ __forceinline__ void tile_step(const YOCO_LDS char* ks, const YOCO_LD
 #pragma unroll
       for (int q = 0; q < 8 / (NV / 2); ++q) {
         const int wi = j * (8 / (NV / 2)) + q;
-        softmax_word(1, wi >> 2, wi & 3);
+        softmax_word(s, w, l, c, neg_m, 1, wi >> 2, wi & 3);
       }
     }
     sched_fence();
@@ -419,10 +454,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
       if (wave_active && key0 <= wave_max_pos) {
         const YOCO_LDS char* ks = smem + (kt % kStages) * kStage;
         const YOCO_LDS char* vs = ks + Geom<D>::kTileBytes;
-        if (kt < full_tiles)
-          tile_step<D, false>(ks, vs, ro, qf, acc, m, l, key0, my_pos, n_kv, c, hf);
-        else
-          tile_step<D, true>(ks, vs, ro, qf, acc, m, l, key0, my_pos, n_kv, c, hf);
+        f32x16 s[2];
+        if (kt >= full_tiles) {
+          qk_step<D>(ks, ro, qf, s);
+          sv_step<D, true>(vs, ro, s, acc, m, l, key0, my_pos, n_kv, c, hf);
+        } else {
+          qk_step<D>(ks, ro, qf, s);
+          sv_step<D, false>(vs, ro, s, acc, m, l, key0, my_pos, n_kv, c, hf);
+        }
       }
     }
     wait_vm_lgkm0<0>();
