@@ -22,6 +22,12 @@ What it computes is the plain definition, written out step by step:
 * Decode: the new token passes the Self-Decoder first, so its own K̂,V̂ row is in
   the cache before the Cross-Decoder layers read it ("YOCO", section "Decode：
   新 token 仍需经过两部分").
+* Sliding-window attention, the Self-Decoder's efficient attention: the current
+  position sees only the tokens of a fixed window of size C, so one layer's
+  decode cache holds O(C) rows instead of O(N) ("YOCO", section "Self-Decoder：
+  把历史编码成可复用的全局表示"; "YOCO 深度技术分析", section 2.3, C = 1024).
+  The same attention with the band mask instead of the causal mask; a decode
+  window cache is a ring of C rows.
 
 Readings where the pages are silent (each is listed in the design notes):
 
@@ -34,6 +40,11 @@ Readings where the pages are silent (each is listed in the design notes):
 * No positional transform inside the cross-attention.
 * LSE is the natural-log log-sum-exp of the scaled scores; an empty sequence
   yields O = 0 and LSE = -inf.
+* A window of size C holds the C most recent positions, the query's own
+  included: position p sees rows max(0, p - C + 1) .. p. Window 0 means no
+  window (plain causal). A ring window cache keeps token t in slot t mod C, so
+  its valid slots are exactly the last min(t + 1, C) tokens, in rotated order;
+  softmax attention does not depend on the order of its keys.
 
 All arithmetic is float64 on exact upcasts of the stored values. Query rows are
 processed in blocks only to bound memory: each row's arithmetic is the
@@ -48,6 +59,7 @@ import numpy as np
 __all__ = [
     "kv_head_of",
     "visible_rows",
+    "window_start",
     "prefill_position",
     "decode_position",
     "scores",
@@ -57,6 +69,7 @@ __all__ = [
     "prefill_ref",
     "decode_ref",
     "kv_append_ref",
+    "ring_append_ref",
 ]
 
 
@@ -72,6 +85,11 @@ def kv_head_of(h: int, q_heads: int, kv_heads: int) -> int:
 def visible_rows(p: int) -> int:
     """Number of shared-cache rows the query at position p sees: rows 0..p."""
     return p + 1
+
+
+def window_start(p: int, window: int) -> int:
+    """First row the query at position p sees under a window of `window` positions (0: none)."""
+    return max(0, p - window + 1) if window > 0 else 0
 
 
 def prefill_position(r: int, n_q: int, n_kv: int) -> int:
@@ -113,10 +131,11 @@ def log_sum_exp(m: np.ndarray, z: np.ndarray) -> np.ndarray:
 
 
 def attend_rows(q: np.ndarray, positions: np.ndarray, k: np.ndarray, v: np.ndarray,
-                scale: float) -> Tuple[np.ndarray, np.ndarray]:
+                scale: float, window: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Causal attention of query rows q [r, d] at `positions` [r] to rows k, v [n, d].
 
-    Row i of the result is sum_j softmax_j(scale q_i.k_j, j <= p_i) v_j and its LSE.
+    Row i of the result is sum_j softmax_j(scale q_i.k_j, j <= p_i) v_j and its LSE;
+    with a window, only rows window_start(p_i, window) <= j take part.
     """
     q = np.asarray(q, dtype=np.float64)
     positions = np.asarray(positions, dtype=np.int64)
@@ -131,7 +150,8 @@ def attend_rows(q: np.ndarray, positions: np.ndarray, k: np.ndarray, v: np.ndarr
     s = scores(q, kk, scale)
     j = np.arange(n_vis)[None, :]
     lim = np.array([visible_rows(int(p)) for p in positions])[:, None]
-    s = np.where(j < lim, s, -np.inf)
+    first = np.array([window_start(int(p), window) for p in positions])[:, None]
+    s = np.where((j < lim) & (j >= first), s, -np.inf)
     w, m, z = softmax_weights(s)
     out = (w @ vv) / z
     lse = log_sum_exp(m, z)[:, 0]
@@ -144,8 +164,8 @@ def attend_rows(q: np.ndarray, positions: np.ndarray, k: np.ndarray, v: np.ndarr
 
 def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start: Sequence[int],
                 seq_len: Sequence[int], cu_seqlens: Sequence[int], scale: float,
-                rows: Optional[Dict[int, Iterable[int]]] = None, block: int = 512
-                ) -> Tuple[np.ndarray, np.ndarray]:
+                rows: Optional[Dict[int, Iterable[int]]] = None, block: int = 512,
+                window: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Causal cross-attention of every packed query row to its sequence's shared rows.
 
     q: [total_q, Hq, d]; k_pool, v_pool: [rows, Hkv, d]. Query row r of sequence b
@@ -153,7 +173,8 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start
     query rows, n = seq_len[b] cache rows: r itself for a full prompt) and sees
     cache rows seq_start[b] + 0 .. seq_start[b] + that position (at most n rows).
     `rows` (optional) restricts the work to {b: [r, ...]}; rows not computed are NaN.
-    Returns out [total_q, Hq, d] and lse [Hq, total_q] (float64).
+    `window` > 0 restricts each query to the rows of its window (sliding-window
+    attention). Returns out [total_q, Hq, d] and lse [Hq, total_q] (float64).
     """
     total_q, hq, d = q.shape
     hkv = k_pool.shape[1]
@@ -175,15 +196,16 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start
             for i in range(0, want.size, block):
                 r = want[i:i + block]
                 pos = np.array([prefill_position(int(x), m, n) for x in r], dtype=np.int64)
-                o, l = attend_rows(q[q0 + r, h, :], pos, kb, vb, scale)
+                o, l = attend_rows(q[q0 + r, h, :], pos, kb, vb, scale, window)
                 out[q0 + r, h, :] = o
                 lse[h, q0 + r] = l
     return out, lse
 
 
 def decode_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start: Sequence[int],
-               seq_len: Sequence[int], scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """One query per sequence at position seq_len[b] - 1, against rows 0..seq_len[b]-1.
+               seq_len: Sequence[int], scale: float, window: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """One query per sequence at position seq_len[b] - 1, against rows 0..seq_len[b]-1
+    (only the last `window` of them when window > 0).
 
     q: [B, Hq, d]. Returns out [B, Hq, d] and lse [B, Hq] (float64). A sequence with
     no rows gives out = 0 and lse = -inf.
@@ -203,7 +225,7 @@ def decode_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start:
             for h in range(hq):
                 if kv_head_of(h, hq, hkv) != kh:
                     continue
-                o, l = attend_rows(q[b, h:h + 1, :], np.array([decode_position(n)]), kb, vb, scale)
+                o, l = attend_rows(q[b, h:h + 1, :], np.array([decode_position(n)]), kb, vb, scale, window)
                 out[b, h] = o[0]
                 lse[b, h] = l[0]
     return out, lse
@@ -230,3 +252,29 @@ def kv_append_ref(k_pool: np.ndarray, v_pool: np.ndarray, seq_start: Sequence[in
         v2[row] = v_new[b]
         lens[b] += 1
     return k2, v2, lens, overflow
+
+
+def ring_append_ref(k_ring: np.ndarray, v_ring: np.ndarray, seq_start: Sequence[int],
+                    seq_len: Sequence[int], seq_cap: Sequence[int], k_new: np.ndarray,
+                    v_new: np.ndarray):
+    """Append to ring window caches: sequence b's token number seq_len[b] goes to
+    slot seq_len[b] mod seq_cap[b] of its seq_cap[b] rows, replacing the token
+    seq_cap[b] positions older; seq_len[b] counts every token appended so far.
+
+    A sequence with no rows (seq_cap 0) stores nothing and raises the flag.
+    Returns (k_ring', v_ring', seq_len', flag) as new arrays.
+    """
+    k2 = np.array(k_ring, copy=True)
+    v2 = np.array(v_ring, copy=True)
+    lens = np.array(seq_len, dtype=np.int64, copy=True)
+    flag = 0
+    for b in range(len(lens)):
+        cap = int(seq_cap[b])
+        if cap <= 0:
+            flag = 1
+            continue
+        row = int(seq_start[b]) + int(lens[b]) % cap
+        k2[row] = k_new[b]
+        v2[row] = v_new[b]
+        lens[b] += 1
+    return k2, v2, lens, flag

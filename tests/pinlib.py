@@ -306,4 +306,123 @@ def check_append():
     assert list(ln3) == [3] and ov3 == 0
 
 
-ALL_PINS = [check_bruteforce, check_sdpa, check_closed_forms, check_invariants, check_chunked_prefill, check_append]
+# ---------------------------------------------------------------------------
+# sliding window and ring window cache
+# ---------------------------------------------------------------------------
+
+def _brute_window_row(q_row, k, v, p, window, scale):
+    """Pure-Python attention of one query at position p to rows max(0, p-C+1)..p."""
+    lo = max(0, p - window + 1)
+    e = [math.exp(scale * math.fsum(float(a) * float(b) for a, b in zip(q_row, k[j]))) for j in range(lo, p + 1)]
+    z = math.fsum(e)
+    out = [math.fsum(e[j - lo] * float(v[j][t]) for j in range(lo, p + 1)) / z for t in range(len(v[0]))]
+    return np.array(out), math.log(z)
+
+
+def check_window():
+    """Sliding-window attention: position p sees rows max(0, p - C + 1) .. p.
+
+    Pinned by pure-Python loops, torch SDPA in fp64 with an explicit band mask,
+    the closed forms C = 1 (O = V[p], LSE = the own score) and K = 0 (moving
+    average of the last C rows, LSE = log of their count), C >= N equal to no
+    window, invariance to rows before the window, decode = prefill's last row,
+    and a chunk of queries = the last rows of the full windowed prefill."""
+    import torch.nn.functional as F
+    rng = _rng(17)
+    # brute force, several windows, GQA 2:1 and packed sequences
+    q, k, v, st, ln, cu = _pool_case(rng, (11, 6), 4, 2, 3, junk=2)
+    for window in (1, 2, 4, 7):
+        o, l = ox.prefill_ref(q, k, v, st, ln, cu, 0.8, window=window)
+        for b in range(2):
+            for r in range(int(ln[b])):
+                for h in range(4):
+                    s0 = int(st[b])
+                    ob, lb = _brute_window_row(q[int(cu[b]) + r, h], k[s0:s0 + int(ln[b]), h // 2],
+                                               v[s0:s0 + int(ln[b]), h // 2], r, window, 0.8)
+                    assert np.max(np.abs(o[int(cu[b]) + r, h] - ob)) <= 1e-13, ("window brute", window, b, r)
+                    assert abs(l[h, int(cu[b]) + r] - lb) <= 1e-13
+    # SDPA with a band mask
+    for n, hq, hkv, d, window in [(50, 4, 1, 8, 9), (130, 6, 3, 16, 64), (70, 2, 2, 4, 1)]:
+        q, k, v, st, ln, cu = _pool_case(rng, (n,), hq, hkv, d, junk=0)
+        o, _ = ox.prefill_ref(q, k, v, st, ln, cu, 0.3, window=window)
+        i, j = np.arange(n)[:, None], np.arange(n)[None, :]
+        band = torch.from_numpy((j <= i) & (j > i - window))
+        tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+        tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+        tv = torch.from_numpy(v).permute(1, 0, 2)[None]
+        ts = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=band, enable_gqa=True, scale=0.3)
+        assert np.max(np.abs(ts[0].permute(1, 0, 2).numpy() - o)) <= 1e-12, ("window vs sdpa", n, window)
+    # closed forms
+    n, hq, hkv, d = 30, 2, 1, 5
+    q, k, v, st, ln, cu = _pool_case(rng, (n,), hq, hkv, d, junk=3)
+    o, l = ox.prefill_ref(q, k, v, st, ln, cu, 0.7, window=1)
+    for h in range(hq):
+        assert np.max(np.abs(o[:, h] - v[:n, 0])) <= 1e-15, "window 1: own row"
+        assert np.max(np.abs(l[h] - 0.7 * np.einsum("rd,rd->r", q[:, h], k[:n, 0]))) <= 1e-13
+    kz = k.copy()
+    kz[:n] = 0.0
+    for window in (3, 8):
+        o, l = ox.prefill_ref(q, kz, v, st, ln, cu, 0.7, window=window)
+        c = np.concatenate([np.zeros((1, d)), np.cumsum(v[:n, 0], axis=0)])
+        for p in range(n):
+            lo = max(0, p - window + 1)
+            avg = (c[p + 1] - c[lo]) / (p + 1 - lo)
+            assert np.max(np.abs(o[p, :] - avg[None])) <= 1e-13, ("K=0 moving average", window, p)
+            assert np.max(np.abs(l[:, p] - math.log(p + 1 - lo))) <= 1e-13
+    # window covering the whole sequence = no window
+    o0, l0 = ox.prefill_ref(q, k, v, st, ln, cu, 0.7)
+    ow, lw = ox.prefill_ref(q, k, v, st, ln, cu, 0.7, window=n)
+    assert np.array_equal(o0, ow) and np.array_equal(l0, lw)
+    # rows before the window of row p do not matter to rows p.. (they do to the rows before p)
+    p, window = 20, 6
+    k2, v2 = k.copy(), v.copy()
+    k2[:p - window + 1] += 3.0
+    v2[:p - window + 1] -= 5.0
+    o2, l2 = ox.prefill_ref(q, k2, v2, st, ln, cu, 0.7, window=window)
+    ow, lw = ox.prefill_ref(q, k, v, st, ln, cu, 0.7, window=window)
+    assert np.array_equal(o2[p:], ow[p:]) and np.array_equal(l2[:, p:], lw[:, p:]), "rows before the window"
+    assert np.max(np.abs(o2[p - 1] - ow[p - 1])) > 1e-3
+    # decode with a window = the windowed prefill's row p
+    for p in (0, 4, 5, 29):
+        od, ld = ox.decode_ref(q[p:p + 1], k, v, st, [p + 1], 0.7, window=window)
+        assert np.max(np.abs(od[0] - ow[p])) <= 1e-14 and np.max(np.abs(ld[0] - lw[:, p])) <= 1e-14
+    # a chunk of the last m positions = the last rows of the full windowed prefill
+    m = 7
+    qc = q[n - m:]
+    oc, lc = ox.prefill_ref(qc, k, v, st, ln, np.array([0, m]), 0.7, window=window)
+    assert np.max(np.abs(oc - ow[n - m:])) <= 1e-14 and np.max(np.abs(lc - lw[:, n - m:])) <= 1e-14
+
+
+def check_ring():
+    """Ring window cache: after every append, attention over the ring's valid
+    slots equals windowed decode over the whole history; slots hold token t at
+    t mod C (hand-checked layout)."""
+    rng = _rng(18)
+    hkv, d, hq, window, steps = 2, 4, 4, 5, 13
+    hist_k = rng.standard_normal((steps, 2, hkv, d))   # [t, b, Hkv, d]
+    hist_v = rng.standard_normal((steps, 2, hkv, d))
+    caps = [window, window]
+    starts = [0, window + 3]
+    ring_k = rng.standard_normal((2 * window + 3, hkv, d))   # junk before the first appends
+    ring_v = rng.standard_normal((2 * window + 3, hkv, d))
+    lens = np.array([0, 0])
+    for t in range(steps):
+        ring_k, ring_v, lens, flag = ox.ring_append_ref(ring_k, ring_v, starts, lens, caps, hist_k[t], hist_v[t])
+        assert flag == 0 and list(lens) == [t + 1, t + 1]
+        qd = rng.standard_normal((2, hq, d))
+        valid = [min(int(x), c) for x, c in zip(lens, caps)]
+        o_ring, l_ring = ox.decode_ref(qd, ring_k, ring_v, starts, valid, 0.6)
+        lin_k = np.concatenate([hist_k[:t + 1, 0], hist_k[:t + 1, 1]])
+        lin_v = np.concatenate([hist_v[:t + 1, 0], hist_v[:t + 1, 1]])
+        o_lin, l_lin = ox.decode_ref(qd, lin_k, lin_v, [0, t + 1], [t + 1, t + 1], 0.6, window=window)
+        assert np.max(np.abs(o_ring - o_lin)) <= 1e-13 and np.max(np.abs(l_ring - l_lin)) <= 1e-13, ("ring", t)
+    # 13 tokens into 5 slots: slot s holds the latest t with t mod 5 = s
+    for slot, tok in enumerate([10, 11, 12, 8, 9]):
+        assert np.array_equal(ring_k[slot], hist_k[tok, 0]) and np.array_equal(ring_v[starts[1] + slot], hist_v[tok, 1])
+    # a sequence without rows stores nothing and raises the flag
+    k3, v3, l3, f3 = ox.ring_append_ref(ring_k, ring_v, [0, 5], [3, 0], [5, 0], hist_k[0], hist_v[0])
+    assert f3 == 1 and list(l3) == [4, 0] and np.array_equal(k3[5:], ring_k[5:])
+
+
+ALL_PINS = [check_bruteforce, check_sdpa, check_closed_forms, check_invariants, check_chunked_prefill, check_append,
+            check_window, check_ring]

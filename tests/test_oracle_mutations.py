@@ -4,7 +4,9 @@ Every mutation replaces one step of the oracle with a plausible wrong version:
 a wrong head map, an off-by-one or missing causal limit, a dropped or doubled
 scale, a sign flip, a transposed operand, a missing normalisation, a dropped
 max term in the LSE, a wrong decode or prefill position, an append at the wrong
-row or without the overflow check.
+row or without the overflow check, a window one row too wide or too narrow,
+ignored or aligned to fixed blocks, a ring append into the wrong slot or
+without wrap-around.
 """
 import numpy as np
 import pytest
@@ -35,6 +37,36 @@ def _append_no_cap(k_pool, v_pool, seq_start, seq_len, seq_cap, k_new, v_new):
         k2[row], v2[row] = k_new[b], v_new[b]
         lens[b] += 1
     return k2, v2, lens, 0
+
+
+def _ring_slot_shift(k_ring, v_ring, seq_start, seq_len, seq_cap, k_new, v_new):
+    k2, v2 = np.array(k_ring, copy=True), np.array(v_ring, copy=True)
+    lens = np.array(seq_len, dtype=np.int64, copy=True)
+    flag = 0
+    for b in range(len(lens)):
+        cap = int(seq_cap[b])
+        if cap <= 0:
+            flag = 1
+            continue
+        row = int(seq_start[b]) + (int(lens[b]) + 1) % cap
+        k2[row], v2[row] = k_new[b], v_new[b]
+        lens[b] += 1
+    return k2, v2, lens, flag
+
+
+def _ring_no_wrap(k_ring, v_ring, seq_start, seq_len, seq_cap, k_new, v_new):
+    k2, v2 = np.array(k_ring, copy=True), np.array(v_ring, copy=True)
+    lens = np.array(seq_len, dtype=np.int64, copy=True)
+    flag = 0
+    for b in range(len(lens)):
+        cap = int(seq_cap[b])
+        if cap <= 0:
+            flag = 1
+            continue
+        row = int(seq_start[b]) + min(int(lens[b]), cap - 1)
+        k2[row], v2[row] = k_new[b], v_new[b]
+        lens[b] += 1
+    return k2, v2, lens, flag
 
 
 def _softmax_no_exp(s):
@@ -71,6 +103,12 @@ MUTATIONS = {
     "decode_position_past_end": ("decode_position", lambda n: n),
     "append_wrong_row": ("kv_append_ref", _append_wrong_row),
     "append_ignores_capacity": ("kv_append_ref", _append_no_cap),
+    "window_one_too_many": ("window_start", lambda p, w: max(0, p - w) if w > 0 else 0),
+    "window_one_too_few": ("window_start", lambda p, w: max(0, p - w + 2) if w > 0 else 0),
+    "window_ignored": ("window_start", lambda p, w: 0),
+    "window_in_fixed_blocks": ("window_start", lambda p, w: (p // w) * w if w > 0 else 0),
+    "ring_slot_shifted": ("ring_append_ref", _ring_slot_shift),
+    "ring_does_not_wrap": ("ring_append_ref", _ring_no_wrap),
 }
 
 
