@@ -13,9 +13,12 @@ from .xattn import (  # noqa: F401
     alloc_workspace,
     decode_splits,
     kv_append,
+    kv_append_ring,
     load_library,
     make_dims,
     workspace_size,
     xattn_decode,
+    xattn_decode_window,
     xattn_prefill,
+    xattn_prefill_window,
 )

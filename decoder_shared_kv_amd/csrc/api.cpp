@@ -110,12 +110,8 @@ AttnParams base_params(const yoco_dims* d, const yoco_kv_cache* c) {
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-yoco_status yoco_kv_append(const yoco_dims* dims, const yoco_kv_cache* cache, const void* k_new,
-                           const void* v_new, int32_t* overflow_flag, void* stream) {
+yoco_status append_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const void* k_new, const void* v_new,
+                        int32_t* overflow_flag, int ring, void* stream) {
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
   st = check_cache(cache);
@@ -133,13 +129,14 @@ yoco_status yoco_kv_append(const yoco_dims* dims, const yoco_kv_cache* cache, co
   p.overflow = overflow_flag;
   p.pool_rows = cache->pool_rows;
   p.row_bytes = dims->num_kv_heads * dims->head_dim * elem_size(dims->dtype);
+  p.ring = ring;
   if (yoco::launch_kv_append(p, dims->batch, static_cast<hipStream_t>(stream)) != hipSuccess) return YOCO_ERR_HIP;
   return YOCO_OK;
 }
 
-yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
-                               const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q, void* out,
-                               float* lse, void* stream) {
+yoco_status prefill_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
+                         const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q, int32_t window, void* out,
+                         float* lse, void* stream) {
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
   st = check_cache(cache);
@@ -155,6 +152,7 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
   p.lse = lse;
   p.cu_seqlens = cu_seqlens_q;
   p.total_q = total_q;
+  p.window = window;
   const int64_t len = max_q_len > 0 ? max_q_len : 1;
   hipError_t err;
   if (dims->dtype == YOCO_DTYPE_BF16) {
@@ -173,6 +171,71 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
     err = yoco::launch_prefill_f32(p, dims->head_dim, (int)(blocks * units), static_cast<hipStream_t>(stream));
   }
   return err == hipSuccess ? YOCO_OK : YOCO_ERR_HIP;
+}
+
+yoco_status decode_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q, int32_t max_kv_len,
+                        int64_t total_kv_len, int32_t window, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return YOCO_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned4(lse)) return YOCO_ERR_INVALID_ARG;
+  if (max_kv_len < 0 || total_kv_len < 0) return YOCO_ERR_INVALID_ARG;
+  if (window > 0) {
+    // only the last `window` rows of each sequence are read: plan for those
+    if (max_kv_len > window) max_kv_len = window;
+    const int64_t cap = (int64_t)dims->batch * window;
+    if (total_kv_len > cap) total_kv_len = cap;
+  }
+  int32_t splits, rows;
+  plan_decode(dims, max_kv_len, total_kv_len, &splits, &rows);
+  const size_t need = decode_workspace(dims, splits);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return YOCO_ERR_WORKSPACE;
+  AttnParams p = base_params(dims, cache);
+  p.q = q;
+  p.out = out;
+  p.lse = lse;
+  p.window = window;
+  p.splits = splits;
+  p.split_rows = rows;
+  p.head_chunks = head_chunks(dims);
+  p.part_o = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ml_offset(dims, splits));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dims->dtype == YOCO_DTYPE_BF16 ? yoco::launch_decode_split_bf16(p, dims->head_dim, s)
+                                                  : yoco::launch_decode_split_f32(p, dims->head_dim, s);
+  if (err != hipSuccess) return YOCO_ERR_HIP;
+  if (yoco::launch_decode_merge(p, dims->head_dim, dims->dtype, s) != hipSuccess) return YOCO_ERR_HIP;
+  return YOCO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+yoco_status yoco_kv_append(const yoco_dims* dims, const yoco_kv_cache* cache, const void* k_new,
+                           const void* v_new, int32_t* overflow_flag, void* stream) {
+  return append_impl(dims, cache, k_new, v_new, overflow_flag, 0, stream);
+}
+
+yoco_status yoco_kv_append_ring(const yoco_dims* dims, const yoco_kv_cache* cache, const void* k_new,
+                                const void* v_new, int32_t* flag, void* stream) {
+  return append_impl(dims, cache, k_new, v_new, flag, 1, stream);
+}
+
+yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
+                               const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q, void* out,
+                               float* lse, void* stream) {
+  return prefill_impl(dims, cache, q, cu_seqlens_q, max_q_len, total_q, 0, out, lse, stream);
+}
+
+yoco_status yoco_xattn_prefill_window(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
+                                      const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q,
+                                      int32_t window, void* out, float* lse, void* stream) {
+  if (window < 1) return YOCO_ERR_INVALID_ARG;
+  return prefill_impl(dims, cache, q, cu_seqlens_q, max_q_len, total_q, window, out, lse, stream);
 }
 
 yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len, int64_t total_kv_len,
@@ -195,32 +258,14 @@ yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len,
 yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
                               int32_t max_kv_len, int64_t total_kv_len, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  yoco_status st = check_dims(dims);
-  if (st != YOCO_OK) return st;
-  st = check_cache(cache);
-  if (st != YOCO_OK) return st;
-  if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return YOCO_ERR_INVALID_ARG;
-  if (lse != nullptr && !aligned4(lse)) return YOCO_ERR_INVALID_ARG;
-  if (max_kv_len < 0 || total_kv_len < 0) return YOCO_ERR_INVALID_ARG;
-  int32_t splits, rows;
-  plan_decode(dims, max_kv_len, total_kv_len, &splits, &rows);
-  const size_t need = decode_workspace(dims, splits);
-  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return YOCO_ERR_WORKSPACE;
-  AttnParams p = base_params(dims, cache);
-  p.q = q;
-  p.out = out;
-  p.lse = lse;
-  p.splits = splits;
-  p.split_rows = rows;
-  p.head_chunks = head_chunks(dims);
-  p.part_o = static_cast<float*>(workspace);
-  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ml_offset(dims, splits));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = dims->dtype == YOCO_DTYPE_BF16 ? yoco::launch_decode_split_bf16(p, dims->head_dim, s)
-                                                  : yoco::launch_decode_split_f32(p, dims->head_dim, s);
-  if (err != hipSuccess) return YOCO_ERR_HIP;
-  if (yoco::launch_decode_merge(p, dims->head_dim, dims->dtype, s) != hipSuccess) return YOCO_ERR_HIP;
-  return YOCO_OK;
+  return decode_impl(dims, cache, q, max_kv_len, total_kv_len, 0, out, lse, workspace, workspace_bytes, stream);
+}
+
+yoco_status yoco_xattn_decode_window(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
+                                     int32_t max_kv_len, int64_t total_kv_len, int32_t window, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 1) return YOCO_ERR_INVALID_ARG;
+  return decode_impl(dims, cache, q, max_kv_len, total_kv_len, window, out, lse, workspace, workspace_bytes, stream);
 }
 
 const char* yoco_status_string(yoco_status status) {

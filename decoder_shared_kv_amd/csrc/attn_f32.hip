@@ -85,7 +85,9 @@ __global__ __launch_bounds__(kPrefillF32Rows) void prefill_f32_kernel(AttnParams
     float m = -INFINITY, l = 0.f;
     int vis = r + offset + 1;
     if (vis > n_kv) vis = n_kv;
-    accumulate_rows<D>(qr, kbase, vbase, row_stride, 0, vis, p.scale_log2, m, l, acc);
+    // sliding window: rows vis - window .. vis - 1 only
+    const int lo = p.window > 0 && vis > p.window ? vis - p.window : 0;
+    accumulate_rows<D>(qr, kbase, vbase, row_stride, lo, vis, p.scale_log2, m, l, acc);
     float* dst = static_cast<float*>(p.out) + (qrow * p.hq + h) * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
@@ -107,7 +109,8 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(AttnParams p) {
   const int h = bh % p.hq;
   const int kh = h / p.group;
   int64_t start;
-  const int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
+  int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
+  n_kv = window_rows(n_kv, p.window, &start);
   const int64_t row_stride = (int64_t)p.hkv * D;
   const float* kbase = static_cast<const float*>(p.k) + start * row_stride + (int64_t)kh * D;
   const float* vbase = static_cast<const float*>(p.v) + start * row_stride + (int64_t)kh * D;

@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
   __bf16* vt = reinterpret_cast<__bf16*>(lds) + wave * (U * D * kVtStride);
 
   int64_t start;
-  const int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
+  int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
+  n_kv = window_rows(n_kv, p.window, &start);   // sliding window: the last `window` rows
   const int j0 = split * p.split_rows;
   int j1 = (split == p.splits - 1) ? n_kv : j0 + p.split_rows;
   if (j1 > n_kv) j1 = n_kv;

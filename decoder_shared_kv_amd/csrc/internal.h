@@ -24,6 +24,7 @@ struct AttnParams {
   int32_t hkv;
   int32_t group;              // hq / hkv
   float scale_log2;           // scale * log2(e): scores are kept in the base-2 domain
+  int32_t window;             // sliding window in positions (0: none, plain causal)
   // prefill grid
   int32_t pos_blocks;         // position blocks covering max_q_len
   // decode split plan
@@ -45,6 +46,7 @@ struct AppendParams {
   int32_t* overflow;
   int64_t pool_rows;
   int32_t row_bytes;          // Hkv * head_dim * element size (multiple of 16)
+  int32_t ring;               // 1: ring window cache, the row goes to slot seq_len mod seq_cap
 };
 
 // Host launchers (one per kernel family); each returns the hipGetLastError code.
@@ -119,6 +121,16 @@ __device__ __forceinline__ int32_t readable_rows(const int64_t* seq_start, const
   if (n < 0) n = 0;
   *start_out = s;
   return (int32_t)n;
+}
+
+// Decode under a sliding window: of the n readable rows only the last `window`
+// are visible to the query at position n - 1.
+__device__ __forceinline__ int32_t window_rows(int32_t n, int32_t window, int64_t* start) {
+  if (window > 0 && n > window) {
+    *start += n - window;
+    return window;
+  }
+  return n;
 }
 
 }  // namespace yoco

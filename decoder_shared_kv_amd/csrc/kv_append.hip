@@ -1,4 +1,6 @@
-// kv_append: one new K^,V^ row per sequence into the shared cache.
+// kv_append: one new K^,V^ row per sequence into the shared cache, or into a
+// ring window cache (the Self-Decoder's sliding-window layers keep only the last
+// C tokens: page "YOCO", section "Self-Decoder：把历史编码成可复用的全局表示").
 //
 // The new token's row exists before any Cross-Decoder layer reads the cache
 // (page "YOCO", section "Decode：新 token 仍需经过两部分"). One workgroup per
@@ -12,12 +14,15 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int64_t start = p.seq_start[b];
   const int32_t len = p.seq_len[b];
   const int32_t cap = p.seq_cap[b];
-  const bool ok = len >= 0 && len < cap && start >= 0 && start + len < p.pool_rows;
+  // shared cache: the next free row; ring window cache: slot len mod cap, which
+  // holds the token cap positions older (or nothing yet)
+  const int64_t slot = p.ring ? (cap > 0 && len >= 0 ? len % cap : -1) : (len < cap ? len : -1);
+  const bool ok = len >= 0 && slot >= 0 && start >= 0 && start + slot < p.pool_rows;
   if (!ok) {
     if (threadIdx.x == 0 && p.overflow != nullptr) p.overflow[0] = 1;
     return;
   }
-  const int64_t row = start + len;
+  const int64_t row = start + slot;
   const int n16 = p.row_bytes / 16;
   const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(p.k_new) + (int64_t)b * p.row_bytes);
   const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(p.v_new) + (int64_t)b * p.row_bytes);

@@ -259,20 +259,26 @@ __device__ __forceinline__ void qk_step(const YOCO_LDS char* ks, const ReadOffs<
 }
 
 // Online-softmax bookkeeping of one tile: mask, row max, lazy rescale of the
-// running state. Returns -m for the exponentials.
-template <int D, bool MASK>
+// running state. Returns -m for the exponentials. MASK: 0 none, 1 keys past the
+// row's position (causal), 2 also keys before its window.
+template <int D, int MASK>
 __device__ __forceinline__ float softmax_max(f32x16 (&s)[2], f32x16 (&acc)[D / 32], float& m, float& l, int key0,
-                                             int my_pos, int n_kv, float c, int hf) {
+                                             int pos, int window, float c, int hf) {
   // register r of chain kb holds key key0 + 32kb + 8(r/4) + 4hf + r%4; keys past
-  // min(my_pos, n_kv - 1) are masked: one compare with a constant per register
-  const int lim = min(my_pos, n_kv - 1) - key0 - 4 * hf;
+  // the row's (clamped) position pos, or before pos - window + 1, are masked:
+  // compares with constants per register
+  const int lim = pos - key0 - 4 * hf;
+  const int lim_lo = lim - window + 1;
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      if constexpr (MASK) {
-        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+      const int rel = kb * 32 + 8 * (r >> 2) + (r & 3);
+      if constexpr (MASK == 1) {
+        if (rel > lim) s[kb][r] = -INFINITY;
+      } else if constexpr (MASK == 2) {
+        if (rel > lim || rel < lim_lo) s[kb][r] = -INFINITY;
       }
       mx = fmaxf(mx, s[kb][r]);
     }
@@ -316,9 +322,9 @@ __device__ __forceinline__ void pv_index(int j, int& kb, int& cc, int& t) {
 // Softmax and O^T += V^T P^T of one tile whose S^T is in s. The exponentials
 // of keys 32..63 are spread between the PV MFMAs of keys 0..31, which run
 // while they issue.
-template <int D, bool MASK>
+template <int D, int MASK>
 __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<D>& ro, f32x16 (&s)[2],
-                                        f32x16 (&acc)[D / 32], float& m, float& l, int key0, int my_pos, int n_kv,
+                                        f32x16 (&acc)[D / 32], float& m, float& l, int key0, int pos, int window,
                                         float c, int hf) {
   constexpr int NV = D / 8;        // PV steps: (kb, cc, t)
   constexpr int RA = kReadsAhead;
@@ -331,7 +337,7 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
     va[j] = read_v<D>(vs, ro, kb, cc, t);
   }
   sched_fence();
-  const float neg_m = softmax_max<D, MASK>(s, acc, m, l, key0, my_pos, n_kv, c, hf);
+  const float neg_m = softmax_max<D, MASK>(s, acc, m, l, key0, pos, window, c, hf);
   uint32_t w[2][2][4];
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
@@ -415,16 +421,24 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     const int wg_last_key = min(wg_last_row + offset, n_kv - 1);
     const int n_tiles = wg_last_key >= 0 ? wg_last_key / kBN + 1 : 0;
     const int r0 = pw * pos_per_wg + pbl * kPrefillRowsPerWave;
-    const int my_pos = r0 + qj + offset;
+    const int my_pos = min(r0 + qj + offset, n_kv - 1);   // rows past the last cache row see every row
     const bool wave_active = r0 < n_q;
     const int wave_max_pos = min(r0 + kPrefillRowsPerWave, n_q) - 1 + offset;
-    // tiles below full_tiles need no mask for any row of this wave
+    // tiles below full_tiles need no causal mask for any row of this wave
     const int full_tiles = min((r0 + offset + 1) / kBN, n_kv / kBN);
+    // sliding window: the workgroup starts at the first tile its first row sees;
+    // a wave skips tiles wholly before its rows' windows and masks the lower
+    // edge below band_full (keys from there on lie in every row's window)
+    const int win = p.window;
+    const int kt_lo = win > 0 ? max(0, min(pw * pos_per_wg + offset, n_kv - 1) - win + 1) / kBN : 0;
+    const int wave_key_lo = win > 0 ? max(0, min(r0 + offset, n_kv - 1) - win + 1) : 0;
+    const int band_full = win > 0 ? min(wave_max_pos, n_kv - 1) - win + 1 : 0;
 
     // the tiles ahead go out first: they have the longest way
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
-      if (st < n_tiles) issue_tile<D>(is, kbase, vbase, row_stride, st * kBN, n_kv - 1, smem + st * kStage);
+      if (kt_lo + st < n_tiles)
+        issue_tile<D>(is, kbase, vbase, row_stride, (kt_lo + st) * kBN, n_kv - 1, smem + ((kt_lo + st) % kStages) * kStage);
 
     bf16x8 qf[D / 16];
     {
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
     float m = -INFINITY, l = 0.f;
 
-    for (int kt = 0; kt < n_tiles; ++kt) {
+    for (int kt = kt_lo; kt < n_tiles; ++kt) {
       // tile kt has landed in LDS (this thread's part): at most the tiles
       // requested after it may still be in flight
       wait_tiles<L>(min(kStages - 2, n_tiles - 1 - kt));
@@ -451,17 +465,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
         issue_tile<D>(is, kbase, vbase, row_stride, (kt + kStages - 1) * kBN, n_kv - 1,
                       smem + ((kt + kStages - 1) % kStages) * kStage);
       const int key0 = kt * kBN;
-      if (wave_active && key0 <= wave_max_pos) {
+      if (wave_active && key0 <= wave_max_pos && key0 + kBN > wave_key_lo) {
         const YOCO_LDS char* ks = smem + (kt % kStages) * kStage;
         const YOCO_LDS char* vs = ks + Geom<D>::kTileBytes;
         f32x16 s[2];
-        if (kt >= full_tiles) {
-          qk_step<D>(ks, ro, qf, s);
-          sv_step<D, true>(vs, ro, s, acc, m, l, key0, my_pos, n_kv, c, hf);
-        } else {
-          qk_step<D>(ks, ro, qf, s);
-          sv_step<D, false>(vs, ro, s, acc, m, l, key0, my_pos, n_kv, c, hf);
-        }
+        qk_step<D>(ks, ro, qf, s);
+        if (win > 0 && key0 < band_full)
+          sv_step<D, 2>(vs, ro, s, acc, m, l, key0, my_pos, win, c, hf);
+        else if (kt >= full_tiles)
+          sv_step<D, 1>(vs, ro, s, acc, m, l, key0, my_pos, win, c, hf);
+        else
+          sv_step<D, 0>(vs, ro, s, acc, m, l, key0, my_pos, win, c, hf);
       }
     }
     wait_vm_lgkm0<0>();

@@ -5,8 +5,8 @@ current HIP stream; every step of the path runs in the library's kernels.
 There is no fallback: if the library is missing, loading raises.
 
 The functions mirror the C ABI (include/yoco_xattn.h) one to one:
-``kv_append``, ``xattn_prefill``, ``xattn_decode``, ``workspace_size``,
-``decode_splits``.
+``kv_append``, ``kv_append_ring``, ``xattn_prefill``, ``xattn_prefill_window``,
+``xattn_decode``, ``xattn_decode_window``, ``workspace_size``, ``decode_splits``.
 """
 from __future__ import annotations
 
@@ -24,7 +24,8 @@ YOCO_OK = 0
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip launch failed"}
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
-EXPORTS = ("yoco_kv_append", "yoco_xattn_prefill", "yoco_xattn_decode", "yoco_xattn_workspace_size",
+EXPORTS = ("yoco_kv_append", "yoco_kv_append_ring", "yoco_xattn_prefill", "yoco_xattn_prefill_window",
+           "yoco_xattn_decode", "yoco_xattn_decode_window", "yoco_xattn_workspace_size",
            "yoco_xattn_decode_splits", "yoco_status_string")
 
 
@@ -58,17 +59,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.c_void_p
     dims_p = ctypes.POINTER(Dims)
     cache_p = ctypes.POINTER(KvCache)
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.yoco_kv_append.argtypes = [dims_p, cache_p, P, P, P, P]
-    lib.yoco_xattn_prefill.argtypes = [dims_p, cache_p, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P]
-    lib.yoco_xattn_decode.argtypes = [dims_p, cache_p, P, ctypes.c_int32, ctypes.c_int64, P, P, P, ctypes.c_size_t,
-                                      P]
+    lib.yoco_kv_append_ring.argtypes = [dims_p, cache_p, P, P, P, P]
+    lib.yoco_xattn_prefill.argtypes = [dims_p, cache_p, P, P, i32, i64, P, P, P]
+    lib.yoco_xattn_prefill_window.argtypes = [dims_p, cache_p, P, P, i32, i64, i32, P, P, P]
+    lib.yoco_xattn_decode.argtypes = [dims_p, cache_p, P, i32, i64, P, P, P, ctypes.c_size_t, P]
+    lib.yoco_xattn_decode_window.argtypes = [dims_p, cache_p, P, i32, i64, i32, P, P, P, ctypes.c_size_t, P]
     lib.yoco_xattn_workspace_size.argtypes = [dims_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.yoco_xattn_decode_splits.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                              ctypes.POINTER(ctypes.c_int32)]
     lib.yoco_status_string.argtypes = [ctypes.c_int]
     lib.yoco_status_string.restype = ctypes.c_char_p
-    for name in ("yoco_kv_append", "yoco_xattn_prefill", "yoco_xattn_decode", "yoco_xattn_workspace_size",
-                 "yoco_xattn_decode_splits"):
+    for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -124,6 +127,17 @@ def kv_append(cache: SharedKV, k_new: torch.Tensor, v_new: torch.Tensor, overflo
                               _stream(stream)), "yoco_kv_append")
 
 
+def kv_append_ring(cache: SharedKV, k_new: torch.Tensor, v_new: torch.Tensor, flag: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Append one row per sequence to ring window caches (slot seq_len mod seq_cap); see yoco_kv_append_ring."""
+    lib = load_library()
+    batch = int(cache.seq_len.shape[0])
+    dims = _dims_for(cache, cache.k.shape[1], 1.0, batch)
+    desc = cache.descriptor()
+    _check(lib.yoco_kv_append_ring(ctypes.byref(dims), ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(flag),
+                                   _stream(stream)), "yoco_kv_append_ring")
+
+
 def xattn_prefill(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, max_q_len: int, scale: float,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
     """Causal prefill over packed queries q [total_q, Hq, d]; returns out (and fills lse [Hq, total_q])."""
@@ -136,6 +150,23 @@ def xattn_prefill(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, ma
     desc = cache.descriptor()
     _check(lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), _ptr(cu_seqlens), int(max_q_len),
                                   int(total_q), _ptr(out), _ptr(lse), _stream(stream)), "yoco_xattn_prefill")
+    return out
+
+
+def xattn_prefill_window(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, max_q_len: int, window: int,
+                         scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         stream=None):
+    """Sliding-window prefill: row at position p attends rows max(0, p - window + 1) .. p."""
+    lib = load_library()
+    total_q, hq, _ = q.shape
+    batch = int(cu_seqlens.shape[0]) - 1
+    if out is None:
+        out = torch.empty_like(q)
+    dims = _dims_for(cache, hq, scale, batch)
+    desc = cache.descriptor()
+    _check(lib.yoco_xattn_prefill_window(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), _ptr(cu_seqlens),
+                                         int(max_q_len), int(total_q), int(window), _ptr(out), _ptr(lse),
+                                         _stream(stream)), "yoco_xattn_prefill_window")
     return out
 
 
@@ -183,4 +214,21 @@ def xattn_decode(cache: SharedKV, q: torch.Tensor, max_kv_len: int, scale: float
                                  _ptr(out),
                                  _ptr(lse), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                  _stream(stream)), "yoco_xattn_decode")
+    return out
+
+
+def xattn_decode_window(cache: SharedKV, q: torch.Tensor, max_kv_len: int, window: int, scale: float,
+                        workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None, total_kv_len: int = 0):
+    """Decode over a full cache with a sliding window: the last min(seq_len, window) rows only."""
+    lib = load_library()
+    batch, hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    dims = _dims_for(cache, hq, scale, batch)
+    desc = cache.descriptor()
+    _check(lib.yoco_xattn_decode_window(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), int(max_kv_len),
+                                        int(total_kv_len), int(window), _ptr(out), _ptr(lse), _ptr(workspace),
+                                        int(workspace.numel() * workspace.element_size()), _stream(stream)),
+           "yoco_xattn_decode_window")
     return out

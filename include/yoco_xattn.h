@@ -139,6 +139,58 @@ yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache,
                               void* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Sliding-window attention (the Self-Decoder's efficient attention)
+ * -----------------------------------------------------------------
+ * The current position sees only the tokens of a fixed window of size C, so a
+ * layer's decode cache is O(C) rather than O(N) (page "YOCO", section
+ * "Self-Decoder：把历史编码成可复用的全局表示"; page "YOCO 深度技术分析", section
+ * 2.3, C = 1024). Reading: a window of size C holds the C most recent positions,
+ * the query's own included: position p attends rows max(0, p - C + 1) .. p.
+ * Here the cache descriptor describes one layer's K, V; everything else is as
+ * in the calls above.
+ */
+
+/*
+ * yoco_xattn_prefill_window -- yoco_xattn_prefill with the band mask: query row
+ * r at position p (as in yoco_xattn_prefill) attends rows max(0, p - window + 1)
+ * .. p. window >= 1 (YOCO_ERR_INVALID_ARG otherwise); a window of at least the
+ * sequence length gives yoco_xattn_prefill's result. Tiles wholly outside every
+ * row's window are neither loaded nor computed.
+ */
+yoco_status yoco_xattn_prefill_window(const yoco_dims* dims, const yoco_kv_cache* cache,
+                                      const void* q, const int32_t* cu_seqlens_q,
+                                      int32_t max_q_len, int64_t total_q, int32_t window,
+                                      void* out, float* lse, void* stream);
+
+/*
+ * yoco_xattn_decode_window -- yoco_xattn_decode over a full (linear) cache with
+ * the band mask: the query at position seq_len[b]-1 attends the last
+ * min(seq_len[b], window) readable rows only; only those are read. window >= 1.
+ * Workspace as for yoco_xattn_decode with the same max_kv_len.
+ */
+yoco_status yoco_xattn_decode_window(const yoco_dims* dims, const yoco_kv_cache* cache,
+                                     const void* q, int32_t max_kv_len, int64_t total_kv_len,
+                                     int32_t window, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * yoco_kv_append_ring -- append to ring window caches (decode cache of a window
+ * of C = seq_cap[b] positions). Sequence b's row goes to pool row seq_start[b] +
+ * (seq_len[b] mod seq_cap[b]), replacing the token C positions older, and
+ * seq_len[b] (which counts every token appended so far) is incremented. A
+ * sequence with seq_cap[b] <= 0 (or whose slot lies outside the pool) stores
+ * nothing and sets *flag to 1 (never cleared; NULL disables it).
+ * Decode over a ring is plain yoco_xattn_decode on the same descriptor: its
+ * readable rows min(seq_len, seq_cap) are exactly the last C tokens (in rotated
+ * slot order, which softmax attention does not depend on); pass max_kv_len =
+ * the largest seq_cap.
+ *   k_new, v_new  [device] [B, Hkv, head_dim], same dtype as the cache.
+ */
+yoco_status yoco_kv_append_ring(const yoco_dims* dims, const yoco_kv_cache* cache,
+                                const void* k_new, const void* v_new,
+                                int32_t* flag, void* stream);
+
 /* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len (any
  * total_kv_len, any smaller max_kv_len). */
 yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes);

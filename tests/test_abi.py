@@ -127,6 +127,28 @@ def test_append_argument_checks(lib):
     assert A(FAKE, FAKE, FAKE + 1, None) == 1
 
 
+def test_window_argument_checks(lib):
+    dims, cache = _dims(batch=2), _cache()
+    need = ctypes.c_size_t(0)
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5000, ctypes.byref(need)) == 0
+    PW = lambda *a: lib.yoco_xattn_prefill_window(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    DW = lambda *a: lib.yoco_xattn_decode_window(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    for w in (0, -1, -1024):
+        assert PW(FAKE, FAKE, 10, 10, w, FAKE, None, None) == 1
+        assert DW(FAKE, 5000, 0, w, FAKE, None, FAKE, need.value, None) == 1
+    # the other checks are the unwindowed calls'
+    assert PW(None, FAKE, 10, 10, 64, FAKE, None, None) == 1
+    assert PW(FAKE, FAKE, 10, 0, 64, FAKE, None, None) == 0       # nothing to do, nothing launched
+    assert DW(FAKE, 5000, 0, 64, FAKE, None, FAKE + 4, need.value, None) == 3
+    assert DW(FAKE, 5000, 0, 64, FAKE, None, None, need.value, None) == 3
+    assert lib.yoco_xattn_prefill_window(ctypes.byref(_dims(head_dim=96)), ctypes.byref(cache), FAKE, FAKE, 10,
+                                         10, 64, FAKE, None, None) == 2
+    A = lambda *a: lib.yoco_kv_append_ring(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    assert A(None, FAKE, None, None) == 1
+    assert A(FAKE, FAKE + 2, None, None) == 1
+    assert A(FAKE, FAKE, FAKE + 1, None) == 1
+
+
 def test_split_plan():
     # decode: 8 x 131072 rows, Hkv=2 -> 16 (sequence, KV head) units, ~1024 workgroups in total
     s, r = dk.decode_splits(8, 16, 2, 128, X.torch.bfloat16, 131072)
