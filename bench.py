@@ -11,6 +11,8 @@ Q and O, over the measured call time) is reported beside it in `decode`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --workload decode_1m     (long-context decode, 64 steps x 16 layers)
+       python bench.py --workload swa           (Self-Decoder sliding window, C = 1024: 32K prefill,
+                                                  token decode over ring window caches)
        python bench.py --copy-probe             (plain copy kernel of known size, for counter scaling)
 """
 from __future__ import annotations
@@ -122,7 +124,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="default", choices=["default", "decode_1m", "ragged"])
+    ap.add_argument("--workload", default="default", choices=["default", "decode_1m", "ragged", "swa"])
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--skip", default="", help="comma list of modes to leave out: prefill,decode (profiling only)")
     args = ap.parse_args()
@@ -146,6 +148,8 @@ def main():
         return bench_decode_1m(args, torch, dk, synth, dev)
     if args.workload == "ragged":
         return bench_ragged(args, torch, dk, synth, dev)
+    if args.workload == "swa":
+        return bench_swa(args, torch, dk, synth, dev)
 
     skip = set(x for x in args.skip.split(",") if x)
     wp = synth.WORKLOADS["prefill_32k"]
@@ -295,6 +299,89 @@ def bench_decode_1m(args, torch, dk, synth, dev):
                      "traffic": None, "kernel": "decode_split_bf16_kernel<128,2> + decode_merge_kernel",
                      "avg_call_ms": ms / calls, "algorithmic_bytes_per_call": nbytes / calls},
         "total_ms": ms}), flush=True)
+
+
+SWA_WINDOW = 1024   # YOCO's Self-Decoder window C
+
+
+def swa_flops(n, window, hq, d):
+    """4 d Hq per (query, visible key) pair; position p sees min(p + 1, C) keys."""
+    c = min(window, n)
+    return 4.0 * d * hq * (c * (c + 1) / 2.0 + (n - c) * c)
+
+
+def bench_swa(args, torch, dk, synth, dev):
+    """Sliding-window attention with C = 1024 at the prefill workload's shape
+    (16 layer calls of a 32K prompt, Hq=16, Hkv=4), then token decode at the
+    decode workload's heads (B=8, Hq=16, Hkv=2): per layer one ring append and
+    one decode over that layer's full ring of C rows (16 rings)."""
+    wp = synth.WORKLOADS["prefill_32k"]
+    wd = synth.WORKLOADS["decode_128k"]
+    C = SWA_WINDOW
+    n = int(wp.seq_lens[0])
+    t = time.perf_counter()
+    pc, pcache, qs = make_prefill(dk, synth, dev, wp)
+    cu = pc.cu_seqlens.to(dev)
+    out_p = torch.empty_like(qs[0])
+    lse_p = torch.empty(wp.q_heads, n, device=dev, dtype=torch.float32)
+    g = torch.Generator(device=dev).manual_seed(5)
+    B, L = wd.batch, wd.layers
+    rings = []
+    for _ in range(L):
+        kr = (torch.randn(B * C, wd.kv_heads, wd.head_dim, device=dev, generator=g) * wd.value_std).to(torch.bfloat16)
+        vr = (torch.randn(B * C, wd.kv_heads, wd.head_dim, device=dev, generator=g) * wd.value_std).to(torch.bfloat16)
+        rings.append(dk.SharedKV(kr, vr, torch.arange(B, device=dev, dtype=torch.int64) * C,
+                                 torch.full((B,), 131071, device=dev, dtype=torch.int32),
+                                 torch.full((B,), C, device=dev, dtype=torch.int32)))
+    qd = (torch.randn(L, B, wd.q_heads, wd.head_dim, device=dev, generator=g) * wd.value_std).to(torch.bfloat16)
+    kn = (torch.randn(B, wd.kv_heads, wd.head_dim, device=dev, generator=g) * wd.value_std).to(torch.bfloat16)
+    ws = dk.alloc_workspace(rings[0], wd.q_heads, C)
+    out_d = torch.empty(B, wd.q_heads, wd.head_dim, device=dev, dtype=torch.bfloat16)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def prefill():
+        for layer in range(wp.layers):
+            dk.xattn_prefill_window(pcache, qs[layer], cu, n, C, pc.scale, out=out_p, lse=lse_p)
+
+    def decode_step():
+        for layer in range(L):
+            dk.kv_append_ring(rings[layer], kn, kn, flag)
+            dk.xattn_decode(rings[layer], qd[layer], C, wd.scale, ws, out=out_d)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode_step()
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(args.steps):
+        prefill()
+    ev[1].record()
+    ev[2].record()
+    for _ in range(args.steps):
+        decode_step()
+    ev[3].record()
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    layer_s = ev[0].elapsed_time(ev[1]) / 1e3 / (args.steps * wp.layers)
+    flops = swa_flops(n, C, wp.q_heads, wp.head_dim)
+    tfl = flops / layer_s / 1e12
+    dec_layer_us = ev[2].elapsed_time(ev[3]) * 1e3 / (args.steps * L)
+    print(json.dumps({
+        "metric": "sliding-window prefill TFLOP/s (% MFMA peak) @32K, C=1024; window decode us per layer",
+        "value": tfl, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": layer_s * 1e3 * wp.layers, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1)/sqrt(128) bf16)",
+        "config": {"workload": "sliding window C=1024: prefill B=1 N=32768 Hq=16 Hkv=4 d=128, 16 layers; "
+                               "decode B=8 Hq=16 Hkv=2 d=128, ring append + decode per layer, 16 layers",
+                   "global_batch": 1, "seq_len": n, "window": C, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": tfl, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tfl / BF16_DENSE_PEAK_TFLOPS, "traffic": None, "kernel": "prefill_bf16_kernel<128>",
+                     "avg_launch_ms": layer_s * 1e3, "algorithmic_per_launch": flops},
+        "decode": {"us_per_layer": dec_layer_us, "bytes_per_call": B * C * wd.kv_heads * wd.head_dim * 4,
+                   "note": "ring append + decode of C rows per layer; 16 rings of 8 MiB fit the 256 MB "
+                           "Infinity Cache, so this is a latency figure, not an HBM rate"}}), flush=True)
 
 
 def bench_ragged(args, torch, dk, synth, dev):
