@@ -13,3 +13,10 @@ from .xattn import (  # noqa: F401
     softmax_weights,
     visible_rows,
 )
+from .producer import (  # noqa: F401
+    YOCOPP_LAMBDA,
+    kv_combine_ref,
+    kv_project_ref,
+    project_append_ref,
+    rmsnorm_ref,
+)

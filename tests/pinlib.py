@@ -31,6 +31,7 @@ import os
 import numpy as np
 import torch
 
+import oracle.producer as op
 import oracle.xattn as ox
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -424,5 +425,107 @@ def check_ring():
     assert f3 == 1 and list(l3) == [4, 0] and np.array_equal(k3[5:], ring_k[5:])
 
 
+# ---------------------------------------------------------------------------
+# the producer: RMSNorm, projection, YOCO++ combine, append into the cache
+# ---------------------------------------------------------------------------
+
+def check_rmsnorm():
+    """RMSNorm against torch's rms_norm in float64, a constant row, scale
+    invariance (eps = 0), the row mean of (y / gamma)^2 = 1 (eps = 0), and a
+    hand-worked row."""
+    import torch.nn.functional as F
+    rng = _rng(19)
+    x = rng.standard_normal((7, 48)) * 3.0
+    g = rng.standard_normal(48)
+    for eps in (1e-6, 0.5):
+        y = op.rmsnorm_ref(x, g, eps)
+        ref = F.rms_norm(torch.from_numpy(x), (48,), weight=torch.from_numpy(g), eps=eps).numpy()
+        assert np.max(np.abs(y - ref)) <= 1e-13, ("rms_norm", eps)
+    y1 = op.rmsnorm_ref(np.full((1, 5), -2.0), np.arange(1.0, 6.0), 0.0)
+    assert np.max(np.abs(y1 - (-np.arange(1.0, 6.0)))) <= 1e-15, "constant row"
+    y0 = op.rmsnorm_ref(x, g, 0.0)
+    assert np.max(np.abs(op.rmsnorm_ref(5.5 * x, g, 0.0) - y0)) <= 1e-13, "scale invariance"
+    assert np.max(np.abs(np.mean((y0 / g) ** 2, axis=1) - 1.0)) <= 1e-13
+    # [3, 4], gain [1, 2], eps 0: rms = sqrt(12.5) -> [3, 8] / sqrt(12.5)
+    yh = op.rmsnorm_ref(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.0)
+    assert np.max(np.abs(yh - np.array([[3.0, 8.0]]) / math.sqrt(12.5))) <= 1e-15
+
+
+def _brute_project(x, g, wk, wv, eps):
+    out_k, out_v = [], []
+    for row in x:
+        ms = math.fsum(float(a) * float(a) for a in row) / len(row)
+        y = [float(a) / math.sqrt(ms + eps) * float(gg) for a, gg in zip(row, g)]
+        out_k.append([math.fsum(y[i] * float(wk[i, j]) for i in range(len(y))) for j in range(wk.shape[1])])
+        out_v.append([math.fsum(y[i] * float(wv[i, j]) for i in range(len(y))) for j in range(wv.shape[1])])
+    return np.array(out_k), np.array(out_v)
+
+
+def check_project():
+    """K̂ = RMSNorm(x) W_K, V̂ = RMSNorm(x) W_V: pure-Python loops on tiny shapes,
+    identity weights (K̂ = the normalised row), K and V not swapped."""
+    rng = _rng(20)
+    x = rng.standard_normal((5, 12))
+    g = rng.standard_normal(12)
+    wk = rng.standard_normal((12, 8))
+    wv = rng.standard_normal((12, 8))
+    k, v = op.kv_project_ref(x, g, wk, wv, 1e-5)
+    kb, vb = _brute_project(x, g, wk, wv, 1e-5)
+    assert np.max(np.abs(k - kb)) <= 1e-13 and np.max(np.abs(v - vb)) <= 1e-13, "projection brute force"
+    k, v = op.kv_project_ref(x, g, np.eye(12), 2.0 * np.eye(12), 0.0)
+    y = op.rmsnorm_ref(x, g, 0.0)
+    assert np.max(np.abs(k - y)) <= 1e-15 and np.max(np.abs(v - 2.0 * y)) <= 1e-15, "identity weights"
+
+
+def check_combine():
+    """YOCO++ residual: the pages' initialisation (a1 = 0, a2 = 1/lambda) gives
+    YOCO's rows; (1/lambda, 0) gives the bottom layer's rows; lambda = 35; a
+    hand-worked value."""
+    rng = _rng(21)
+    x = rng.standard_normal((6, 16))
+    g = rng.standard_normal(16)
+    wk, wv = rng.standard_normal((16, 8)), rng.standard_normal((16, 8))
+    k1, v1 = rng.standard_normal((6, 8)), rng.standard_normal((6, 8))
+    lam = op.YOCOPP_LAMBDA
+    assert lam == 35.0
+    k, v = op.kv_project_ref(x, g, wk, wv, 1e-6)
+    init = {"k1": k1, "v1": v1, "ak": (0.0, 1.0 / lam), "av": (0.0, 1.0 / lam), "lam": lam}
+    ki, vi = op.kv_project_ref(x, g, wk, wv, 1e-6, init)
+    assert np.max(np.abs(ki - k)) <= 1e-13 * np.max(np.abs(k)) and np.max(np.abs(vi - v)) <= 1e-13 * np.max(np.abs(v))
+    bottom = {"k1": k1, "v1": v1, "ak": (1.0 / lam, 0.0), "av": (1.0 / lam, 0.0), "lam": lam}
+    kb, vb = op.kv_project_ref(x, g, wk, wv, 1e-6, bottom)
+    assert np.max(np.abs(kb - k1)) <= 1e-14 and np.max(np.abs(vb - v1)) <= 1e-14
+    mixed = {"k1": k1, "v1": v1, "ak": (0.01, 0.02), "av": (0.03, -0.01), "lam": lam}
+    km, vm = op.kv_project_ref(x, g, wk, wv, 1e-6, mixed)
+    assert np.max(np.abs(km - 35.0 * (0.01 * k1 + 0.02 * k))) <= 1e-13
+    assert np.max(np.abs(vm - 35.0 * (0.03 * v1 - 0.01 * v))) <= 1e-13
+    assert abs(op.kv_combine_ref(np.array(2.0), np.array(4.0), 0.1, 0.2, 35.0) - 35.0 * (0.4 + 0.4)) <= 1e-13
+
+
+def check_project_append():
+    """Projected rows land after each sequence's valid rows; a chunk that does
+    not fit changes nothing of its sequence and raises the flag; decode-style
+    single rows are plain appends."""
+    rng = _rng(22)
+    hkv, d, dm = 2, 4, 10
+    kp = rng.standard_normal((30, hkv, d))
+    vp = rng.standard_normal((30, hkv, d))
+    st, ln, cap = [0, 10, 20], [3, 0, 8], [10, 10, 10]
+    cu = [0, 4, 9, 12]                     # 4, 5 and 3 new rows; sequence 2 has room for 2 only
+    x = rng.standard_normal((12, dm))
+    g = rng.standard_normal(dm)
+    wk, wv = rng.standard_normal((dm, hkv * d)), rng.standard_normal((dm, hkv * d))
+    k2, v2, ln2, flag = op.project_append_ref(kp, vp, st, ln, cap, cu, x, g, wk, wv, 1e-6)
+    k, v = op.kv_project_ref(x, g, wk, wv, 1e-6)
+    assert list(ln2) == [7, 5, 8] and flag == 1
+    assert np.array_equal(k2[3:7].reshape(4, -1), k[0:4]) and np.array_equal(v2[10:15].reshape(5, -1), v[4:9])
+    changed = [i for i in range(30) if not np.array_equal(k2[i], kp[i]) or not np.array_equal(v2[i], vp[i])]
+    assert changed == list(range(3, 7)) + list(range(10, 15)), changed
+    # one row per sequence = the per-token append of the projected row
+    k3, v3, ln3, f3 = op.project_append_ref(kp, vp, st, ln, cap, [0, 1, 2, 3], x[:3], g, wk, wv, 1e-6)
+    ka, va, lna, fa = ox.kv_append_ref(kp, vp, st, ln, cap, k[:3].reshape(3, hkv, d), v[:3].reshape(3, hkv, d))
+    assert np.array_equal(k3, ka) and np.array_equal(v3, va) and list(ln3) == list(lna) and f3 == fa == 0
+
+
 ALL_PINS = [check_bruteforce, check_sdpa, check_closed_forms, check_invariants, check_chunked_prefill, check_append,
-            check_window, check_ring]
+            check_window, check_ring, check_rmsnorm, check_project, check_combine, check_project_append]

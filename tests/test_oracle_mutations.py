@@ -6,11 +6,14 @@ scale, a sign flip, a transposed operand, a missing normalisation, a dropped
 max term in the LSE, a wrong decode or prefill position, an append at the wrong
 row or without the overflow check, a window one row too wide or too narrow,
 ignored or aligned to fixed blocks, a ring append into the wrong slot or
-without wrap-around.
+without wrap-around, an RMSNorm with sum for mean, eps outside the root, no or
+early gain, K and V weights swapped, the YOCO++ weights swapped or lambda
+dropped, projected rows appended at the sequence start or partially.
 """
 import numpy as np
 import pytest
 
+import oracle.producer as op
 import oracle.xattn as ox
 import pinlib
 
@@ -69,6 +72,66 @@ def _ring_no_wrap(k_ring, v_ring, seq_start, seq_len, seq_cap, k_new, v_new):
     return k2, v2, lens, flag
 
 
+def _rms_sum_not_mean(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * gamma
+
+
+def _rms_eps_outside(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * gamma
+
+
+def _rms_no_gain(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _rms_gain_first(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64) * gamma
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _project_swapped(x, gamma, w_k, w_v, eps, combine=None):
+    y = op.rmsnorm_ref(x, gamma, eps)
+    return y @ np.asarray(w_v, dtype=np.float64), y @ np.asarray(w_k, dtype=np.float64)
+
+
+def _append_chunk_at_start(k_pool, v_pool, seq_start, seq_len, seq_cap, cu, x, gamma, w_k, w_v, eps, combine=None):
+    hkv, d = k_pool.shape[1], k_pool.shape[2]
+    k, v = op.kv_project_ref(x, gamma, w_k, w_v, eps, combine)
+    k2, v2 = np.array(k_pool, dtype=np.float64), np.array(v_pool, dtype=np.float64)
+    lens = np.array(seq_len, dtype=np.int64)
+    flag = 0
+    for b in range(len(lens)):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        if lens[b] + r1 - r0 > int(seq_cap[b]):
+            flag = 1
+            continue
+        base = int(seq_start[b])
+        k2[base:base + r1 - r0] = k[r0:r1].reshape(-1, hkv, d)
+        v2[base:base + r1 - r0] = v[r0:r1].reshape(-1, hkv, d)
+        lens[b] += r1 - r0
+    return k2, v2, lens, flag
+
+
+def _append_partial_chunk(k_pool, v_pool, seq_start, seq_len, seq_cap, cu, x, gamma, w_k, w_v, eps, combine=None):
+    hkv, d = k_pool.shape[1], k_pool.shape[2]
+    k, v = op.kv_project_ref(x, gamma, w_k, w_v, eps, combine)
+    k2, v2 = np.array(k_pool, dtype=np.float64), np.array(v_pool, dtype=np.float64)
+    lens = np.array(seq_len, dtype=np.int64)
+    flag = 0
+    for b in range(len(lens)):
+        for r in range(int(cu[b]), int(cu[b + 1])):
+            if lens[b] >= int(seq_cap[b]):
+                flag = 1
+                break
+            k2[int(seq_start[b]) + lens[b]] = k[r].reshape(hkv, d)
+            v2[int(seq_start[b]) + lens[b]] = v[r].reshape(hkv, d)
+            lens[b] += 1
+    return k2, v2, lens, flag
+
+
 def _softmax_no_exp(s):
     m = np.max(s, axis=-1, keepdims=True)
     w = np.where(np.isfinite(s), s - m + 10.0, 0.0)
@@ -109,6 +172,15 @@ MUTATIONS = {
     "window_in_fixed_blocks": ("window_start", lambda p, w: (p // w) * w if w > 0 else 0),
     "ring_slot_shifted": ("ring_append_ref", _ring_slot_shift),
     "ring_does_not_wrap": ("ring_append_ref", _ring_no_wrap),
+    "rmsnorm_sum_not_mean": ("op.rmsnorm_ref", _rms_sum_not_mean),
+    "rmsnorm_eps_outside_sqrt": ("op.rmsnorm_ref", _rms_eps_outside),
+    "rmsnorm_no_gain": ("op.rmsnorm_ref", _rms_no_gain),
+    "rmsnorm_gain_before_norm": ("op.rmsnorm_ref", _rms_gain_first),
+    "projection_k_v_swapped": ("op.kv_project_ref", _project_swapped),
+    "combine_weights_swapped": ("op.kv_combine_ref", lambda km, kb, a1, a2, lam: lam * (a2 * kb + a1 * km)),
+    "combine_without_lambda": ("op.kv_combine_ref", lambda km, kb, a1, a2, lam: a1 * kb + a2 * km),
+    "project_append_at_sequence_start": ("op.project_append_ref", _append_chunk_at_start),
+    "project_append_partial_chunk": ("op.project_append_ref", _append_partial_chunk),
 }
 
 
@@ -120,7 +192,10 @@ def test_unmutated_oracle_passes_all_pins():
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_mutation_is_caught(name, monkeypatch):
     attr, repl = MUTATIONS[name]
-    monkeypatch.setattr(ox, attr, repl)
+    module = ox
+    if attr.startswith("op."):
+        module, attr = op, attr[3:]
+    monkeypatch.setattr(module, attr, repl)
     caught = []
     for check in pinlib.ALL_PINS:
         try:
