@@ -14,6 +14,8 @@ from .xattn import (  # noqa: F401
     decode_splits,
     kv_append,
     kv_append_ring,
+    kv_project_append,
+    kv_project_pack,
     load_library,
     make_dims,
     workspace_size,

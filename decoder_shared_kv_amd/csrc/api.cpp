@@ -268,6 +268,69 @@ yoco_status yoco_xattn_decode_window(const yoco_dims* dims, const yoco_kv_cache*
   return decode_impl(dims, cache, q, max_kv_len, total_kv_len, window, out, lse, workspace, workspace_bytes, stream);
 }
 
+yoco_status yoco_kv_project_pack(const yoco_dims* dims, int32_t d_model, const void* gain, const void* w_k,
+                                 const void* w_v, void* w_packed, void* stream) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  if (dims->dtype != YOCO_DTYPE_BF16) return YOCO_ERR_UNSUPPORTED;
+  if (d_model < 64 || d_model % 64 != 0) return YOCO_ERR_UNSUPPORTED;
+  if (gain == nullptr || w_k == nullptr || w_v == nullptr || w_packed == nullptr) return YOCO_ERR_INVALID_ARG;
+  if (!aligned16(w_packed)) return YOCO_ERR_INVALID_ARG;
+  const int hd = dims->num_kv_heads * dims->head_dim;
+  if (yoco::launch_kv_pack(gain, w_k, w_v, w_packed, d_model, hd, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return YOCO_ERR_HIP;
+  return YOCO_OK;
+}
+
+yoco_status yoco_kv_project_append(const yoco_dims* dims, const yoco_kv_cache* cache, const void* x,
+                                   const int32_t* cu_seqlens, int64_t total_rows, int32_t d_model,
+                                   const void* w_packed, float eps, const yoco_kv_residual* residual,
+                                   int32_t* overflow_flag, void* stream) {
+  yoco_status st = check_dims(dims);
+  if (st != YOCO_OK) return st;
+  st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (dims->dtype != YOCO_DTYPE_BF16) return YOCO_ERR_UNSUPPORTED;
+  if (d_model < 64 || d_model % 64 != 0 || d_model > (1 << 20)) return YOCO_ERR_UNSUPPORTED;
+  if (x == nullptr || cu_seqlens == nullptr || w_packed == nullptr) return YOCO_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_packed) || !aligned4(cu_seqlens)) return YOCO_ERR_INVALID_ARG;
+  if (overflow_flag != nullptr && !aligned4(overflow_flag)) return YOCO_ERR_INVALID_ARG;
+  if (total_rows < 0 || !std::isfinite(eps) || eps < 0.f) return YOCO_ERR_INVALID_ARG;
+  if (residual != nullptr) {
+    if (residual->k1 == nullptr || residual->v1 == nullptr) return YOCO_ERR_INVALID_ARG;
+    if (!std::isfinite(residual->lambda) || !std::isfinite(residual->a_k[0]) || !std::isfinite(residual->a_k[1]) ||
+        !std::isfinite(residual->a_v[0]) || !std::isfinite(residual->a_v[1]))
+      return YOCO_ERR_INVALID_ARG;
+  }
+  yoco::ProjectParams p{};
+  p.x = x;
+  p.w = w_packed;
+  p.k = cache->k;
+  p.v = cache->v;
+  p.seq_start = cache->seq_start;
+  p.seq_len = cache->seq_len;
+  p.seq_cap = cache->seq_cap;
+  p.cu_seqlens = cu_seqlens;
+  p.overflow = overflow_flag;
+  p.pool_rows = cache->pool_rows;
+  p.total_rows = total_rows;
+  p.batch = dims->batch;
+  p.k_dim = d_model;
+  p.n_cols = 2 * dims->num_kv_heads * dims->head_dim;
+  p.eps = eps;
+  if (residual != nullptr) {
+    p.k1 = residual->k1;
+    p.v1 = residual->v1;
+    p.lam = residual->lambda;
+    p.ak1 = residual->a_k[0];
+    p.ak2 = residual->a_k[1];
+    p.av1 = residual->a_v[0];
+    p.av2 = residual->a_v[1];
+  }
+  if (yoco::launch_kv_project(p, static_cast<hipStream_t>(stream)) != hipSuccess) return YOCO_ERR_HIP;
+  return YOCO_OK;
+}
+
 const char* yoco_status_string(yoco_status status) {
   switch (status) {
     case YOCO_OK: return "ok";

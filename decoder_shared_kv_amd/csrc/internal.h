@@ -49,6 +49,28 @@ struct AppendParams {
   int32_t ring;               // 1: ring window cache, the row goes to slot seq_len mod seq_cap
 };
 
+// The shared cache's producer: RMSNorm + [W_K | W_V] projection + append.
+struct ProjectParams {
+  const void* x;              // [total_rows, k_dim] bf16, the Self-Decoder output rows
+  const void* w;              // [n_cols, k_dim] bf16, gain-folded packed weights
+  void* k;                    // cache pools [pool_rows, n_cols / 2] bf16
+  void* v;
+  const void* k1;             // YOCO++ bottom-layer rows [total_rows, n_cols / 2] or null
+  const void* v1;
+  const int64_t* seq_start;
+  int32_t* seq_len;
+  const int32_t* seq_cap;
+  const int32_t* cu_seqlens;  // [batch + 1]
+  int32_t* overflow;
+  int64_t pool_rows;
+  int64_t total_rows;
+  int32_t batch;
+  int32_t k_dim;              // d_model, a multiple of 64
+  int32_t n_cols;             // 2 * Hkv * head_dim, a multiple of 128
+  float eps;
+  float lam, ak1, ak2, av1, av2;
+};
+
 // Host launchers (one per kernel family); each returns the hipGetLastError code.
 hipError_t launch_kv_append(const AppendParams& p, int batch, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
@@ -56,6 +78,9 @@ hipError_t launch_prefill_f32(const AttnParams& p, int head_dim, int grid, hipSt
 hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_split_f32(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_kv_project(const ProjectParams& p, hipStream_t stream);
+hipError_t launch_kv_pack(const void* gain, const void* wk, const void* wv, void* out, int k_dim, int hd,
+                          hipStream_t stream);
 
 // Prefill tiling shared between the planner and the kernels.
 #ifndef YOCO_PREFILL_WAVES

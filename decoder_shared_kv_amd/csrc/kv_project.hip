@@ -1,0 +1,253 @@
+// The shared cache's producer: K^ = RMSNorm(X) W_K, V^ = RMSNorm(X) W_V for the
+// rows of the last Self-Decoder output, written straight into each sequence's
+// rows of the shared cache (page "YOCO", section "架构总览", the K^, V^
+// equations; LN is RMSNorm: xingfushuangcheng.com explainer of YOCO, section
+// "自解码器"). Optionally the YOCO++ residual with the bottom layer's rows,
+// K' = lambda (a1 K_1 + a2 K^), is formed in the same epilogue, so the cache holds
+// the combined rows and decode reads no more than YOCO (gist.science explainer
+// of YOCO++, sections 2.1 and 2.2).
+//
+// One GEMM on v_mfma_f32_32x32x16_bf16: C[t][n] = X[t][:] . W'[n][:], with
+// W' = (gamma * [W_K | W_V])^T packed once (kv_pack_kernel): the gain is
+// folded into the weights, and since RMSNorm's 1/rms is a per-row scalar the
+// GEMM runs on the raw rows and the epilogue multiplies by it. The row sums of
+// squares come from the A operands already in registers (v_dot2_f32_bf16).
+//
+// Workgroup: 8 waves, a 256 (rows) x 128 (columns) tile, each wave 64 x 64
+// (2 x 2 MFMA blocks). X and W' tiles of 64 k stream HBM -> LDS by the load
+// unit through 3 stages, 16-byte chunks XOR-swizzled by the row (conflict-free
+// A/B reads). A sequence whose rows do not all fit its capacity is skipped
+// (kv_commit_kernel raises the flag; it also advances seq_len afterwards).
+#include <hip/hip_bf16.h>
+
+#include "internal.h"
+#include "lds_copy.h"
+
+namespace yoco {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPM = 256;           // rows per workgroup tile
+constexpr int kPN = 128;           // columns per workgroup tile
+constexpr int kPK = 64;            // k per stage
+constexpr int kPStages = 3;
+constexpr int kPThreads = 512;
+constexpr int kXBytes = kPM * kPK * 2;     // 32 KB
+constexpr int kWBytes = kPN * kPK * 2;     // 16 KB
+constexpr int kPStage = kXBytes + kWBytes;
+constexpr int kXLoads = kPM * kPK / 8 / kPThreads;   // 16-byte chunks per thread and stage
+constexpr int kWLoads = kPN * kPK / 8 / kPThreads;
+static_assert(kXLoads == 4 && kWLoads == 2, "tile split");
+
+// byte offset of 16-byte chunk c of tile row r (64 k = 8 chunks per row)
+__device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 128 + 16 * (c ^ (r & 7))); }
+
+__global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPStages * kPStage];
+  __shared__ int64_t prow[kPM];     // pool row of each tile row, -1: not written
+  __shared__ float inv_rms[kPM];
+  YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;          // 0..3: rows wm*64 ..
+  const int wn = wave & 1;           // 0..1: columns wn*64 ..
+  const int n_tiles = p.n_cols / kPN;
+  const int nt = blockIdx.x % n_tiles;
+  const int mt = blockIdx.x / n_tiles;
+  const int64_t m0 = (int64_t)mt * kPM;
+  const int n0 = nt * kPN;
+
+  // where each tile row goes: sequence b by binary search over cu_seqlens
+  if (tid < kPM) {
+    const int64_t t = m0 + tid;
+    int64_t dst = -1;
+    if (t < p.total_rows) {
+      int lo = 0, hi = p.batch;       // find b with cu[b] <= t < cu[b + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu_seqlens[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int b = lo;
+      const int64_t c0 = p.cu_seqlens[b], c1 = p.cu_seqlens[b + 1];
+      const int64_t len = p.seq_len[b], cap = p.seq_cap[b], start = p.seq_start[b];
+      const bool fits = t >= c0 && t < c1 && c1 <= p.total_rows && len >= 0 && start >= 0 &&
+                        len + (c1 - c0) <= cap && start + len + (c1 - c0) <= p.pool_rows;
+      if (fits) dst = start + len + (t - c0);
+    }
+    prow[tid] = dst;
+  }
+
+  // this thread's chunks: X chunk q = i * threads + tid -> row q / 8, chunk q % 8
+  uint32_t xoff[kXLoads], xdst[kXLoads], woff[kWLoads], wdst[kWLoads];
+  const uint32_t wave_lds = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64 * 16;
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int q = i * kPThreads + tid;
+    int64_t row = m0 + q / 8;
+    if (row >= p.total_rows) row = p.total_rows - 1;     // rows past the end repeat the last one
+    const int c = (q % 8) ^ ((q / 8) & 7);               // the chunk that belongs at this LDS slot
+    xoff[i] = (uint32_t)((row - m0) * p.k_dim * 2 + c * 16);
+    xdst[i] = i * kPThreads * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kWLoads; ++i) {
+    const int q = i * kPThreads + tid;
+    const int c = (q % 8) ^ ((q / 8) & 7);
+    woff[i] = (uint32_t)((q / 8) * p.k_dim * 2 + c * 16);
+    wdst[i] = kXBytes + i * kPThreads * 16;
+  }
+  const char* xbase = static_cast<const char*>(p.x) + m0 * p.k_dim * 2;
+  const char* wbase = static_cast<const char*>(p.w) + (int64_t)n0 * p.k_dim * 2;
+  const int k_steps = p.k_dim / kPK;
+
+  auto issue = [&](int ks) {
+    const uint32_t st = wave_lds + (ks % kPStages) * kPStage;
+    const char* xb = xbase + (int64_t)ks * kPK * 2;
+    const char* wb = wbase + (int64_t)ks * kPK * 2;
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) dma16(xb, xoff[i], st + xdst[i]);
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i) dma16(wb, woff[i], st + wdst[i]);
+  };
+  constexpr int L = kXLoads + kWLoads;
+
+#pragma unroll
+  for (int s = 0; s < kPStages - 1; ++s)
+    if (s < k_steps) issue(s);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  float ss[2] = {0.f, 0.f};
+  const int qr = lane & 31, hf = lane >> 5;
+
+  for (int ks = 0; ks < k_steps; ++ks) {
+    if (ks + 1 < k_steps) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();
+    barrier_only();   // stage ks is in for every thread; stage (ks - 1) % S is free
+    if (ks + kPStages - 1 < k_steps) issue(ks + kPStages - 1);
+    const YOCO_LDS char* xs = smem + (ks % kPStages) * kPStage;
+    const YOCO_LDS char* ws = xs + kXBytes;
+#pragma unroll
+    for (int kk = 0; kk < kPK / 16; ++kk) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + 32 * i + qr;
+        a[i] = *reinterpret_cast<const YOCO_LDS bf16x8*>(xs + swz(r, 2 * kk + hf));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + 32 * j + qr;
+        b[j] = *reinterpret_cast<const YOCO_LDS bf16x8*>(ws + swz(r, 2 * kk + hf));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if (wn == 0) {
+        // sum of squares of this lane's 8 values of row r (k half hf)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 v2 = {a[i][2 * e], a[i][2 * e + 1]};
+            ss[i] = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss[i], false);
+          }
+        }
+      }
+    }
+  }
+  if (wn == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float tot = ss[i] + __shfl_xor(ss[i], 32);
+      if (hf == 0) inv_rms[wm * 64 + 32 * i + qr] = 1.0f / sqrtf(tot / (float)p.k_dim + p.eps);
+    }
+  }
+  __syncthreads();
+
+  // epilogue: lane holds column n0 + wn*64 + 32j + qr, rows 8(r/4) + 4hf + r%4 of block i
+  const int hd = p.n_cols / 2;                 // K^ columns, then V^ columns
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + 32 * j + qr;
+    const bool is_v = n >= hd;
+    const int nc = is_v ? n - hd : n;
+    __bf16* dst = static_cast<__bf16*>(is_v ? p.v : p.k);
+    const __bf16* bottom = static_cast<const __bf16*>(is_v ? p.v1 : p.k1);
+    const float a1 = is_v ? p.av1 : p.ak1, a2 = is_v ? p.av2 : p.ak2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int64_t pr = prow[lr];
+        if (pr < 0) continue;
+        float val = acc[i][j][r] * inv_rms[lr];
+        if (bottom != nullptr) val = p.lam * (a1 * (float)bottom[(m0 + lr) * hd + nc] + a2 * val);
+        dst[pr * hd + nc] = (__bf16)val;
+      }
+    }
+  }
+}
+
+// seq_len[b] += rows of sequence b if they fit (the projection wrote them),
+// else the flag.
+__global__ void kv_commit_kernel(ProjectParams p) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= p.batch) return;
+  const int64_t c0 = p.cu_seqlens[b], c1 = p.cu_seqlens[b + 1];
+  const int64_t len = p.seq_len[b], cap = p.seq_cap[b], start = p.seq_start[b];
+  const bool fits = c1 >= c0 && c1 <= p.total_rows && len >= 0 && start >= 0 && len + (c1 - c0) <= cap &&
+                    start + len + (c1 - c0) <= p.pool_rows;
+  if (fits) p.seq_len[b] = (int32_t)(len + (c1 - c0));
+  else if (p.overflow != nullptr) p.overflow[0] = 1;
+}
+
+// W'[n][k] = gain[k] * (n < hd ? W_K[k][n] : W_V[k][n - hd]), through a 32 x 32 LDS tile.
+__global__ __launch_bounds__(256) void kv_pack_kernel(const __bf16* gain, const __bf16* wk, const __bf16* wv,
+                                                      __bf16* out, int k_dim, int hd) {
+  __shared__ float tile[32][33];
+  const int n_cols = 2 * hd;
+  const int tk = blockIdx.y * 32, tn = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    const int k = tk + r, n = tn + tx;
+    float v = 0.f;
+    if (k < k_dim && n < n_cols)
+      v = (float)gain[k] * (float)(n < hd ? wk[(int64_t)k * hd + n] : wv[(int64_t)k * hd + n - hd]);
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int n = tn + r, k = tk + tx;
+    if (n < n_cols && k < k_dim) out[(int64_t)n * k_dim + k] = (__bf16)tile[tx][r];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_project(const ProjectParams& p, hipStream_t stream) {
+  const int64_t m_tiles = (p.total_rows + kPM - 1) / kPM;
+  const int64_t grid = m_tiles * (p.n_cols / kPN);
+  if (grid > 0) hipLaunchKernelGGL(kv_project_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
+  hipLaunchKernelGGL(kv_commit_kernel, dim3((p.batch + 255) / 256), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_pack(const void* gain, const void* wk, const void* wv, void* out, int k_dim, int hd,
+                          hipStream_t stream) {
+  dim3 grid((2 * hd + 31) / 32, (k_dim + 31) / 32);
+  hipLaunchKernelGGL(kv_pack_kernel, grid, dim3(256), 0, stream, static_cast<const __bf16*>(gain),
+                     static_cast<const __bf16*>(wk), static_cast<const __bf16*>(wv), static_cast<__bf16*>(out), k_dim,
+                     hd);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

@@ -33,8 +33,7 @@
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
-
-#define YOCO_LDS __attribute__((address_space(3)))
+#include "lds_copy.h"
 
 namespace yoco {
 
@@ -64,14 +63,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
-// s_waitcnt with vmcnt = n and lgkmcnt = 0 (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
 // Wait until at most `ahead` (< kStages - 1) tiles of L loads each are still in flight.
 template <int L>
 __device__ __forceinline__ void wait_tiles(int ahead) {
@@ -79,15 +70,6 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
   else if (kStages >= 4 && ahead >= 2) wait_vm_lgkm0<(kStages >= 4 ? 2 * L : 0)>();
   else if (kStages >= 3 && ahead >= 1) wait_vm_lgkm0<L>();
   else wait_vm_lgkm0<0>();
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would also
-// wait for the tiles still in flight); the empty asm keeps the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 template <int D>
@@ -139,27 +121,6 @@ __device__ __forceinline__ void make_issue(Issue<D>& is, int64_t row_stride) {
     is.voff[i] = (uint32_t)((r * row_stride + is.vcol[i]) * 2);
   }
 }
-
-// 16-byte-per-lane HBM -> LDS copies by the load unit: lane l's 16 bytes land
-// at dst + 16 l (dst is wave-uniform). Written as asm so that the compiler does
-// not count them among its own LDS events (which would make it wait for every
-// LDS read to finish before the next MFMA); their completion is awaited
-// explicitly with s_waitcnt vmcnt before the workgroup barrier of their tile.
-// The s_nop covers the wait states a load-to-LDS needs after an M0 write (and
-// after a VALU write of an SGPR operand), which the compiler does not insert
-// inside asm.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; nothing else in this kernel uses it
-// per-lane 64-bit source address
-__device__ __forceinline__ void dma16(const __bf16* src, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
-}
-// wave-uniform 64-bit base + per-lane 32-bit byte offset: no per-lane address arithmetic
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(base)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Request one K^/V^ tile into a stage. Rows past `last` repeat row `last`.
 template <int D>

@@ -6,7 +6,8 @@ There is no fallback: if the library is missing, loading raises.
 
 The functions mirror the C ABI (include/yoco_xattn.h) one to one:
 ``kv_append``, ``kv_append_ring``, ``xattn_prefill``, ``xattn_prefill_window``,
-``xattn_decode``, ``xattn_decode_window``, ``workspace_size``, ``decode_splits``.
+``xattn_decode``, ``xattn_decode_window``, ``workspace_size``, ``decode_splits``,
+``kv_project_pack``, ``kv_project_append``.
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTS = ("yoco_kv_append", "yoco_kv_append_ring", "yoco_xattn_prefill", "yoco_xattn_prefill_window",
            "yoco_xattn_decode", "yoco_xattn_decode_window", "yoco_xattn_workspace_size",
-           "yoco_xattn_decode_splits", "yoco_status_string")
+           "yoco_xattn_decode_splits", "yoco_kv_project_pack", "yoco_kv_project_append", "yoco_status_string")
 
 
 class YocoError(RuntimeError):
@@ -43,6 +44,11 @@ class Dims(ctypes.Structure):
 class KvCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pool_rows", ctypes.c_int64),
                 ("seq_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("seq_cap", ctypes.c_void_p)]
+
+
+class Residual(ctypes.Structure):
+    _fields_ = [("k1", ctypes.c_void_p), ("v1", ctypes.c_void_p), ("lam", ctypes.c_float),
+                ("a_k", ctypes.c_float * 2), ("a_v", ctypes.c_float * 2)]
 
 
 _lib = None
@@ -66,6 +72,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_xattn_prefill_window.argtypes = [dims_p, cache_p, P, P, i32, i64, i32, P, P, P]
     lib.yoco_xattn_decode.argtypes = [dims_p, cache_p, P, i32, i64, P, P, P, ctypes.c_size_t, P]
     lib.yoco_xattn_decode_window.argtypes = [dims_p, cache_p, P, i32, i64, i32, P, P, P, ctypes.c_size_t, P]
+    lib.yoco_kv_project_pack.argtypes = [dims_p, i32, P, P, P, P, P]
+    lib.yoco_kv_project_append.argtypes = [dims_p, cache_p, P, P, i64, i32, P, ctypes.c_float,
+                                           ctypes.POINTER(Residual), P, P]
     lib.yoco_xattn_workspace_size.argtypes = [dims_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.yoco_xattn_decode_splits.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                              ctypes.POINTER(ctypes.c_int32)]
@@ -232,3 +241,35 @@ def xattn_decode_window(cache: SharedKV, q: torch.Tensor, max_kv_len: int, windo
                                         int(workspace.numel() * workspace.element_size()), _stream(stream)),
            "yoco_xattn_decode_window")
     return out
+
+
+def kv_project_pack(gain: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, kv_heads: int, head_dim: int,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Packed projection weights (gain folded, [W_K | W_V] transposed): [2 * Hkv * d, d_model] bf16."""
+    lib = load_library()
+    d_model = int(w_k.shape[0])
+    if out is None:
+        out = torch.empty(2 * kv_heads * head_dim, d_model, dtype=torch.bfloat16, device=w_k.device)
+    dims = make_dims(1, kv_heads, kv_heads, head_dim, w_k.dtype, 1.0)
+    _check(lib.yoco_kv_project_pack(ctypes.byref(dims), d_model, _ptr(gain), _ptr(w_k), _ptr(w_v), _ptr(out),
+                                    _stream(stream)), "yoco_kv_project_pack")
+    return out
+
+
+def kv_project_append(cache: SharedKV, x: torch.Tensor, cu_seqlens: torch.Tensor, w_packed: torch.Tensor, eps: float,
+                      residual: Optional[dict] = None, overflow: Optional[torch.Tensor] = None, stream=None) -> None:
+    """RMSNorm(x) [W_K | W_V] appended to each sequence's rows (x [T, d_model], packed by cu_seqlens).
+
+    residual (optional): {"k1", "v1" (device [T, Hkv*d]), "lam", "a_k": (a1, a2), "a_v": (a1, a2)}."""
+    lib = load_library()
+    batch = int(cu_seqlens.shape[0]) - 1
+    dims = _dims_for(cache, cache.k.shape[1], 1.0, batch)
+    desc = cache.descriptor()
+    res = None
+    if residual is not None:
+        res = Residual(_ptr(residual["k1"]), _ptr(residual["v1"]), float(residual["lam"]),
+                       (ctypes.c_float * 2)(*residual["a_k"]), (ctypes.c_float * 2)(*residual["a_v"]))
+    _check(lib.yoco_kv_project_append(ctypes.byref(dims), ctypes.byref(desc), _ptr(x), _ptr(cu_seqlens),
+                                      int(x.shape[0]), int(x.shape[1]), _ptr(w_packed), float(eps),
+                                      ctypes.byref(res) if res is not None else None, _ptr(overflow),
+                                      _stream(stream)), "yoco_kv_project_append")

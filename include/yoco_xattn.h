@@ -191,6 +191,66 @@ yoco_status yoco_kv_append_ring(const yoco_dims* dims, const yoco_kv_cache* cach
                                 const void* k_new, const void* v_new,
                                 int32_t* flag, void* stream);
 
+/*
+ * The shared cache's producer (bf16 only)
+ * ---------------------------------------
+ * The Self-Decoder output X^{L/2} is normalised and projected once into the
+ * global pair K^ = LN(X) W_K, V^ = LN(X) W_V (page "YOCO", section "架构总览",
+ * the K^, V^ equations), LN being RMSNorm (xingfushuangcheng.com explainer of
+ * YOCO, section "自解码器"): y = x / sqrt(mean(x^2) + eps) * gain. The rows go
+ * straight into each sequence's rows of the shared cache.
+ */
+
+/*
+ * yoco_kv_project_pack -- prepack the projection once per model:
+ * w_packed[n][k] = gain[k] * W[k][n] rounded to bf16, for n < Hkv*head_dim from
+ * W_K and after that from W_V (the gain folds into the weights because 1/rms is
+ * a per-row factor).
+ *   gain      [device] bf16 [d_model]
+ *   w_k, w_v  [device] bf16 [d_model, Hkv * head_dim] (row-major: x @ W)
+ *   w_packed  [device] bf16 [2 * Hkv * head_dim, d_model] (caller-owned,
+ *             2 * Hkv * head_dim * d_model * 2 bytes), 16-byte aligned
+ * d_model must be a positive multiple of 64 (YOCO_ERR_UNSUPPORTED otherwise).
+ */
+yoco_status yoco_kv_project_pack(const yoco_dims* dims, int32_t d_model, const void* gain,
+                                 const void* w_k, const void* w_v, void* w_packed, void* stream);
+
+/* [host] YOCO++ residual with the bottom layer's rows (gist.science explainer of
+ * YOCO++ (2604.13556), sections 2.1 and 2.2): K' = lambda (a_k[0] K_1 + a_k[1] K^),
+ * V' = lambda (a_v[0] V_1 + a_v[1] V^); the pages fix lambda = 35 and start
+ * from a[0] = 0, a[1] = 1/lambda (which gives YOCO's rows). The combined rows are
+ * what the cache holds, so decode reads no more than YOCO. */
+typedef struct {
+  const void* k1;            /* [device] bf16 [total_rows, Hkv * head_dim], bottom-layer K rows */
+  const void* v1;            /* [device] bf16 [total_rows, Hkv * head_dim] */
+  float lambda;
+  float a_k[2];
+  float a_v[2];
+} yoco_kv_residual;
+
+/*
+ * yoco_kv_project_append -- K^, V^ of the packed rows x and their append to the
+ * shared cache in one GEMM (MFMA) with the RMSNorm and the optional YOCO++
+ * combine in its epilogue. Sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+ * of x; its i-th row lands at pool row seq_start[b] + seq_len[b] + i, and then
+ * seq_len[b] grows by its row count (one row per sequence is the per-token
+ * append after the Self-Decoder; a whole prompt, the prefill). A sequence whose
+ * rows do not all fit seq_cap[b] (or the pool) is left untouched and sets
+ * *overflow_flag to 1 (never cleared; NULL disables it).
+ *   x          [device] bf16 [total_rows, d_model]
+ *   cu_seqlens [device] int32 [B+1], non-decreasing
+ *   w_packed   [device] from yoco_kv_project_pack with the same dims and d_model
+ *   eps        RMSNorm epsilon, finite and >= 0
+ *   residual   [host] YOCO++ combine or NULL
+ * The normalised rows are not rounded before the product; scores of the GEMM
+ * accumulate in fp32 and each cache element is rounded once to bf16.
+ */
+yoco_status yoco_kv_project_append(const yoco_dims* dims, const yoco_kv_cache* cache,
+                                   const void* x, const int32_t* cu_seqlens, int64_t total_rows,
+                                   int32_t d_model, const void* w_packed, float eps,
+                                   const yoco_kv_residual* residual, int32_t* overflow_flag,
+                                   void* stream);
+
 /* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len (any
  * total_kv_len, any smaller max_kv_len). */
 yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes);

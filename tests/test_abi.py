@@ -149,6 +149,28 @@ def test_window_argument_checks(lib):
     assert A(FAKE, FAKE, FAKE + 1, None) == 1
 
 
+def test_producer_argument_checks(lib):
+    dims, cache = _dims(batch=2), _cache()
+    res = X.Residual(None, FAKE, 35.0, (ctypes.c_float * 2)(0.0, 1 / 35), (ctypes.c_float * 2)(0.0, 1 / 35))
+    PA = lambda d, *a: lib.yoco_kv_project_append(ctypes.byref(d), ctypes.byref(cache), *a)  # noqa: E731
+    assert PA(_dims(dtype=0), FAKE, FAKE, 10, 256, FAKE, 1e-6, None, None, None) == 2   # fp32: not built
+    assert PA(dims, FAKE, FAKE, 10, 100, FAKE, 1e-6, None, None, None) == 2             # d_model % 64
+    assert PA(dims, FAKE, FAKE, 10, 0, FAKE, 1e-6, None, None, None) == 2
+    assert PA(dims, None, FAKE, 10, 256, FAKE, 1e-6, None, None, None) == 1
+    assert PA(dims, FAKE, None, 10, 256, FAKE, 1e-6, None, None, None) == 1
+    assert PA(dims, FAKE, FAKE, 10, 256, None, 1e-6, None, None, None) == 1
+    assert PA(dims, FAKE + 8, FAKE, 10, 256, FAKE, 1e-6, None, None, None) == 1
+    assert PA(dims, FAKE, FAKE, -1, 256, FAKE, 1e-6, None, None, None) == 1
+    assert PA(dims, FAKE, FAKE, 10, 256, FAKE, -1.0, None, None, None) == 1
+    assert PA(dims, FAKE, FAKE, 10, 256, FAKE, float("nan"), None, None, None) == 1
+    assert PA(dims, FAKE, FAKE, 10, 256, FAKE, 1e-6, ctypes.byref(res), None, None) == 1   # k1 missing
+    PK = lambda d, *a: lib.yoco_kv_project_pack(ctypes.byref(d), *a)  # noqa: E731
+    assert PK(_dims(dtype=0), 256, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert PK(dims, 96, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert PK(dims, 256, None, FAKE, FAKE, FAKE, None) == 1
+    assert PK(dims, 256, FAKE, FAKE, FAKE, FAKE + 2, None) == 1
+
+
 def test_split_plan():
     # decode: 8 x 131072 rows, Hkv=2 -> 16 (sequence, KV head) units, ~1024 workgroups in total
     s, r = dk.decode_splits(8, 16, 2, 128, X.torch.bfloat16, 131072)
