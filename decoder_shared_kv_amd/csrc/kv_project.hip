@@ -197,6 +197,89 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
   }
 }
 
+// Few rows (decode: one per sequence): the tile above would leave most CUs idle
+// and stream the weights through one pipeline per 128 columns. Here a workgroup
+// owns 16 columns and all (<= 16) rows; its 8 waves split d_model, read their
+// A (rows) and B (weights) operands straight from memory (16 bytes per lane;
+// the 12.6 MB of weights of the 3B geometry stay cached between calls), run
+// v_mfma_f32_16x16x32_bf16 and add their partial tiles in LDS.
+constexpr int kSmallRows = 16;
+constexpr int kSmallWaves = 8;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(64 * kSmallWaves) void kv_project_small_kernel(ProjectParams p) {
+  __shared__ float part[kSmallWaves][kSmallRows][17];
+  __shared__ float ssq[kSmallWaves][kSmallRows];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int col = lane & 15, grp = lane >> 4;          // MFMA 16x16x32: k = 8 grp .. 8 grp + 7
+  int64_t row = col < p.total_rows ? col : p.total_rows - 1;   // rows past the end repeat the last one
+  const __bf16* xr = static_cast<const __bf16*>(p.x) + row * p.k_dim;
+  const __bf16* wr = static_cast<const __bf16*>(p.w) + (int64_t)(n0 + col) * p.k_dim;
+  const int per_wave = p.k_dim / kSmallWaves;          // a multiple of 8; steps of 32 k plus a tail of 8-k groups
+  const int k_lo = wave * per_wave, k_hi = k_lo + per_wave;
+  f32x4 acc = f32x4{};
+  float ss = 0.f;
+  for (int k = k_lo; k < k_hi; k += 32) {
+    const int kk = k + 8 * grp;
+    bf16x8 a = bf16x8{}, b = bf16x8{};
+    if (kk < k_hi) {
+      a = *reinterpret_cast<const bf16x8*>(xr + kk);
+      b = *reinterpret_cast<const bf16x8*>(wr + kk);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 v2 = {a[2 * e], a[2 * e + 1]};
+      ss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss, false);
+    }
+  }
+  // lane holds column col, rows 4 grp .. 4 grp + 3 (D layout of the 16x16 MFMA);
+  // the sum of squares of row `col` over this wave's k is spread over the 4 groups
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[wave][4 * grp + r][col] = acc[r];
+  if (grp == 0) ssq[wave][col] = ss;
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0: sum the waves' partial tiles and write 16 columns x 16 rows
+  const int hd = p.n_cols / 2;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = 4 * grp + r;
+    float v = 0.f, sq = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+      v += part[w][rr][col];
+      sq += ssq[w][rr];
+    }
+    const int64_t t = rr;
+    if (t >= p.total_rows) continue;
+    int lo = 0, hi = p.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.cu_seqlens[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int64_t c0 = p.cu_seqlens[lo], c1 = p.cu_seqlens[lo + 1];
+    const int64_t len = p.seq_len[lo], cap = p.seq_cap[lo], start = p.seq_start[lo];
+    const bool fits = t >= c0 && t < c1 && c1 <= p.total_rows && len >= 0 && start >= 0 &&
+                      len + (c1 - c0) <= cap && start + len + (c1 - c0) <= p.pool_rows;
+    if (!fits) continue;
+    const int64_t pr = start + len + (t - c0);
+    const int n = n0 + col;
+    const bool is_v = n >= hd;
+    const int nc = is_v ? n - hd : n;
+    float val = v * (1.0f / sqrtf(sq / (float)p.k_dim + p.eps));
+    const __bf16* bottom = static_cast<const __bf16*>(is_v ? p.v1 : p.k1);
+    if (bottom != nullptr)
+      val = p.lam * ((is_v ? p.av1 : p.ak1) * (float)bottom[t * hd + nc] + (is_v ? p.av2 : p.ak2) * val);
+    static_cast<__bf16*>(is_v ? p.v : p.k)[pr * hd + nc] = (__bf16)val;
+  }
+}
+
 // seq_len[b] += rows of sequence b if they fit (the projection wrote them),
 // else the flag.
 __global__ void kv_commit_kernel(ProjectParams p) {
@@ -234,9 +317,13 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const __bf16* gain, const 
 }  // namespace
 
 hipError_t launch_kv_project(const ProjectParams& p, hipStream_t stream) {
-  const int64_t m_tiles = (p.total_rows + kPM - 1) / kPM;
-  const int64_t grid = m_tiles * (p.n_cols / kPN);
-  if (grid > 0) hipLaunchKernelGGL(kv_project_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
+  if (p.total_rows > 0 && p.total_rows <= kSmallRows) {
+    hipLaunchKernelGGL(kv_project_small_kernel, dim3(p.n_cols / 16), dim3(64 * kSmallWaves), 0, stream, p);
+  } else if (p.total_rows > 0) {
+    const int64_t m_tiles = (p.total_rows + kPM - 1) / kPM;
+    const int64_t grid = m_tiles * (p.n_cols / kPN);
+    hipLaunchKernelGGL(kv_project_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
+  }
   hipLaunchKernelGGL(kv_commit_kernel, dim3((p.batch + 255) / 256), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

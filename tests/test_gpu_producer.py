@@ -81,6 +81,9 @@ def _compare(cache, host, ref, what):
     ([5, 17, 0], [700, 40, 300], [600, 20, 257], 2, 128, 1024),
     ([0], [64], [64], 1, 64, 192),                       # K and V halves inside one 128-column tile
     ([3, 9, 100, 0, 1, 2, 7, 8], [200] * 8, [1] * 8, 8, 128, 3072),   # decode: one row per sequence
+    ([0], [50], [1], 2, 64, 320),                        # a single row
+    ([2, 0], [40, 40], [9, 7], 4, 128, 448),             # 16 rows: the few-rows kernel's limit
+    ([2, 0], [40, 40], [9, 8], 4, 128, 448),             # 17 rows: the tiled kernel
 ])
 def test_project_append(lens_before, caps, chunks, hkv, d, d_model):
     say(f"producer lens={lens_before} chunks={chunks} hkv={hkv} d={d} d_model={d_model}")
@@ -98,10 +101,12 @@ def test_sequence_that_does_not_fit():
     assert int(flag.item()) == 1 and flag_ref == 1
 
 
-@pytest.mark.parametrize("a_k,a_v", [((0.0, 1.0 / 35.0), (0.0, 1.0 / 35.0)), ((0.01, 0.02), (-0.03, 0.025))])
-def test_yoco_pp_residual(a_k, a_v):
-    say(f"producer with YOCO++ residual a_k={a_k} a_v={a_v}")
-    cache, host = _setup([0, 4], [600, 300], [513, 130], 8, 128, 768, seed=11)
+@pytest.mark.parametrize("a_k,a_v,chunks", [((0.0, 1.0 / 35.0), (0.0, 1.0 / 35.0), [513, 130]),
+                                             ((0.01, 0.02), (-0.03, 0.025), [513, 130]),
+                                             ((0.01, 0.02), (-0.03, 0.025), [1, 1])])
+def test_yoco_pp_residual(a_k, a_v, chunks):
+    say(f"producer with YOCO++ residual a_k={a_k} a_v={a_v} chunks={chunks}")
+    cache, host = _setup([0, 4], [600, 300], chunks, 8, 128, 768, seed=11)
     g = torch.Generator().manual_seed(12)
     T = int(host["cu"][-1])
     residual = {"k1": torch.randn(T, 8 * 128, generator=g).to(torch.bfloat16),
