@@ -20,3 +20,12 @@ from .producer import (  # noqa: F401
     project_append_ref,
     rmsnorm_ref,
 )
+from .gret import (  # noqa: F401
+    GRET_CHUNK,
+    gret_chunkwise_ref,
+    gret_decay_matrix,
+    gret_decode_ref,
+    gret_parallel_ref,
+    gret_prefill_ref,
+    gret_recurrent_ref,
+)

@@ -31,6 +31,7 @@ import os
 import numpy as np
 import torch
 
+import oracle.gret as og
 import oracle.producer as op
 import oracle.xattn as ox
 
@@ -527,5 +528,102 @@ def check_project_append():
     assert np.array_equal(k3, ka) and np.array_equal(v3, va) and list(ln3) == list(lna) and f3 == fa == 0
 
 
+# ---------------------------------------------------------------------------
+# gated retention (gRet)
+# ---------------------------------------------------------------------------
+
+def _brute_gret(q, k, v, g, s0=None):
+    """Pure-Python recurrence on lists: S <- g S + k^T v, o = q S."""
+    dk, dv = len(k[0]), len(v[0])
+    st = [[0.0] * dv for _ in range(dk)] if s0 is None else [list(map(float, row)) for row in s0]
+    out = []
+    for t in range(len(q)):
+        st = [[float(g[t]) * st[i][j] + float(k[t][i]) * float(v[t][j]) for j in range(dv)] for i in range(dk)]
+        out.append([math.fsum(float(q[t][i]) * st[i][j] for i in range(dk)) for j in range(dv)])
+    return np.array(out), np.array(st)
+
+
+def check_gret_forms():
+    """The three forms agree (the pages state they are equivalent): the parallel
+    form against pure-Python loops of the recurrence, the NumPy recurrence and
+    the chunkwise form at several chunk sizes, with and without an initial state."""
+    rng = _rng(23)
+    for n, dk, dv in [(1, 3, 2), (9, 4, 3), (40, 8, 5)]:
+        q, k, v = rng.standard_normal((n, dk)), rng.standard_normal((n, dk)), rng.standard_normal((n, dv))
+        g = rng.uniform(0.3, 1.0, n)
+        for s0 in (None, rng.standard_normal((dk, dv))):
+            o_p, s_p = og.gret_parallel_ref(q, k, v, g, s0)
+            o_b, s_b = _brute_gret(q, k, v, g, s0)
+            assert np.max(np.abs(o_p - o_b)) <= 1e-12 and np.max(np.abs(s_p - s_b)) <= 1e-12, ("brute", n)
+            o_r, s_r = og.gret_recurrent_ref(q, k, v, g, s0)
+            assert np.max(np.abs(o_p - o_r)) <= 1e-12 and np.max(np.abs(s_p - s_r)) <= 1e-12, ("recurrent", n)
+            for chunk in (1, 3, 4, 7, n, 256):
+                o_c, s_c = og.gret_chunkwise_ref(q, k, v, g, s0, chunk)
+                assert np.max(np.abs(o_p - o_c)) <= 1e-12 and np.max(np.abs(s_p - s_c)) <= 1e-12, ("chunk", n, chunk)
+
+
+def check_gret_closed_forms():
+    """gamma = 1 is causal linear attention, tril(q k^T) v; a zero gate at t0
+    forgets everything before t0; one token gives (q.k) v + gamma q S0; the decay
+    matrix and a two-token case worked by hand."""
+    rng = _rng(24)
+    n, dk, dv = 30, 6, 4
+    q, k, v = rng.standard_normal((n, dk)), rng.standard_normal((n, dk)), rng.standard_normal((n, dv))
+    o, s = og.gret_parallel_ref(q, k, v, np.ones(n))
+    assert np.max(np.abs(o - np.tril(q @ k.T) @ v)) <= 1e-12 and np.max(np.abs(s - k.T @ v)) <= 1e-12, "gamma = 1"
+    g = rng.uniform(0.5, 1.0, n)
+    g[12] = 0.0
+    o1, s1 = og.gret_parallel_ref(q, k, v, g)
+    k2, v2 = k.copy(), v.copy()
+    k2[:12] += 4.0
+    v2[:12] -= 3.0
+    o2, s2 = og.gret_parallel_ref(q, k2, v2, g)
+    assert np.array_equal(o1[12:], o2[12:]) and np.array_equal(s1, s2), "zero gate forgets"
+    assert np.max(np.abs(o1[12] - (q[12] @ k[12]) * v[12])) <= 1e-12
+    s0 = rng.standard_normal((dk, dv))
+    o3, s3 = og.gret_parallel_ref(q[:1], k[:1], v[:1], np.array([0.7]), s0)
+    assert np.max(np.abs(o3[0] - ((q[0] @ k[0]) * v[0] + 0.7 * q[0] @ s0))) <= 1e-12
+    assert np.max(np.abs(s3 - (0.7 * s0 + np.outer(k[0], v[0])))) <= 1e-12
+    d = og.gret_decay_matrix(np.array([0.9, 0.5, 0.25]))
+    assert np.max(np.abs(d - np.array([[1, 0, 0], [0.5, 1, 0], [0.125, 0.25, 1]]))) <= 1e-16
+    # hand-worked: q = [1, 2], k = [3, 4], v = [5, 6], gamma = [0.5, 0.25] (dk = dv = 1):
+    # S0 = 15, o0 = 15; S1 = 0.25 * 15 + 24 = 27.75, o1 = 55.5
+    oh, sh = og.gret_parallel_ref(np.array([[1.0], [2.0]]), np.array([[3.0], [4.0]]), np.array([[5.0], [6.0]]),
+                                  np.array([0.5, 0.25]))
+    assert np.max(np.abs(oh[:, 0] - [15.0, 55.5])) <= 1e-14 and abs(sh[0, 0] - 27.75) <= 1e-14
+
+
+def check_gret_packing():
+    """Packed sequences equal separate calls; a sequence split in two calls with
+    the state passed on equals one call; a decode step after a prefill equals the
+    last row of the longer prefill."""
+    rng = _rng(25)
+    lens, h, dk, dv = (17, 5, 33), 3, 4, 6
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    tq = int(cu[-1])
+    q, k = rng.standard_normal((tq, h, dk)), rng.standard_normal((tq, h, dk))
+    v, g = rng.standard_normal((tq, h, dv)), rng.uniform(0.4, 1.0, (tq, h))
+    s0 = rng.standard_normal((3, h, dk, dv))
+    out, st = og.gret_prefill_ref(q, k, v, g, cu, s0)
+    for b in range(3):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        o_b, s_b = og.gret_prefill_ref(q[r0:r1], k[r0:r1], v[r0:r1], g[r0:r1], [0, r1 - r0], s0[b:b + 1])
+        assert np.max(np.abs(o_b - out[r0:r1])) <= 1e-13 and np.max(np.abs(s_b[0] - st[b])) <= 1e-13
+    # split sequence 2 at row 20 of 33
+    r0 = int(cu[2])
+    oa, sa = og.gret_prefill_ref(q[r0:r0 + 20], k[r0:r0 + 20], v[r0:r0 + 20], g[r0:r0 + 20], [0, 20], s0[2:3])
+    ob, sb = og.gret_prefill_ref(q[r0 + 20:r0 + 33], k[r0 + 20:r0 + 33], v[r0 + 20:r0 + 33], g[r0 + 20:r0 + 33],
+                                 [0, 13], sa)
+    assert np.max(np.abs(np.concatenate([oa, ob]) - out[r0:r0 + 33])) <= 1e-12 and np.max(np.abs(sb[0] - st[2])) <= 1e-12
+    # decode the last row of every sequence from the state after the others
+    stp = np.stack([og.gret_prefill_ref(q[int(cu[b]):int(cu[b + 1]) - 1], k[int(cu[b]):int(cu[b + 1]) - 1],
+                                        v[int(cu[b]):int(cu[b + 1]) - 1], g[int(cu[b]):int(cu[b + 1]) - 1],
+                                        [0, lens[b] - 1], s0[b:b + 1])[1][0] for b in range(3)])
+    last = cu[1:] - 1
+    od, sd = og.gret_decode_ref(q[last], k[last], v[last], g[last], stp)
+    assert np.max(np.abs(od - out[last])) <= 1e-12 and np.max(np.abs(sd - st)) <= 1e-12
+
+
 ALL_PINS = [check_bruteforce, check_sdpa, check_closed_forms, check_invariants, check_chunked_prefill, check_append,
-            check_window, check_ring, check_rmsnorm, check_project, check_combine, check_project_append]
+            check_window, check_ring, check_rmsnorm, check_project, check_combine, check_project_append,
+            check_gret_forms, check_gret_closed_forms, check_gret_packing]

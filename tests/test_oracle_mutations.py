@@ -8,11 +8,16 @@ row or without the overflow check, a window one row too wide or too narrow,
 ignored or aligned to fixed blocks, a ring append into the wrong slot or
 without wrap-around, an RMSNorm with sum for mean, eps outside the root, no or
 early gain, K and V weights swapped, the YOCO++ weights swapped or lambda
-dropped, projected rows appended at the sequence start or partially.
+dropped, projected rows appended at the sequence start or partially; a gRet
+decay that includes the row's own gate or drops the diagonal, a recurrence
+that decays the new term or reads the state before the update, a chunkwise
+carry without the decay into the row, an initial state not decayed by the
+first gate.
 """
 import numpy as np
 import pytest
 
+import oracle.gret as og
 import oracle.producer as op
 import oracle.xattn as ox
 import pinlib
@@ -132,6 +137,65 @@ def _append_partial_chunk(k_pool, v_pool, seq_start, seq_len, seq_cap, cu, x, ga
     return k2, v2, lens, flag
 
 
+def _decay_includes_own(gamma):
+    g = np.asarray(gamma, dtype=np.float64)
+    n = g.shape[0]
+    d = np.zeros((n, n))
+    for i in range(n):
+        d[i, i] = g[i]
+        for j in range(i - 1, -1, -1):
+            d[i, j] = d[i, j + 1] * g[j]
+    return d
+
+
+def _decay_strict(gamma):
+    return og.__dict__["_orig_decay"](gamma) - np.eye(len(gamma))
+
+
+def _recurrent_decay_after(q, k, v, gamma, s0=None):
+    s = np.zeros((k.shape[1], v.shape[1])) if s0 is None else np.array(s0, dtype=np.float64)
+    o = np.zeros((q.shape[0], v.shape[1]))
+    for t in range(q.shape[0]):
+        s = float(gamma[t]) * (s + np.outer(k[t], v[t]))
+        o[t] = q[t] @ s
+    return o, s
+
+
+def _recurrent_output_before_update(q, k, v, gamma, s0=None):
+    s = np.zeros((k.shape[1], v.shape[1])) if s0 is None else np.array(s0, dtype=np.float64)
+    o = np.zeros((q.shape[0], v.shape[1]))
+    for t in range(q.shape[0]):
+        o[t] = q[t] @ s
+        s = float(gamma[t]) * s + np.outer(k[t], v[t])
+    return o, s
+
+
+def _chunk_state_not_decayed(q, k, v, gamma, s0=None, chunk=256):
+    q, k, v, g = (np.asarray(x, dtype=np.float64) for x in (q, k, v, gamma))
+    s = np.zeros((k.shape[1], v.shape[1])) if s0 is None else np.array(s0, dtype=np.float64)
+    o = np.zeros((q.shape[0], v.shape[1]))
+    for c0 in range(0, q.shape[0], chunk):
+        c1 = min(c0 + chunk, q.shape[0])
+        d = og.gret_decay_matrix(g[c0:c1])
+        o[c0:c1] = ((q[c0:c1] @ k[c0:c1].T) * d) @ v[c0:c1] + q[c0:c1] @ s
+        s = np.prod(g[c0:c1]) * s + (d[-1][:, None] * k[c0:c1]).T @ v[c0:c1]
+    return o, s
+
+
+def _parallel_prefix_excludes_first(q, k, v, gamma, s0=None):
+    q, k, v, g = (np.asarray(x, dtype=np.float64) for x in (q, k, v, gamma))
+    d = og.gret_decay_matrix(g)
+    o = ((q @ k.T) * d) @ v
+    s_n = np.zeros((k.shape[1], v.shape[1]))
+    if s0 is not None:
+        prefix = np.concatenate([[1.0], np.cumprod(g[1:])]) if len(g) else np.zeros(0)
+        o = o + (prefix[:, None] * q) @ np.asarray(s0, dtype=np.float64)
+        s_n = (prefix[-1] if len(g) else 1.0) * np.asarray(s0, dtype=np.float64)
+    if len(g):
+        s_n = s_n + (d[-1][:, None] * k).T @ v
+    return o, s_n
+
+
 def _softmax_no_exp(s):
     m = np.max(s, axis=-1, keepdims=True)
     w = np.where(np.isfinite(s), s - m + 10.0, 0.0)
@@ -181,6 +245,12 @@ MUTATIONS = {
     "combine_without_lambda": ("op.kv_combine_ref", lambda km, kb, a1, a2, lam: a1 * kb + a2 * km),
     "project_append_at_sequence_start": ("op.project_append_ref", _append_chunk_at_start),
     "project_append_partial_chunk": ("op.project_append_ref", _append_partial_chunk),
+    "gret_decay_includes_own_gate": ("og.gret_decay_matrix", _decay_includes_own),
+    "gret_decay_without_diagonal": ("og.gret_decay_matrix", _decay_strict),
+    "gret_recurrence_decays_new_term": ("og.gret_recurrent_ref", _recurrent_decay_after),
+    "gret_output_before_state_update": ("og.gret_recurrent_ref", _recurrent_output_before_update),
+    "gret_chunk_state_not_decayed_to_row": ("og.gret_chunkwise_ref", _chunk_state_not_decayed),
+    "gret_prefix_decay_excludes_first": ("og.gret_parallel_ref", None),
 }
 
 
@@ -195,6 +265,11 @@ def test_mutation_is_caught(name, monkeypatch):
     module = ox
     if attr.startswith("op."):
         module, attr = op, attr[3:]
+    elif attr.startswith("og."):
+        module, attr = og, attr[3:]
+        monkeypatch.setitem(og.__dict__, "_orig_decay", og.gret_decay_matrix)
+        if repl is None:
+            repl = _parallel_prefix_excludes_first
     monkeypatch.setattr(module, attr, repl)
     caught = []
     for check in pinlib.ALL_PINS:
