@@ -22,14 +22,11 @@
 
 #include "internal.h"
 #include "lds_copy.h"
+#include "tile_common.h"
 
 namespace yoco {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPM = 256;           // rows per workgroup tile
 constexpr int kPN = 128;           // columns per workgroup tile
@@ -205,8 +202,6 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
 // v_mfma_f32_16x16x32_bf16 and add their partial tiles in LDS.
 constexpr int kSmallRows = 16;
 constexpr int kSmallWaves = 8;
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(64 * kSmallWaves) void kv_project_small_kernel(ProjectParams p) {
   __shared__ float part[kSmallWaves][kSmallRows][17];

@@ -34,18 +34,11 @@
 
 #include "internal.h"
 #include "lds_copy.h"
+#include "tile_common.h"
 
 namespace yoco {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef YOCO_PREFILL_STAGES
 #define YOCO_PREFILL_STAGES 4
@@ -57,11 +50,6 @@ constexpr int kStages = YOCO_PREFILL_STAGES;
 
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kRescaleSlack = 8.0f;   // base-2 growth of the running max tolerated before a rescale
-
-// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
-}
 
 // Wait until at most `ahead` (< kStages - 1) tiles of L loads each are still in flight.
 template <int L>
@@ -81,20 +69,6 @@ struct Geom {
   static constexpr int kStageBytes = 2 * kTileBytes;         // K^ tile then V^ tile
   static_assert(kChunks % kPrefillThreads == 0, "every thread issues the same number of loads");
 };
-
-// XOR applied to the 16-byte chunk index of V^ row r. A transposing read of one
-// wave covers 8 rows x 64 bytes; with these values its 16-lane groups (32 banks)
-// and its 32-lane halves (64 banks) both hit distinct banks (checked exhaustively
-// over the read pattern on the host).
-template <int D>
-__device__ __forceinline__ int v_swizzle(int r) {
-  if constexpr (D == 128) {
-    constexpr int t[4] = {0, 4, 10, 14};
-    return t[r & 3];
-  } else {
-    return 2 * (r & 3);
-  }
-}
 
 // Source offsets of this thread's chunks, relative to the tile's first row:
 // LDS chunk p = i * threads + t holds row p / cpr, swizzled chunk p % cpr.
