@@ -12,6 +12,9 @@ from .xattn import (  # noqa: F401
     YocoError,
     alloc_workspace,
     decode_splits,
+    gret_decode,
+    gret_prefill,
+    gret_workspace_size,
     kv_append,
     kv_append_ring,
     kv_project_append,

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "lib", "libyoco_xattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "kv_append.hip", "attn_f32.hip", "decode_merge.hip", "decode_bf16.hip", "prefill_bf16.hip",
-           "kv_project.hip"]
+           "kv_project.hip", "gret.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -331,6 +331,112 @@ yoco_status yoco_kv_project_append(const yoco_dims* dims, const yoco_kv_cache* c
   return YOCO_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int kGretChunk = 256;
+
+yoco_status check_gret(const yoco_gret_dims* d) {
+  if (d == nullptr) return YOCO_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->num_heads < 1) return YOCO_ERR_INVALID_ARG;
+  if (d->dtype != YOCO_DTYPE_BF16) return YOCO_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return YOCO_ERR_UNSUPPORTED;
+  return YOCO_OK;
+}
+
+struct GretWorkspace {
+  size_t state_off, in_off, decay_off, total;
+};
+
+GretWorkspace gret_workspace(const yoco_gret_dims* d, int64_t max_chunks) {
+  const size_t per = (size_t)d->batch * d->num_heads * max_chunks;
+  const size_t dd = (size_t)d->head_dim * d->head_dim;
+  GretWorkspace w;
+  w.state_off = 0;
+  w.in_off = (per * dd * 4 + 255) & ~(size_t)255;
+  w.decay_off = (w.in_off + per * dd * 2 + 255) & ~(size_t)255;
+  w.total = w.decay_off + per * 4;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int32_t max_len, size_t* bytes) {
+  yoco_status st = check_gret(dims);
+  if (st != YOCO_OK) return st;
+  if (bytes == nullptr || max_len < 0) return YOCO_ERR_INVALID_ARG;
+  *bytes = gret_workspace(dims, ((int64_t)max_len + kGretChunk - 1) / kGretChunk).total;
+  return YOCO_OK;
+}
+
+yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const void* k, const void* v,
+                              const float* gamma, const int32_t* cu_seqlens, int64_t total_rows, int32_t max_len,
+                              const float* state_in, float* state_out, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  yoco_status st = check_gret(dims);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || gamma == nullptr || cu_seqlens == nullptr || out == nullptr)
+    return YOCO_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(gamma) ||
+      !aligned4(cu_seqlens))
+    return YOCO_ERR_INVALID_ARG;
+  if ((state_in != nullptr && !aligned16(state_in)) || (state_out != nullptr && !aligned16(state_out)))
+    return YOCO_ERR_INVALID_ARG;
+  if (total_rows < 0 || max_len < 0) return YOCO_ERR_INVALID_ARG;
+  const int64_t chunks = ((int64_t)max_len + kGretChunk - 1) / kGretChunk;
+  if (chunks > 65535) return YOCO_ERR_UNSUPPORTED;
+  if (total_rows == 0 || chunks == 0) {
+    if (state_out == nullptr) return YOCO_OK;      // nothing to compute; a state still has to be passed on
+  }
+  const GretWorkspace w = gret_workspace(dims, chunks > 0 ? chunks : 1);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < w.total) return YOCO_ERR_WORKSPACE;
+  yoco::GretParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gamma = gamma;
+  p.out = out;
+  p.cu_seqlens = cu_seqlens;
+  p.state_in = state_in;
+  p.state_out = state_out;
+  char* ws = static_cast<char*>(workspace);
+  p.chunk_state = reinterpret_cast<float*>(ws + w.state_off);
+  p.chunk_in = reinterpret_cast<uint16_t*>(ws + w.in_off);
+  p.chunk_decay = reinterpret_cast<float*>(ws + w.decay_off);
+  p.total_rows = total_rows;
+  p.batch = dims->batch;
+  p.heads = dims->num_heads;
+  p.max_chunks = (int32_t)(chunks > 0 ? chunks : 1);
+  if (yoco::launch_gret_prefill(p, dims->head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return YOCO_ERR_HIP;
+  return YOCO_OK;
+}
+
+yoco_status yoco_gret_decode(const yoco_gret_dims* dims, const void* q, const void* k, const void* v,
+                             const float* gamma, float* state, void* out, void* stream) {
+  yoco_status st = check_gret(dims);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || gamma == nullptr || state == nullptr || out == nullptr)
+    return YOCO_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(gamma) || !aligned16(state))
+    return YOCO_ERR_INVALID_ARG;
+  yoco::GretParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gamma = gamma;
+  p.out = out;
+  p.state_out = state;
+  p.batch = dims->batch;
+  p.heads = dims->num_heads;
+  if (yoco::launch_gret_decode(p, dims->head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return YOCO_ERR_HIP;
+  return YOCO_OK;
+}
+
 const char* yoco_status_string(yoco_status status) {
   switch (status) {
     case YOCO_OK: return "ok";

@@ -1,0 +1,466 @@
+// Gated retention (gRet), the Self-Decoder's default attention ("YOCO 深度技术分析",
+// liuhc.cn, section 2.2: the parallel form (Q K^T ⊙ D) V with the data-controlled
+// decay D[n][m] = γ_{m+1} ... γ_n, the recurrent form S_n = γ_n S_{n-1} + K_n^T V_n,
+// o_n = Q_n S_n, and the chunkwise form; section 5.3.2: chunks of 256 rows).
+//
+// Prefill runs the chunkwise form in three launches, so that every (sequence,
+// head, chunk) works in parallel and only the cheap state recurrence is serial:
+//   1. gret_state_kernel: per chunk, U = sum_m w_m k_m^T v_m with w_m the decay
+//      from row m to the chunk's end, and the chunk's total decay G
+//      (MFMA: U^T = V^T diag(w) K, both operands by transposing LDS reads);
+//   2. gret_scan_kernel: S_{c+1} = G_c S_c + U_c over the chunks (fp32), writing
+//      each chunk's incoming state S_c (bf16, for the MFMA of step 3) and the
+//      final state;
+//   3. gret_out_kernel: o_j = e_j q_j S_c + sum_{m <= j} (e_j / e_m) (q_j . k_m) v_m
+//      with e_j the decay from the chunk's start to row j: the first term is one
+//      MFMA product with the staged S_c, the second the intra-chunk parallel
+//      form, tiled like attention (S^T = K Q^T, decay and causal mask on the
+//      accumulator registers, O^T += V^T P^T) but without a softmax.
+// Decays are handled as base-2 logarithms, accumulated along the chunk; a gate
+// below 2^-126 counts as 2^-126 (its products vanish below fp32's range).
+// Decode is the recurrent form's step on the fp32 state (gret_decode_kernel).
+#include "internal.h"
+#include "lds_copy.h"
+#include "tile_common.h"
+
+namespace yoco {
+
+namespace {
+
+constexpr int kGC = 256;           // rows per chunk
+constexpr int kGT = 64;            // keys per LDS tile in the output kernel
+constexpr int kGThreads = 512;     // 8 waves, 32 rows each
+constexpr float kLogGateFloor = -126.0f;
+
+// inclusive prefix sum of 256 values held by threads 0..255 (one each); every
+// thread of the workgroup must call it. Returns the sum up to and including
+// this thread's value (threads >= 256 get garbage).
+__device__ __forceinline__ float chunk_prefix(float x, float* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63 && wave < 4) wsum[wave] = x;
+  __syncthreads();
+  float add = 0.f;
+  for (int w = 0; w < wave && w < 4; ++w) add += wsum[w];
+  return x + add;
+}
+
+// base-2 log of the gate of chunk row j (rows past the chunk's end: gate 1)
+__device__ __forceinline__ float log2_gate(const float* gamma, int64_t row, int h, int H, bool valid) {
+  if (!valid) return 0.f;
+  const float g = gamma[row * H + h];
+  const float l = __log2f(g);
+  return l > kLogGateFloor ? l : kLogGateFloor;   // also catches g = 0 (log -inf) and NaN-free clamps
+}
+
+// LDS byte offset of 16-byte chunk c of row r of a row-major [rows][D] bf16 tile
+// that is read with transposing reads
+template <int D>
+__device__ __forceinline__ uint32_t tr_slot(int r, int c) {
+  return (uint32_t)(r * (D * 2) + 16 * (c ^ v_swizzle<D>(r)));
+}
+// ... and of one that is read row-wise (16 bytes per lane): chunk c at c ^ (r mod chunks)
+template <int D>
+__device__ __forceinline__ uint32_t row_slot(int r, int c) {
+  return (uint32_t)(r * (D * 2) + 16 * (c ^ (r & (D / 8 - 1))));
+}
+
+// Transposing read: 8 bf16 of one column (dim 32t + lane col) at rows
+// base + 4h + {0..3} and base + 8 + 4h + {0..3} of a tr_slot tile.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const YOCO_LDS char* tile, int base_row, int t, int lane) {
+  const int i = lane & 15, g = lane >> 4, h = lane >> 5;
+  const int q = i >> 2, w = i & 3;
+  const int r = base_row + 4 * h + q;
+  const int chunk = 4 * t + 2 * (g & 1) + (w >> 1);
+  const YOCO_LDS char* p = tile + tr_slot<D>(r, chunk) + 8 * (w & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p + 8 * (D * 2)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Copy rows [0, n_rows) of a [rows, H, D] bf16 tensor (row stride H*D) starting
+// at global row `row0` into a tile of `rows` rows (rows >= n_rows repeat row
+// n_rows - 1), in the tr_slot (TR) or row_slot layout, by the load unit.
+template <int D, bool TR>
+__device__ __forceinline__ void load_tile(const __bf16* src, int64_t row0, int n_rows, int rows, int H, int h,
+                                          uint32_t lds) {
+  constexpr int cpr = D / 8;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int i = 0; i < rows * cpr / kGThreads; ++i) {
+    const int p = i * kGThreads + (int)threadIdx.x;
+    const int r = p / cpr, slot = p % cpr;
+    const int c = TR ? (slot ^ v_swizzle<D>(r)) : (slot ^ (r & (cpr - 1)));
+    const int rr = r < n_rows ? r : n_rows - 1;
+    dma16(src + ((row0 + rr) * H + h) * D + 8 * c, lds + (i * kGThreads + wave * 64) * 16);
+  }
+}
+
+struct ChunkInfo {
+  int64_t row0;   // first global row of the chunk
+  int n;          // rows of the chunk (0: no chunk)
+};
+
+__device__ __forceinline__ ChunkInfo chunk_info(const GretParams& p, int b, int c) {
+  int64_t r0 = p.cu_seqlens[b], r1 = p.cu_seqlens[b + 1];
+  if (r1 > p.total_rows) r1 = p.total_rows;
+  ChunkInfo ci{r0 + (int64_t)c * kGC, 0};
+  if (r0 < 0 || r1 <= r0) return ci;
+  const int64_t left = r1 - ci.row0;
+  ci.n = left <= 0 ? 0 : (left < kGC ? (int)left : kGC);
+  return ci;
+}
+
+// ---------------------------------------------------------------------------
+// 1. per-chunk state contribution U^T[dv][dk] and total decay
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kGThreads, 1) void gret_state_kernel(GretParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kGC * D * 2];
+  __shared__ __attribute__((aligned(16))) float wgt[kGC];
+  __shared__ float wsum[4];
+  YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const ChunkInfo ci = chunk_info(p, b, c);
+  if (ci.n == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t kl = (uint32_t)(uintptr_t)smem, vl = kl + kGC * D * 2;
+  load_tile<D, true>(static_cast<const __bf16*>(p.k), ci.row0, ci.n, kGC, p.heads, h, kl);
+  load_tile<D, true>(static_cast<const __bf16*>(p.v), ci.row0, ci.n, kGC, p.heads, h, vl);
+
+  // decay from row m to the chunk's end: 2^(A_last - A_m), A = prefix of log2 gates
+  const float a = log2_gate(p.gamma, ci.row0 + tid, h, p.heads, tid < ci.n);
+  const float A = chunk_prefix(a, wsum);
+  const float a_last = wsum[0] + wsum[1] + wsum[2] + wsum[3];   // gates past the end count 1
+  if (tid < kGC) wgt[tid] = tid < ci.n ? exp2f(a_last - A) : 0.f;
+  if (tid == 0) p.chunk_decay[((int64_t)b * p.heads + h) * p.max_chunks + c] = exp2f(a_last);
+  wait_vm_lgkm0<0>();
+  __syncthreads();
+
+  // output blocks (dv block i, dk block j) of 32 x 32; D = 128: 16 blocks, two per
+  // wave (same i); D = 64: 4 blocks, waves 0..3
+  constexpr int NB = D / 32;
+  constexpr int PER = (NB * NB) / 8 > 0 ? (NB * NB) / 8 : 1;
+  if (wave * PER >= NB * NB) return;
+  const int blk0 = wave * PER;
+  const int bi = blk0 / NB;
+  f32x16 acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = f32x16{};
+  const int hf = lane >> 5;
+  const YOCO_LDS char* kt = smem;
+  const YOCO_LDS char* vt = smem + kGC * D * 2;
+  for (int s = 0; s < kGC / 16; ++s) {
+    // k-step s: keys base + {0..3, 8..11} + 4h with base = 16 s (two 4-key runs per lane)
+    const int base = 16 * s;
+    const bf16x8 av = read_tr<D>(vt, base, bi, lane);                 // V^T rows dv, 8 keys
+    const f32x4 w0 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (base + 4 * hf));
+    const f32x4 w1 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (base + 8 + 4 * hf));
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int bj = (blk0 + e) % NB;
+      const bf16x8 kb = read_tr<D>(kt, base, bj, lane);               // K columns dk, same 8 keys
+      uint32_t wv[4];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const f32x4 ww = z == 0 ? w0 : w1;
+        wv[2 * z] = pack2((float)kb[4 * z + 0] * ww[0], (float)kb[4 * z + 1] * ww[1]);
+        wv[2 * z + 1] = pack2((float)kb[4 * z + 2] * ww[2], (float)kb[4 * z + 3] * ww[3]);
+      }
+      const bf16x8 kw = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+      acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, kw, acc[e], 0, 0, 0);
+    }
+  }
+  // lane holds dk = 32 bj + lane % 32, dv rows 32 bi + 8(r/4) + 4hf + r%4
+  float* u = p.chunk_state + (((int64_t)b * p.heads + h) * p.max_chunks + c) * (D * D);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int bj = (blk0 + e) % NB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dv = 32 * bi + 8 * (r >> 2) + 4 * hf + (r & 3);
+      u[dv * D + 32 * bj + (lane & 31)] = acc[e][r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. the state recurrence across chunks
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void gret_scan_kernel(GretParams p) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;   // element (dv, dk..dk+3) of S^T
+  if (e0 >= D * D) return;
+  const int dv = e0 / D, dk = e0 % D;
+  int64_t r0 = p.cu_seqlens[b], r1 = p.cu_seqlens[b + 1];
+  if (r1 > p.total_rows) r1 = p.total_rows;
+  const int64_t n = (r0 >= 0 && r1 > r0) ? r1 - r0 : 0;
+  int64_t nc = (n + kGC - 1) / kGC;
+  if (nc > p.max_chunks) nc = p.max_chunks;     // rows past the planned chunks are not computed
+  const int64_t bh = (int64_t)b * p.heads + h;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.state_in != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = p.state_in[(bh * D + dk + i) * D + dv];
+  }
+  for (int c = 0; c < nc; ++c) {
+    const int64_t off = (bh * p.max_chunks + c) * (D * D) + e0;
+    *reinterpret_cast<u32x2*>(p.chunk_in + off) = u32x2{pack2(s[0], s[1]), pack2(s[2], s[3])};
+    const float g = p.chunk_decay[bh * p.max_chunks + c];
+    const f32x4 u = *reinterpret_cast<const f32x4*>(p.chunk_state + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = fmaf(g, s[i], u[i]);
+  }
+  if (p.state_out != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p.state_out[(bh * D + dk + i) * D + dv] = s[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. outputs of one chunk
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
+  constexpr int kTile = kGT * D * 2;          // one K or V tile
+  constexpr int kStage = 2 * kTile;
+  constexpr int kOStride = D + 8;
+  static_assert(8 * 32 * kOStride * 2 <= 2 * kStage + D * D * 2, "staging fits");
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kStage + D * D * 2];
+  __shared__ __attribute__((aligned(16))) float A_lds[kGC];
+  __shared__ float wsum[4];
+  YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const ChunkInfo ci = chunk_info(p, b, c);
+  if (ci.n == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qj = lane & 31, hf = lane >> 5;
+  const int H = p.heads;
+  const uint32_t base_lds = (uint32_t)(uintptr_t)smem;
+  const uint32_t s_lds = base_lds + 2 * kStage;      // S_c^T [dv][dk], row_slot layout
+  const int n_tiles = (ci.n + kGT - 1) / kGT;
+  const __bf16* kg = static_cast<const __bf16*>(p.k);
+  const __bf16* vg = static_cast<const __bf16*>(p.v);
+  const int64_t bh = (int64_t)b * H + h;
+  const bool has_state = c > 0 || p.state_in != nullptr;
+
+  // incoming state (bf16 [dv][dk] in the workspace) and the first two K/V tiles
+  if (has_state) {
+    constexpr int cpr = D / 8;
+    const __bf16* sg = reinterpret_cast<const __bf16*>(p.chunk_in) + (bh * p.max_chunks + c) * (D * D);
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
+    for (int i = 0; i < D * cpr / kGThreads; ++i) {
+      const int q = i * kGThreads + tid;
+      const int r = q / cpr, slot = q % cpr;
+      dma16(sg + r * D + 8 * (slot ^ (r & (cpr - 1))), s_lds + (i * kGThreads + wv * 64) * 16);
+    }
+  }
+  auto issue = [&](int t) {
+    const uint32_t st = base_lds + (t & 1) * kStage;
+    const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
+    load_tile<D, false>(kg, ci.row0 + t * kGT, n_t, kGT, H, h, st);
+    load_tile<D, true>(vg, ci.row0 + t * kGT, n_t, kGT, H, h, st + kTile);
+  };
+  issue(0);
+  if (n_tiles > 1) issue(1);
+
+  // decay prefix A_j (base 2) of the chunk's rows
+  const float a = log2_gate(p.gamma, ci.row0 + tid, h, H, tid < ci.n);
+  const float A = chunk_prefix(a, wsum);
+  if (tid < kGC) A_lds[tid] = A;
+
+  // Q^T as the B operand: query row qj of this wave, dims 16kk + 8hf .. +7
+  const int j_row = 32 * wave + qj;                         // row within the chunk
+  const int j_load = j_row < ci.n ? j_row : ci.n - 1;
+  bf16x8 qf[D / 16];
+  {
+    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + ((ci.row0 + j_load) * H + h) * D + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qsrc + 16 * kk));
+  }
+  wait_vm_lgkm0<0>();
+  __syncthreads();   // state, first tiles and A in LDS (the second tile too: all waited)
+
+  const bool wave_active = 32 * wave < ci.n;
+  const float Aj = A_lds[j_load];
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  if (has_state && wave_active) {
+    // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j
+    const YOCO_LDS char* sl = smem + 2 * kStage;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 sa = *reinterpret_cast<const YOCO_LDS bf16x8*>(sl + row_slot<D>(32 * t + qj, 2 * kk + hf));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qf[kk], acc[t], 0, 0, 0);
+      }
+    }
+    const float e = exp2f(Aj);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] *= e;
+  }
+
+  // intra-chunk term, tile by tile
+  constexpr int L = 2 * (kGT * D / 8 / kGThreads);   // copies per thread and tile
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t > 0) {
+      // tile t is in when at most the copies of tile t + 1 (if requested) are in flight
+      if (t + 1 < n_tiles) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();
+      __syncthreads();
+    }
+    const int key0 = t * kGT;
+    if (wave_active && key0 <= j_row) {
+      const YOCO_LDS char* ks = smem + (t & 1) * kStage;
+      const YOCO_LDS char* vs = ks + kTile;
+      // S^T[m][j] = K Q^T: two 32-key chains
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ka = *reinterpret_cast<const YOCO_LDS bf16x8*>(ks + row_slot<D>(32 * kb + qj, 2 * kk + hf));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[kb], 0, 0, 0);
+        }
+      }
+      // P^T = S^T * 2^(A_j - A_m) for m <= j, else 0; register r of chain kb is
+      // key key0 + 32kb + 8(r/4) + 4hf + r%4
+      uint32_t w[2][2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int m0 = key0 + 32 * kb + 8 * g4 + 4 * hf;
+          const f32x4 am = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)A_lds + 4 * m0);
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float d = exp2f(Aj - am[e]);
+            pv[e] = (m0 + e <= j_row) ? s[kb][4 * g4 + e] * d : 0.f;
+          }
+          w[kb][g4 >> 1][2 * (g4 & 1)] = pack2(pv[0], pv[1]);
+          w[kb][g4 >> 1][2 * (g4 & 1) + 1] = pack2(pv[2], pv[3]);
+        }
+      }
+      // O^T += V^T P^T: B operand of step (kb, cc) = registers 8cc .. 8cc + 7 of chain kb
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[kb][cc][0], w[kb][cc][1], w[kb][cc][2],
+                                                                  w[kb][cc][3]));
+#pragma unroll
+          for (int tt = 0; tt < D / 32; ++tt) {
+            const bf16x8 va = read_tr<D>(vs, 32 * kb + 16 * cc, tt, lane);
+            acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[tt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (t + 2 < n_tiles) {
+      __syncthreads();   // every wave is done with stage t & 1
+      issue(t + 2);
+    }
+  }
+  wait_vm_lgkm0<0>();
+  __syncthreads();   // the tiles are done with: stage the outputs in LDS
+
+  YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)smem + wave * (32 * kOStride);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const u32x2 wv = {pack2(acc[t][4 * g4 + 0], acc[t][4 * g4 + 1]), pack2(acc[t][4 * g4 + 2], acc[t][4 * g4 + 3])};
+      *reinterpret_cast<YOCO_LDS u32x2*>(ot + qj * kOStride + 32 * t + 8 * g4 + 4 * hf) = wv;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __bf16* obase = static_cast<__bf16*>(p.out);
+#pragma unroll
+  for (int i = 0; i < 32 * (D / 8) / 64; ++i) {
+    const int ci8 = lane + 64 * i;
+    const int row = ci8 / (D / 8), c8 = ci8 % (D / 8);
+    const int jr = 32 * wave + row;
+    if (jr < ci.n)
+      *reinterpret_cast<u32x4*>(obase + ((ci.row0 + jr) * H + h) * D + 8 * c8) =
+          *reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode: one recurrent step per (sequence, head)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void gret_decode_kernel(GretParams p) {
+  constexpr int kParts = 256 / D;                 // threads per state column
+  constexpr int kRows = D / kParts;               // dk rows per thread
+  __shared__ float qk[2][D];
+  __shared__ float part[kParts][D];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t bh = (int64_t)b * p.heads + h;
+  const int tid = threadIdx.x;
+  const __bf16* q = static_cast<const __bf16*>(p.q) + bh * D;
+  const __bf16* k = static_cast<const __bf16*>(p.k) + bh * D;
+  const __bf16* v = static_cast<const __bf16*>(p.v) + bh * D;
+  if (tid < D) {
+    qk[0][tid] = (float)q[tid];
+    qk[1][tid] = (float)k[tid];
+  }
+  __syncthreads();
+  const int col = tid % D, part_i = tid / D;
+  const float g = p.gamma[bh];
+  const float vv = (float)v[col];
+  float* st = p.state_out + bh * D * D;
+  float o = 0.f;
+#pragma unroll 8
+  for (int i = part_i * kRows; i < (part_i + 1) * kRows; ++i) {
+    const float s = fmaf(g, st[i * D + col], qk[1][i] * vv);
+    st[i * D + col] = s;
+    o = fmaf(qk[0][i], s, o);
+  }
+  part[part_i][col] = o;
+  __syncthreads();
+  if (tid < D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kParts; ++i) sum += part[i][tid];
+    static_cast<__bf16*>(p.out)[bh * D + tid] = (__bf16)sum;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gret_prefill(const GretParams& p, int head_dim, hipStream_t stream) {
+  const dim3 grid_c(p.max_chunks, p.heads, p.batch);
+  const dim3 grid_s((head_dim * head_dim / 4 + 255) / 256, p.heads, p.batch);
+  if (head_dim == 64) {
+    hipLaunchKernelGGL(gret_state_kernel<64>, grid_c, dim3(kGThreads), 0, stream, p);
+    hipLaunchKernelGGL(gret_scan_kernel<64>, grid_s, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gret_out_kernel<64>, grid_c, dim3(kGThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(gret_state_kernel<128>, grid_c, dim3(kGThreads), 0, stream, p);
+    hipLaunchKernelGGL(gret_scan_kernel<128>, grid_s, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gret_out_kernel<128>, grid_c, dim3(kGThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gret_decode(const GretParams& p, int head_dim, hipStream_t stream) {
+  const dim3 grid(p.heads, p.batch);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(gret_decode_kernel<64>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gret_decode_kernel<128>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

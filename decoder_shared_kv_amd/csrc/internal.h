@@ -71,6 +71,25 @@ struct ProjectParams {
   float lam, ak1, ak2, av1, av2;
 };
 
+// Gated retention (gRet): chunkwise prefill and recurrent decode.
+struct GretParams {
+  const void* q;              // [T, H, D] bf16 (decode: [B, H, D])
+  const void* k;
+  const void* v;
+  const float* gamma;         // [T, H] (decode: [B, H]) per-token, per-head gates
+  void* out;                  // [T, H, D] bf16 (decode: [B, H, D])
+  const int32_t* cu_seqlens;  // [B + 1] (prefill)
+  const float* state_in;      // [B, H, D(dk), D(dv)] fp32 or null (prefill)
+  float* state_out;           // [B, H, D, D]: prefill's final states; decode's states, updated in place
+  float* chunk_state;         // workspace: per chunk U^T [D(dv)][D(dk)] fp32
+  uint16_t* chunk_in;         // workspace: per chunk incoming state S^T, bf16 bits
+  float* chunk_decay;         // workspace: per chunk total decay
+  int64_t total_rows;
+  int32_t batch;
+  int32_t heads;
+  int32_t max_chunks;         // chunks of the longest sequence (grid and workspace stride)
+};
+
 // Host launchers (one per kernel family); each returns the hipGetLastError code.
 hipError_t launch_kv_append(const AppendParams& p, int batch, hipStream_t stream);
 hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
@@ -79,6 +98,8 @@ hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream
 hipError_t launch_decode_split_f32(const AttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_kv_project(const ProjectParams& p, hipStream_t stream);
+hipError_t launch_gret_prefill(const GretParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_gret_decode(const GretParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_pack(const void* gain, const void* wk, const void* wv, void* out, int k_dim, int hd,
                           hipStream_t stream);
 

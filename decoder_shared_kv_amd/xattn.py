@@ -7,7 +7,8 @@ There is no fallback: if the library is missing, loading raises.
 The functions mirror the C ABI (include/yoco_xattn.h) one to one:
 ``kv_append``, ``kv_append_ring``, ``xattn_prefill``, ``xattn_prefill_window``,
 ``xattn_decode``, ``xattn_decode_window``, ``workspace_size``, ``decode_splits``,
-``kv_project_pack``, ``kv_project_append``.
+``kv_project_pack``, ``kv_project_append``, ``gret_workspace_size``, ``gret_prefill``,
+``gret_decode``.
 """
 from __future__ import annotations
 
@@ -27,7 +28,8 @@ DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTS = ("yoco_kv_append", "yoco_kv_append_ring", "yoco_xattn_prefill", "yoco_xattn_prefill_window",
            "yoco_xattn_decode", "yoco_xattn_decode_window", "yoco_xattn_workspace_size",
-           "yoco_xattn_decode_splits", "yoco_kv_project_pack", "yoco_kv_project_append", "yoco_status_string")
+           "yoco_xattn_decode_splits", "yoco_kv_project_pack", "yoco_kv_project_append", "yoco_gret_workspace_size",
+           "yoco_gret_prefill", "yoco_gret_decode", "yoco_status_string")
 
 
 class YocoError(RuntimeError):
@@ -44,6 +46,11 @@ class Dims(ctypes.Structure):
 class KvCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pool_rows", ctypes.c_int64),
                 ("seq_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("seq_cap", ctypes.c_void_p)]
+
+
+class GretDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
 class Residual(ctypes.Structure):
@@ -75,6 +82,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_kv_project_pack.argtypes = [dims_p, i32, P, P, P, P, P]
     lib.yoco_kv_project_append.argtypes = [dims_p, cache_p, P, P, i64, i32, P, ctypes.c_float,
                                            ctypes.POINTER(Residual), P, P]
+    gdims_p = ctypes.POINTER(GretDims)
+    lib.yoco_gret_workspace_size.argtypes = [gdims_p, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.yoco_gret_prefill.argtypes = [gdims_p, P, P, P, P, P, i64, i32, P, P, P, P, ctypes.c_size_t, P]
+    lib.yoco_gret_decode.argtypes = [gdims_p, P, P, P, P, P, P, P]
     lib.yoco_xattn_workspace_size.argtypes = [dims_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.yoco_xattn_decode_splits.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                              ctypes.POINTER(ctypes.c_int32)]
@@ -273,3 +284,47 @@ def kv_project_append(cache: SharedKV, x: torch.Tensor, cu_seqlens: torch.Tensor
                                       int(x.shape[0]), int(x.shape[1]), _ptr(w_packed), float(eps),
                                       ctypes.byref(res) if res is not None else None, _ptr(overflow),
                                       _stream(stream)), "yoco_kv_project_append")
+
+
+def gret_dims(batch: int, heads: int, head_dim: int, dtype: torch.dtype = torch.bfloat16) -> GretDims:
+    if dtype not in DTYPE_CODE:
+        raise YocoError(2, f"dtype {dtype}")
+    return GretDims(batch, heads, head_dim, DTYPE_CODE[dtype])
+
+
+def gret_workspace_size(batch: int, heads: int, head_dim: int, max_len: int) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.yoco_gret_workspace_size(ctypes.byref(gret_dims(batch, heads, head_dim)), int(max_len),
+                                        ctypes.byref(n)), "yoco_gret_workspace_size")
+    return int(n.value)
+
+
+def gret_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, cu_seqlens: torch.Tensor,
+                 max_len: int, workspace: torch.Tensor, state_in: Optional[torch.Tensor] = None,
+                 state_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
+    """Gated retention over packed sequences (q, k, v [T, H, d] bf16, gamma [T, H] fp32); returns out."""
+    lib = load_library()
+    total, heads, d = q.shape
+    batch = int(cu_seqlens.shape[0]) - 1
+    if out is None:
+        out = torch.empty_like(v)
+    dims = gret_dims(batch, heads, d, q.dtype)
+    _check(lib.yoco_gret_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(cu_seqlens),
+                                 int(total), int(max_len), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                 _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                 _stream(stream)), "yoco_gret_prefill")
+    return out
+
+
+def gret_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, state: torch.Tensor,
+                out: Optional[torch.Tensor] = None, stream=None):
+    """One recurrent gRet step (q, k, v [B, H, d], gamma [B, H]); updates state [B, H, d, d] in place."""
+    lib = load_library()
+    batch, heads, d = q.shape
+    if out is None:
+        out = torch.empty_like(v)
+    dims = gret_dims(batch, heads, d, q.dtype)
+    _check(lib.yoco_gret_decode(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(state), _ptr(out),
+                                _stream(stream)), "yoco_gret_decode")
+    return out

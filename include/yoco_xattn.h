@@ -251,6 +251,57 @@ yoco_status yoco_kv_project_append(const yoco_dims* dims, const yoco_kv_cache* c
                                    const yoco_kv_residual* residual, int32_t* overflow_flag,
                                    void* stream);
 
+/*
+ * Gated retention (gRet), the Self-Decoder's default attention
+ * -------------------------------------------------------------
+ * Page "YOCO 深度技术分析", section 2.2 (three equivalent forms) and 5.3.2
+ * (chunkwise for prefill, chunk size 256; recurrent for decode):
+ *   parallel   O = (Q K^T ⊙ D) V,  D[n][m] = γ_{m+1} γ_{m+2} ... γ_n (m <= n), 0 (m > n)
+ *   recurrent  S_n = γ_n S_{n-1} + K_n^T V_n,  o_n = Q_n S_n
+ * Q and K come already multiplied by the caller's Θ; γ is one gate per token
+ * and head (the head-wise γ = sigmoid(X W_γ)^(1/τ)), in (0, 1]; a gate below
+ * 2^-126 counts as 2^-126. No scale, no normalisation inside (GroupNorm and the
+ * swish gate are outside). Layouts: q, k, v, out [T, H, head_dim] bf16 (one head
+ * dim for K and V); gamma [T, H] fp32; states [B, H, head_dim (k), head_dim (v)]
+ * fp32, the recurrent form's S. Products are bf16 MFMA with fp32 accumulation;
+ * the state recurrence is fp32; outputs are rounded once to bf16.
+ */
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t num_heads;   /* H >= 1 */
+  int32_t head_dim;    /* d_k = d_v, 64 or 128 */
+  int32_t dtype;       /* YOCO_DTYPE_BF16 (fp32 storage: YOCO_ERR_UNSUPPORTED) */
+} yoco_gret_dims;
+
+/* [host] Workspace bytes of yoco_gret_prefill for sequences of at most max_len rows. */
+yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int32_t max_len, size_t* bytes);
+
+/*
+ * yoco_gret_prefill -- the chunkwise form over packed sequences: sequence b owns
+ * rows cu_seqlens[b] .. cu_seqlens[b+1]-1. Three launches: per-chunk state
+ * contributions, the state recurrence across chunks, per-chunk outputs.
+ *   max_len    [host] the longest sequence's rows; it sizes the grid and the
+ *              workspace and MUST be >= every sequence's length (rows past
+ *              max_len rounded up to a chunk are not computed)
+ *   state_in   [device] [B, H, d, d] fp32 initial states, or NULL for zero
+ *   state_out  [device] [B, H, d, d] fp32 states after each sequence's last row,
+ *              or NULL; may be the same buffer as state_in
+ *   workspace  [device] >= yoco_gret_workspace_size(dims, max_len), 16-byte
+ *              aligned; needs no initialisation; serialise calls that share it
+ */
+yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const void* k, const void* v,
+                              const float* gamma, const int32_t* cu_seqlens, int64_t total_rows,
+                              int32_t max_len, const float* state_in, float* state_out, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * yoco_gret_decode -- one recurrent step per sequence and head: q, k, v
+ * [B, H, d] bf16, gamma [B, H] fp32; state [B, H, d, d] fp32 is updated in
+ * place (S = γ S + k^T v) and out [B, H, d] bf16 gets q S.
+ */
+yoco_status yoco_gret_decode(const yoco_gret_dims* dims, const void* q, const void* k, const void* v,
+                             const float* gamma, float* state, void* out, void* stream);
+
 /* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len (any
  * total_kv_len, any smaller max_kv_len). */
 yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes);

@@ -1,0 +1,129 @@
+"""Gated retention through the C ABI against the fp64 oracle: chunkwise prefill
+(packed sequences, partial chunks, head_dim 64 and 128, with and without an
+initial state, gates that close completely), the final states, recurrent
+decode steps, and the chain prefill -> decode."""
+import numpy as np
+import pytest
+import torch
+
+import decoder_shared_kv_amd as dk
+import oracle
+import parity
+import synth
+from gpu_util import DEV, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(lens, heads, d, seed, with_state):
+    g = torch.Generator().manual_seed(seed)
+    T = int(sum(lens))
+    std = d ** -0.25                      # q.k ~ N(0, 1): unit-spread scores
+    q = (torch.randn(T, heads, d, generator=g) * std).to(torch.bfloat16)
+    k = (torch.randn(T, heads, d, generator=g) * std).to(torch.bfloat16)
+    v = torch.randn(T, heads, d, generator=g).to(torch.bfloat16)
+    gam = 0.8 + 0.2 * torch.rand(T, heads, generator=g)
+    gam[torch.rand(T, heads, generator=g) < 0.05] = 1.0
+    gam[torch.rand(T, heads, generator=g) < 0.02] = 0.01
+    if T > 40:
+        gam[37, 0] = 0.0                  # a gate that closes completely
+    s0 = torch.randn(len(lens), heads, d, d, generator=g) * 0.1 if with_state else None
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    return q, k, v, gam.float(), s0, cu
+
+
+def _state_check(st, ref, what):
+    err = np.abs(st - ref).reshape(st.shape[0] * st.shape[1], -1).max(axis=1)
+    mag = np.abs(ref).reshape(ref.shape[0] * ref.shape[1], -1).max(axis=1)
+    rel = float((err / np.maximum(mag, 1e-30)).max())
+    assert rel <= 1e-2, f"{what}: state relative error {rel:.3e}"
+    return rel
+
+
+def _run_prefill(q, k, v, gam, s0, cu, lens):
+    heads, d = q.shape[1], q.shape[2]
+    ws = torch.empty(dk.gret_workspace_size(len(lens), heads, d, max(lens)), dtype=torch.uint8, device=DEV)
+    st = torch.full((len(lens), heads, d, d), float("nan"), device=DEV)
+    out = dk.gret_prefill(q.to(DEV), k.to(DEV), v.to(DEV), gam.to(DEV), cu.to(DEV), max(lens), ws,
+                          state_in=None if s0 is None else s0.to(DEV), state_out=st)
+    torch.cuda.synchronize()
+    return f64(out), st.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("lens,heads,d,with_state", [
+    ([1000], 4, 128, False),            # 3 full chunks and a partial one
+    ([256, 300, 17], 2, 128, True),     # a whole chunk, a chunk and a bit, a tiny one
+    ([700], 3, 64, True),               # head_dim 64
+    ([5000, 1234], 4, 128, True),
+])
+def test_gret_prefill(lens, heads, d, with_state):
+    say(f"gret prefill lens={lens} H={heads} d={d} state={with_state}")
+    q, k, v, gam, s0, cu = _inputs(lens, heads, d, seed=sum(lens) + d, with_state=with_state)
+    out, st = _run_prefill(q, k, v, gam, s0, cu, lens)
+    ref, ref_st = oracle.gret_prefill_ref(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), gam.double().numpy(),
+                                          cu.numpy(), None if s0 is None else s0.double().numpy())
+    e = parity.check(out, ref, "bf16", discriminating=True, what="gret prefill")
+    rel = _state_check(st, ref_st, "gret prefill")
+    say(f"  out row-rel {e['row_rel']:.2e}, state rel {rel:.2e}")
+
+
+def test_gret_decode_steps():
+    say("gret decode: 5 recurrent steps from a prefill's state")
+    lens, heads, d = [300, 77, 1], 4, 128
+    q, k, v, gam, s0, cu = _inputs(lens, heads, d, seed=3, with_state=True)
+    _, st_ref = oracle.gret_prefill_ref(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), gam.double().numpy(),
+                                        cu.numpy(), s0.double().numpy())
+    state = torch.from_numpy(st_ref.astype(np.float32)).to(DEV)
+    cur = st_ref.astype(np.float32).astype(np.float64)
+    g = torch.Generator().manual_seed(4)
+    for step in range(5):
+        qd = (torch.randn(3, heads, d, generator=g) * d ** -0.25).to(torch.bfloat16)
+        kd = (torch.randn(3, heads, d, generator=g) * d ** -0.25).to(torch.bfloat16)
+        vd = torch.randn(3, heads, d, generator=g).to(torch.bfloat16)
+        gd = (0.8 + 0.2 * torch.rand(3, heads, generator=g)).float()
+        out = dk.gret_decode(qd.to(DEV), kd.to(DEV), vd.to(DEV), gd.to(DEV), state)
+        torch.cuda.synchronize()
+        ref, cur = oracle.gret_decode_ref(synth.to_f64(qd), synth.to_f64(kd), synth.to_f64(vd), gd.double().numpy(),
+                                          cur)
+        parity.check(f64(out), ref, "bf16", discriminating=True, what=f"gret decode step {step}")
+        err = np.abs(state.cpu().numpy() - cur).max() / np.abs(cur).max()
+        assert err <= 1e-5, f"decode state step {step}: {err:.2e}"   # the step is fp32 throughout
+
+
+def test_gret_prefill_then_decode_equals_longer_prefill():
+    """Decode of row n from the state after rows 0..n-1 = row n of the prefill of n + 1 rows."""
+    lens, heads, d = [513], 2, 128
+    q, k, v, gam, s0, cu = _inputs(lens, heads, d, seed=8, with_state=False)
+    out_full, st_full = _run_prefill(q, k, v, gam, None, cu, lens)
+    n = 512
+    _, st_n = _run_prefill(q[:n], k[:n], v[:n], gam[:n], None, torch.tensor([0, n], dtype=torch.int32), [n])
+    state = torch.from_numpy(st_n.astype(np.float32)).to(DEV)
+    out = dk.gret_decode(q[n:].to(DEV), k[n:].to(DEV), v[n:].to(DEV), gam[n:].to(DEV), state)
+    torch.cuda.synchronize()
+    assert parity.errors(f64(out), out_full[n:n + 1])["row_rel"] < 2e-2
+    assert np.abs(state.cpu().numpy() - st_full).max() / np.abs(st_full).max() < 2e-2
+
+
+def test_gret_state_passing_equals_one_call():
+    lens, heads, d = [900], 2, 64
+    q, k, v, gam, s0, cu = _inputs(lens, heads, d, seed=12, with_state=True)
+    out_full, st_full = _run_prefill(q, k, v, gam, s0, cu, lens)
+    a = 333
+    out_a, st_a = _run_prefill(q[:a], k[:a], v[:a], gam[:a], s0, torch.tensor([0, a], dtype=torch.int32), [a])
+    out_b, st_b = _run_prefill(q[a:], k[a:], v[a:], gam[a:], torch.from_numpy(st_a.astype(np.float32)),
+                               torch.tensor([0, 900 - a], dtype=torch.int32), [900 - a])
+    assert parity.errors(np.concatenate([out_a, out_b]), out_full)["row_rel"] < 2e-2
+    assert np.abs(st_b - st_full).max() / np.abs(st_full).max() < 2e-2
+
+
+def test_gret_32k_two_heads_against_recurrence():
+    """A 32K-row sequence (128 chunks), heads checked against the fp64 recurrence."""
+    say("gret prefill 32K rows, 16 heads; heads 0 and 9 against the fp64 recurrence")
+    lens, heads, d = [32768], 16, 128
+    q, k, v, gam, s0, cu = _inputs(lens, heads, d, seed=21, with_state=False)
+    out, st = _run_prefill(q, k, v, gam, None, cu, lens)
+    for h in (0, 9):
+        ref, ref_st = oracle.gret_recurrent_ref(synth.to_f64(q[:, h]), synth.to_f64(k[:, h]), synth.to_f64(v[:, h]),
+                                                gam[:, h].double().numpy())
+        parity.check(out[:, h][:, None], ref[:, None], "bf16", discriminating=True, what=f"32K head {h}")
+        _state_check(st[:1, h:h + 1], ref_st[None, None], f"32K head {h}")
