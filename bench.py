@@ -15,6 +15,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                                   token decode over ring window caches)
        python bench.py --workload producer      (RMSNorm + [W_K|W_V] projection into the shared cache,
                                                   d_model 3072, 8 KV heads: a 32K prompt, then decode rows)
+       python bench.py --workload gret          (gated retention: chunkwise prefill of 32K rows x 16 heads,
+                                                  recurrent decode steps for 8 sequences)
        python bench.py --copy-probe             (plain copy kernel of known size, for counter scaling)
 """
 from __future__ import annotations
@@ -126,7 +128,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="default", choices=["default", "decode_1m", "ragged", "swa", "producer"])
+    ap.add_argument("--workload", default="default", choices=["default", "decode_1m", "ragged", "swa", "producer", "gret"])
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--skip", default="", help="comma list of modes to leave out: prefill,decode (profiling only)")
     args = ap.parse_args()
@@ -154,6 +156,8 @@ def main():
         return bench_swa(args, torch, dk, synth, dev)
     if args.workload == "producer":
         return bench_producer(args, torch, dk, synth, dev)
+    if args.workload == "gret":
+        return bench_gret(args, torch, dk, synth, dev)
 
     skip = set(x for x in args.skip.split(",") if x)
     wp = synth.WORKLOADS["prefill_32k"]
@@ -457,6 +461,86 @@ def bench_producer(args, torch, dk, synth, dev):
         "decode_rows": {"us_per_call": row_us, "rows": B, "weight_bytes": wbytes,
                         "weight_read_GBps": wbytes / (row_us / 1e6) / 1e9,
                         "note": "the 12.6 MB of packed weights stay in the Infinity Cache between calls"}}),
+        flush=True)
+
+
+GRET_CHUNK = 256
+
+
+def gret_chunk_flops(n, d):
+    """MFMA work of the chunkwise form per head: per chunk of c rows, the causal
+    Q K^T and P V products (2 d c(c+1)/2 each), the carried state Q S and the
+    chunk's contribution K^T V (2 c d^2 each)."""
+    total, r = 0.0, 0
+    while r < n:
+        c = min(GRET_CHUNK, n - r)
+        total += 2.0 * d * c * (c + 1) + 4.0 * c * d * d
+        r += c
+    return total
+
+
+def bench_gret(args, torch, dk, synth, dev):
+    """Gated retention at the prefill workload's length: one chunkwise prefill of
+    32768 rows x 16 heads (d = 128) per layer call, 16 calls; then recurrent
+    decode steps for 8 sequences x 16 heads."""
+    N, H, d, B = 32768, 16, 128, 8
+    g = torch.Generator(device=dev).manual_seed(13)
+    std = d ** -0.25
+    q = (torch.randn(N, H, d, device=dev, generator=g) * std).to(torch.bfloat16)
+    k = (torch.randn(N, H, d, device=dev, generator=g) * std).to(torch.bfloat16)
+    v = torch.randn(N, H, d, device=dev, generator=g).to(torch.bfloat16)
+    gam = 0.9 + 0.1 * torch.rand(N, H, device=dev, generator=g)
+    cu = torch.tensor([0, N], dtype=torch.int32, device=dev)
+    ws = torch.empty(dk.gret_workspace_size(1, H, d, N), dtype=torch.uint8, device=dev)
+    st = torch.empty(1, H, d, d, device=dev)
+    out = torch.empty_like(v)
+    qd = (torch.randn(B, H, d, device=dev, generator=g) * std).to(torch.bfloat16)
+    kd = (torch.randn(B, H, d, device=dev, generator=g) * std).to(torch.bfloat16)
+    vd = torch.randn(B, H, d, device=dev, generator=g).to(torch.bfloat16)
+    gd = 0.9 + 0.1 * torch.rand(B, H, device=dev, generator=g)
+    state = torch.zeros(B, H, d, d, device=dev)
+    outd = torch.empty_like(vd)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    L = 16
+    for _ in range(args.warmup):
+        dk.gret_prefill(q, k, v, gam, cu, N, ws, state_out=st, out=out)
+        dk.gret_decode(qd, kd, vd, gd, state, out=outd)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(args.steps * L):
+        dk.gret_prefill(q, k, v, gam, cu, N, ws, state_out=st, out=out)
+    ev[1].record()
+    ev[2].record()
+    for _ in range(args.steps * L):
+        dk.gret_decode(qd, kd, vd, gd, state, out=outd)
+    ev[3].record()
+    torch.cuda.synchronize()
+    call_s = ev[0].elapsed_time(ev[1]) / 1e3 / (args.steps * L)
+    flops = H * gret_chunk_flops(N, d)
+    tfl = flops / call_s / 1e12
+    # 128 flop per byte of input and output, below the ridge point (2.5 PFLOP/s / 8 TB/s):
+    # the bound is HBM; algorithmic bytes = Q, K, V and the gates read once, O and the
+    # final state written once
+    alg_bytes = 4 * N * H * d * 2 + N * H * 4 + H * d * d * 4
+    gbs = alg_bytes / call_s / 1e9
+    dec_us = ev[2].elapsed_time(ev[3]) * 1e3 / (args.steps * L)
+    state_bytes = B * H * d * d * 4 * 2
+    print(json.dumps({
+        "metric": "gRet chunkwise prefill GB/s (% HBM peak) @32K x 16 heads; recurrent decode us per step",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": call_s * 1e3 * L, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded q, k ~ N(0, d^-1/2), v ~ N(0,1), gates U[0.9, 1), bf16)",
+        "config": {"workload": "gated retention: prefill N=32768 H=16 d=128 (chunk 256), 16 layer calls; "
+                               "decode B=8 H=16 d=128, 16 layer steps", "global_batch": 1, "seq_len": N,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gret_state_kernel + gret_scan_kernel + gret_out_kernel (one call, timed together)",
+                     "avg_launch_ms": call_s * 1e3, "algorithmic_per_launch": alg_bytes,
+                     "mfma_tflops": tfl, "mfma_flops_per_launch": flops},
+        "decode": {"us_per_step": dec_us, "state_bytes_per_step": state_bytes,
+                   "GBps": state_bytes / (dec_us / 1e6) / 1e9,
+                   "note": "8 MiB of fp32 state read and written per step; it stays in the Infinity Cache"}}),
         flush=True)
 
 
