@@ -83,17 +83,19 @@ __device__ __forceinline__ bf16x8 read_tr(const YOCO_LDS char* tile, int base_ro
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Copy rows [0, n_rows) of a [rows, H, D] bf16 tensor (row stride H*D) starting
-// at global row `row0` into a tile of `rows` rows (rows >= n_rows repeat row
-// n_rows - 1), in the tr_slot (TR) or row_slot layout, by the load unit.
+// Copy tile rows [first, first + rows) of a [rows, H, D] bf16 tensor (row
+// stride H*D) whose row 0 is global row `row0` (rows >= n_rows, n_rows >= 1,
+// repeat row n_rows - 1) into LDS at `lds` (tile row `first` at offset 0), in
+// the tr_slot (TR) or row_slot layout, by the load unit. rows * D / 8 must be a
+// multiple of the thread count.
 template <int D, bool TR>
-__device__ __forceinline__ void load_tile(const __bf16* src, int64_t row0, int n_rows, int rows, int H, int h,
-                                          uint32_t lds) {
+__device__ __forceinline__ void load_tile(const __bf16* src, int64_t row0, int n_rows, int first, int rows, int H,
+                                          int h, uint32_t lds) {
   constexpr int cpr = D / 8;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int i = 0; i < rows * cpr / kGThreads; ++i) {
     const int p = i * kGThreads + (int)threadIdx.x;
-    const int r = p / cpr, slot = p % cpr;
+    const int r = first + p / cpr, slot = p % cpr;
     const int c = TR ? (slot ^ v_swizzle<D>(r)) : (slot ^ (r & (cpr - 1)));
     const int rr = r < n_rows ? r : n_rows - 1;
     dma16(src + ((row0 + rr) * H + h) * D + 8 * c, lds + (i * kGThreads + wave * 64) * 16);
@@ -128,25 +130,32 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_state_kernel(GretParams p) 
   const ChunkInfo ci = chunk_info(p, b, c);
   if (ci.n == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t kl = (uint32_t)(uintptr_t)smem, vl = kl + kGC * D * 2;
-  load_tile<D, true>(static_cast<const __bf16*>(p.k), ci.row0, ci.n, kGC, p.heads, h, kl);
-  load_tile<D, true>(static_cast<const __bf16*>(p.v), ci.row0, ci.n, kGC, p.heads, h, vl);
-
   // decay from row m to the chunk's end: 2^(A_last - A_m), A = prefix of log2 gates
   const float a = log2_gate(p.gamma, ci.row0 + tid, h, p.heads, tid < ci.n);
   const float A = chunk_prefix(a, wsum);
   const float a_last = wsum[0] + wsum[1] + wsum[2] + wsum[3];   // gates past the end count 1
   if (tid < kGC) wgt[tid] = tid < ci.n ? exp2f(a_last - A) : 0.f;
   if (tid == 0) p.chunk_decay[((int64_t)b * p.heads + h) * p.max_chunks + c] = exp2f(a_last);
-  wait_vm_lgkm0<0>();
-  __syncthreads();
+
+  // K and V of the chunk in two halves of 128 rows: the second half's copies
+  // overlap the first half's MFMAs. Half f of a matrix sits at its tile rows 128 f.
+  const uint32_t kl = (uint32_t)(uintptr_t)smem, vl = kl + kGC * D * 2;
+  constexpr int kHalf = kGC / 2;
+  constexpr int LH = 2 * (kHalf * D / 8 / kGThreads);          // copies per thread and half
+  const __bf16* kg = static_cast<const __bf16*>(p.k);
+  const __bf16* vg = static_cast<const __bf16*>(p.v);
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    load_tile<D, true>(kg, ci.row0, ci.n, kHalf * f, kHalf, p.heads, h, kl + kHalf * f * D * 2);
+    load_tile<D, true>(vg, ci.row0, ci.n, kHalf * f, kHalf, p.heads, h, vl + kHalf * f * D * 2);
+  }
 
   // output blocks (dv block i, dk block j) of 32 x 32; D = 128: 16 blocks, two per
   // wave (same i); D = 64: 4 blocks, waves 0..3
   constexpr int NB = D / 32;
   constexpr int PER = (NB * NB) / 8 > 0 ? (NB * NB) / 8 : 1;
-  if (wave * PER >= NB * NB) return;
-  const int blk0 = wave * PER;
+  const bool idle = wave * PER >= NB * NB;     // D = 64: waves 4..7 only join the barriers
+  const int blk0 = idle ? 0 : wave * PER;
   const int bi = blk0 / NB;
   f32x16 acc[PER];
 #pragma unroll
@@ -155,7 +164,13 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_state_kernel(GretParams p) 
   const YOCO_LDS char* kt = smem;
   const YOCO_LDS char* vt = smem + kGC * D * 2;
   for (int s = 0; s < kGC / 16; ++s) {
+    if (s == 0 || s == kGC / 32) {
+      // the half that begins here is in (the first half: with the second's copies in flight)
+      if (s == 0) wait_vm_lgkm0<LH>(); else wait_vm_lgkm0<0>();
+      barrier_only();
+    }
     // k-step s: keys base + {0..3, 8..11} + 4h with base = 16 s (two 4-key runs per lane)
+    if (idle) continue;
     const int base = 16 * s;
     const bf16x8 av = read_tr<D>(vt, base, bi, lane);                 // V^T rows dv, 8 keys
     const f32x4 w0 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (base + 4 * hf));
@@ -175,6 +190,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_state_kernel(GretParams p) 
       acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, kw, acc[e], 0, 0, 0);
     }
   }
+  if (idle) return;
   // lane holds dk = 32 bj + lane % 32, dv rows 32 bi + 8(r/4) + 4hf + r%4
   float* u = p.chunk_state + (((int64_t)b * p.heads + h) * p.max_chunks + c) * (D * D);
 #pragma unroll
@@ -208,13 +224,28 @@ __global__ __launch_bounds__(256) void gret_scan_kernel(GretParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = p.state_in[(bh * D + dk + i) * D + dv];
   }
-  for (int c = 0; c < nc; ++c) {
-    const int64_t off = (bh * p.max_chunks + c) * (D * D) + e0;
-    *reinterpret_cast<u32x2*>(p.chunk_in + off) = u32x2{pack2(s[0], s[1]), pack2(s[2], s[3])};
-    const float g = p.chunk_decay[bh * p.max_chunks + c];
-    const f32x4 u = *reinterpret_cast<const f32x4*>(p.chunk_state + off);
+  // the loads do not depend on the state: fetch a group of chunks ahead, then
+  // run the (serial) recurrence over the group
+  constexpr int kAhead = 8;
+  const float* __restrict__ us = p.chunk_state + bh * p.max_chunks * (D * D) + e0;
+  const float* __restrict__ gs = p.chunk_decay + bh * p.max_chunks;
+  uint16_t* __restrict__ sin = p.chunk_in + bh * p.max_chunks * (D * D) + e0;
+  for (int c0 = 0; c0 < nc; c0 += kAhead) {
+    f32x4 u[kAhead];
+    float g[kAhead];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = fmaf(g, s[i], u[i]);
+    for (int i = 0; i < kAhead; ++i) {
+      const int c = c0 + i < nc ? c0 + i : nc - 1;
+      u[i] = *reinterpret_cast<const f32x4*>(us + (int64_t)c * (D * D));
+      g[i] = gs[c];
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      if (c0 + i >= nc) break;
+      *reinterpret_cast<u32x2*>(sin + (int64_t)(c0 + i) * (D * D)) = u32x2{pack2(s[0], s[1]), pack2(s[2], s[3])};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] = fmaf(g[i], s[j], u[i][j]);
+    }
   }
   if (p.state_out != nullptr) {
 #pragma unroll
@@ -263,8 +294,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   auto issue = [&](int t) {
     const uint32_t st = base_lds + (t & 1) * kStage;
     const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
-    load_tile<D, false>(kg, ci.row0 + t * kGT, n_t, kGT, H, h, st);
-    load_tile<D, true>(vg, ci.row0 + t * kGT, n_t, kGT, H, h, st + kTile);
+    load_tile<D, false>(kg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st);
+    load_tile<D, true>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile);
   };
   issue(0);
   if (n_tiles > 1) issue(1);
@@ -314,7 +345,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
     if (t > 0) {
       // tile t is in when at most the copies of tile t + 1 (if requested) are in flight
       if (t + 1 < n_tiles) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();
-      __syncthreads();
+      barrier_only();
     }
     const int key0 = t * kGT;
     if (wave_active && key0 <= j_row) {
@@ -365,7 +396,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       }
     }
     if (t + 2 < n_tiles) {
-      __syncthreads();   // every wave is done with stage t & 1
+      barrier_only();   // every wave is done with stage t & 1 (its reads fed MFMAs already)
       issue(t + 2);
     }
   }
