@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+CALL_REPS = 32               # back-to-back calls for the per-call median / min / p90
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "decode HBM GB/s (% peak) @128K-1M; prefill TFLOP/s (% MFMA peak) @32K"
 
@@ -104,7 +105,14 @@ def cpu_baseline(synth, oracle, w, budget_s=12.0):
         done_rows.append((lo, hi))
         hi = lo
     dt = time.perf_counter() - t0
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except Exception:  # noqa: BLE001
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu": model,
             "sample": f"fp64 NumPy oracle, prefill layer 0 of the 32K workload, query rows "
                       f"{done_rows[-1][0]}..{n - 1} (all {w.q_heads} heads), {dt:.1f} s; "
                       f"rate = causal flops of those rows / time"}
@@ -223,6 +231,21 @@ def main():
     wall = time.perf_counter() - t0
     assert int(flag.item()) == 0, "append overflowed"
 
+    def call_stats(call, reps=CALL_REPS):
+        """Per-call spread after the timed region: one event pair around each of
+        `reps` back-to-back calls (the timed region itself records none)."""
+        import numpy as np
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for layer, (a, b) in enumerate(evs):
+            a.record()
+            call(layer)
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        return {"calls": reps, "median_ms": float(np.median(t)), "min_ms": float(t.min()),
+                "p90_ms": float(np.percentile(t, 90))}
+
     flops_layer = prefill_flops(wp.seq_lens, wp.q_heads, wp.head_dim)
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
@@ -239,6 +262,8 @@ def main():
                            **traffic_fields("prefill_bf16_kernel<128>", layer_s),
                            "kernel": "prefill_bf16_kernel<128>", "avg_launch_ms": layer_s * 1e3,
                            "algorithmic_per_launch": flops_layer}
+        res["prefill_calls"] = call_stats(
+            lambda i: dk.xattn_prefill(pcache, qs[i % wp.layers], cu, n, pc.scale, out=out_p, lse=lse_p))
     if "decode" not in skip:
         calls = args.steps * wd.layers
         call_s = dec_ms / 1e3 / calls
@@ -249,14 +274,37 @@ def main():
                                       "frac": gbs / HBM_PEAK_GBS, **traffic_fields("decode_split_bf16_kernel<128, 2>",
                                                                                     call_s),
                                       "kernel": "decode_split_bf16_kernel<128, 2> + decode_merge_kernel "
-                                                "(one call: both launches, timed together)"}}
+                                                "(one call: both launches, timed together)"},
+                         "calls": call_stats(
+                             lambda i: dk.xattn_decode(dcache, qd[i % wd.layers], max(lens_now), dc.scale, ws,
+                                                       out=out_d, lse=lse_d))}
         if "prefill" in skip:
             res.update({"value": gbs, "unit": "GB/s"})
+    res["device"] = device_info(torch, dev)
     if not args.no_cpu_baseline:
         import oracle
         log("timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(synth, oracle, wp)
     print(json.dumps(res), flush=True)
+
+
+def device_info(torch, dev):
+    """CU count and a read probe: torch's sum over 2 GiB of bf16 (a plain streaming
+    read, for context beside the 8 TB/s published figure)."""
+    props = torch.cuda.get_device_properties(dev)
+    x = torch.ones(1 << 30, dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        x.sum()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * x.numel() * 2 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del x
+    return {"name": props.name, "compute_units": props.multi_processor_count,
+            "read_probe_GBps": gbs, "read_probe": "torch sum over 2 GiB of bf16, 5 passes"}
 
 
 def bench_decode_1m(args, torch, dk, synth, dev):
