@@ -21,16 +21,11 @@
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
+#include "tile_common.h"
 
 namespace yoco {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Tuning knobs (measured on MI355X at 8 x 131072 and 1 x 1048576 rows): two
 // 16-key blocks per wave and iteration, no register double buffer (the freed
@@ -67,13 +62,6 @@ __device__ __forceinline__ uint2 stream_load8(const void* p) {
 }
 constexpr int kVtStride = 20;  // 16 keys + 4 pad (bf16 elements) per transposed V^ row
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
-}
 
 __device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
@@ -198,7 +186,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
         mx = fmaxf(mx, t);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));   // (lane swaps without LDS measured slower here)
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -214,8 +202,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
         e[r] = exp2f(s[u][r] - m_use);
         psum += e[r];
       }
-      const uint32_t w0 = pack_bf16x2(e[0], e[1]);
-      const uint32_t w1 = pack_bf16x2(e[2], e[3]);
+      const uint32_t w0 = pack2(e[0], e[1]);
+      const uint32_t w1 = pack2(e[2], e[3]);
       pf[u] = s16x4{(short)lo16(w0), (short)hi16(w0), (short)lo16(w1), (short)hi16(w1)};
     }
     l = l * alpha + psum;

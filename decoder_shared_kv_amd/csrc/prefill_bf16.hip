@@ -48,6 +48,7 @@ constexpr int kStages = YOCO_PREFILL_STAGES;
 #define YOCO_PREFILL_SCHED 1
 #endif
 
+
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kRescaleSlack = 8.0f;   // base-2 growth of the running max tolerated before a rescale
 
@@ -218,7 +219,9 @@ __device__ __forceinline__ float softmax_max(f32x16 (&s)[2], f32x16 (&acc)[D / 3
       mx = fmaxf(mx, s[kb][r]);
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // lanes l and l ^ 32 hold the two key halves of one query row; the exchange
+  // stays out of LDS, so it waits on none of the operand reads in flight
+  mx = max_xor32(mx);
   const float mx2 = mx * c;  // c > 0: the max commutes with the scale
   // only the lanes whose own max grew move their reference, so every row's
   // arithmetic stays independent of the other rows of the wave
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
 
     // Epilogue: normalise, stage the wave's 32 x D output tile in LDS, then
     // store whole rows with 16-byte writes.
-    const float l_tot = l + __shfl_xor(l, 32);
+    const float l_tot = sum_xor32(l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)smem + wave * (kPrefillRowsPerWave * kOStride);
 #pragma unroll

@@ -21,6 +21,24 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// Cross-lane exchanges without LDS (gfx950 v_permlane{16,32}_swap). Called
+// with the same register twice, the swap leaves lanes l and l ^ 32 (resp.
+// l ^ 16) holding each other's value in one of the two results, so combining
+// the pair gives the reduction over that lane pair in every lane. The whole
+// wave must be active.
+__device__ __forceinline__ f32x2 lane_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 lane_pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor32(float x) { const f32x2 r = lane_pair32(x); return fmaxf(r[0], r[1]); }
+__device__ __forceinline__ float max_xor16(float x) { const f32x2 r = lane_pair16(x); return fmaxf(r[0], r[1]); }
+__device__ __forceinline__ float sum_xor32(float x) { const f32x2 r = lane_pair32(x); return r[0] + r[1]; }
+__device__ __forceinline__ float sum_xor16(float x) { const f32x2 r = lane_pair16(x); return r[0] + r[1]; }
+
 // XOR applied to the 16-byte chunk index of row r of a row-major bf16 tile that
 // is read with ds_read_b64_tr_b16 (4 rows x 16 columns per 16-lane group). A
 // transposing read of one wave covers 8 rows x 64 bytes; with these values its
