@@ -14,14 +14,19 @@ namespace {
 using yoco::AttnParams;
 
 constexpr float kLog2e = 1.4426950408889634f;
-#ifndef YOCO_DEC_U
-#define YOCO_DEC_U 2
-#endif
+// bf16 decode: workgroups of all columns together. Two fit one CU, so 512 are
+// one round on 256 CUs. Measured on MI355X (8 x 131072, 1 x 1048576, 4 x 131072
+// and 16 x 17292 rows): one round is fastest with one or two columns (KV
+// heads x head chunks), two rounds with four or more.
 #ifndef YOCO_DECODE_TARGET_WGS
-#define YOCO_DECODE_TARGET_WGS 1024
+#define YOCO_DECODE_TARGET_WGS 0
 #endif
-constexpr int kDecodeKeysPerIter = 4 * 16 * YOCO_DEC_U;  // rows one decode workgroup consumes per iteration
-constexpr int kDecodeTargetWgs = YOCO_DECODE_TARGET_WGS;  // split-K target
+int64_t decode_target_wgs(int64_t columns) {
+  if (YOCO_DECODE_TARGET_WGS > 0) return YOCO_DECODE_TARGET_WGS;
+  return columns <= 2 ? 512 : 1024;
+}
+// f32 decode: threads of all columns together
+constexpr int kDecodeTargetThreadsF32 = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -53,45 +58,54 @@ int head_chunks(const yoco_dims* d) {
   return (g + 15) / 16;
 }
 
-// Split plan: rows per split are sized so that the (sequence, KV head, head
-// chunk, split) workgroups holding rows number about kDecodeTargetWgs, counting
-// the rows of every sequence (total_kv_len, at least max_kv_len); a multiple of
-// one workgroup iteration, at least one. The splits cover max_kv_len.
-int64_t rows_per_split(const yoco_dims* d, int32_t max_kv_len, int64_t total_kv_len) {
+// Columns of the balanced decode split: workgroups of one (KV head, head chunk)
+// for bf16, threads of one query head for f32.
+int64_t decode_columns(const yoco_dims* d) {
+  return d->dtype == YOCO_DTYPE_BF16 ? (int64_t)d->num_kv_heads * head_chunks(d) : (int64_t)d->num_q_heads;
+}
+
+// Most shares per column any plan uses.
+int32_t decode_share_cap(const yoco_dims* d) {
+  const int64_t cols = decode_columns(d);
+  const int64_t target = d->dtype == YOCO_DTYPE_BF16 ? decode_target_wgs(cols) : kDecodeTargetThreadsF32;
+  const int64_t c = target / cols;
+  return (int32_t)(c < 1 ? 1 : c);
+}
+
+// Blocks of 128 rows the hints describe: total_kv_len (0: B * max_kv_len),
+// kept within max_kv_len .. B * max_kv_len.
+int64_t decode_hint_blocks(const yoco_dims* d, int32_t max_kv_len, int64_t total_kv_len) {
   const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
-  int64_t total = total_kv_len > 0 ? total_kv_len : (int64_t)d->batch * n;
+  const int64_t all = (int64_t)d->batch * n;
+  int64_t total = total_kv_len > 0 && total_kv_len < all ? total_kv_len : all;
   if (total < n) total = n;
-  const int64_t per_row = (int64_t)d->num_kv_heads * head_chunks(d);
-  int64_t r = (total * per_row + kDecodeTargetWgs - 1) / kDecodeTargetWgs;
-  r = (r + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter * kDecodeKeysPerIter;
-  return r < kDecodeKeysPerIter ? kDecodeKeysPerIter : r;
+  return (total + yoco::kDecodeBlockRows - 1) / yoco::kDecodeBlockRows;
 }
 
-void plan_decode(const yoco_dims* d, int32_t max_kv_len, int64_t total_kv_len, int32_t* splits, int32_t* rows) {
-  const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
-  const int64_t r = rows_per_split(d, max_kv_len, total_kv_len);
-  *rows = (int32_t)r;
-  *splits = (int32_t)((n + r - 1) / r);
+// Split plan: every column cuts the 128-row blocks of all sequences into
+// `shares` equal shares; about decode_target_wgs workgroups in all, fewer when
+// the hinted rows hold fewer blocks, so that no share is planned empty. The
+// hints size the plan only: the kernels count the blocks on the device. The
+// plan grows with max_kv_len, so a workspace sized for max_kv_len fits every
+// call with a smaller one and any total_kv_len.
+int32_t decode_shares(const yoco_dims* d, int32_t max_kv_len, int64_t total_kv_len) {
+  const int64_t blocks = decode_hint_blocks(d, max_kv_len, total_kv_len);
+  const int64_t cap = decode_share_cap(d);
+  return (int32_t)(blocks < cap ? blocks : cap);
 }
 
-// An upper bound of the splits of every plan with max_kv_len <= n and any
-// total_kv_len (monotone in n): rows >= n * per_row / target and rows >= one
-// iteration, so splits <= min(ceil(target / per_row), ceil(n / iteration)).
-int32_t decode_split_bound(const yoco_dims* d, int32_t max_kv_len) {
-  const int64_t n = max_kv_len > 0 ? max_kv_len : 1;
-  const int64_t by_rows = (n + kDecodeKeysPerIter - 1) / kDecodeKeysPerIter;
-  const int64_t per_row = (int64_t)d->num_kv_heads * head_chunks(d);
-  const int64_t by_target = (kDecodeTargetWgs + per_row - 1) / per_row;
-  return (int32_t)(by_rows < by_target ? by_rows : by_target);
-}
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_ml_offset(const yoco_dims* d, int32_t splits) {
-  const size_t o = (size_t)d->batch * d->num_q_heads * splits * d->head_dim * sizeof(float);
-  return (o + 255) & ~(size_t)255;
+// Workspace: part_o [Hq, shares + B, D] fp32, part_ml [Hq, shares + B, 2] fp32,
+// meta [B, 2] int32.
+size_t decode_ml_offset(const yoco_dims* d, int32_t shares) {
+  return align256((size_t)d->num_q_heads * (shares + d->batch) * d->head_dim * sizeof(float));
 }
-
-size_t decode_workspace(const yoco_dims* d, int32_t splits) {
-  return decode_ml_offset(d, splits) + (size_t)d->batch * d->num_q_heads * splits * 2 * sizeof(float);
+size_t decode_meta_offset(const yoco_dims* d, int32_t shares) {
+  return decode_ml_offset(d, shares) + align256((size_t)d->num_q_heads * (shares + d->batch) * 2 * sizeof(float));
+}
+size_t decode_workspace(const yoco_dims* d, int32_t shares) {
+  return decode_meta_offset(d, shares) + (size_t)d->batch * 2 * sizeof(int32_t);
 }
 
 AttnParams base_params(const yoco_dims* d, const yoco_kv_cache* c) {
@@ -189,20 +203,20 @@ yoco_status decode_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const
     const int64_t cap = (int64_t)dims->batch * window;
     if (total_kv_len > cap) total_kv_len = cap;
   }
-  int32_t splits, rows;
-  plan_decode(dims, max_kv_len, total_kv_len, &splits, &rows);
-  const size_t need = decode_workspace(dims, splits);
+  const int32_t shares = decode_shares(dims, max_kv_len, total_kv_len);
+  const size_t need = decode_workspace(dims, shares);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return YOCO_ERR_WORKSPACE;
   AttnParams p = base_params(dims, cache);
   p.q = q;
   p.out = out;
   p.lse = lse;
   p.window = window;
-  p.splits = splits;
-  p.split_rows = rows;
+  p.splits = shares;
+  p.slots = shares + dims->batch;
   p.head_chunks = head_chunks(dims);
   p.part_o = static_cast<float*>(workspace);
-  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ml_offset(dims, splits));
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ml_offset(dims, shares));
+  p.decode_meta = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + decode_meta_offset(dims, shares));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = dims->dtype == YOCO_DTYPE_BF16 ? yoco::launch_decode_split_bf16(p, dims->head_dim, s)
                                                   : yoco::launch_decode_split_f32(p, dims->head_dim, s);
@@ -243,7 +257,10 @@ yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len, 
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
   if (splits == nullptr || rows_per_split == nullptr || max_kv_len < 0 || total_kv_len < 0) return YOCO_ERR_INVALID_ARG;
-  plan_decode(dims, max_kv_len, total_kv_len, splits, rows_per_split);
+  const int32_t shares = decode_shares(dims, max_kv_len, total_kv_len);
+  const int64_t blocks = decode_hint_blocks(dims, max_kv_len, total_kv_len);
+  *splits = shares;
+  *rows_per_split = (int32_t)((blocks + shares - 1) / shares * yoco::kDecodeBlockRows);
   return YOCO_OK;
 }
 
@@ -251,7 +268,7 @@ yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len,
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
   if (bytes == nullptr || max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
-  *bytes = decode_workspace(dims, decode_split_bound(dims, max_kv_len));
+  *bytes = decode_workspace(dims, decode_shares(dims, max_kv_len, 0));
   return YOCO_OK;
 }
 

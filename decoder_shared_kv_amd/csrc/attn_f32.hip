@@ -3,7 +3,7 @@
 // Same operation as the bf16 kernels (page "YOCO", section "Cross-Decoder",
 // Attn_l equation, causal mask j <= i), in true fp32 arithmetic throughout so
 // that fp32 inputs keep fp32 accuracy. One thread owns one query row (prefill)
-// or one (sequence, head, split) triple (decode) and keeps a running max, a
+// or one (share of the rows, head) pair (decode) and keeps a running max, a
 // running sum of weights and an unnormalised output vector (online softmax in
 // the base-2 domain: exp(s*scale) = exp2(s*scale*log2 e)).
 #include "internal.h"
@@ -97,41 +97,60 @@ __global__ __launch_bounds__(kPrefillF32Rows) void prefill_f32_kernel(AttnParams
   }
 }
 
-// One thread per (sequence, query head, split): partial (m, l, unnormalised O).
+// One thread per (share, query head): the share's rows of every sequence it
+// spans, one partial (m, l, unnormalised O) per piece, in slot share + sequence
+// (the balanced split of the bf16 decode kernel, walked sequentially).
 template <int D>
 __global__ __launch_bounds__(64) void decode_split_f32_kernel(AttnParams p) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.batch * p.hq * p.splits;
-  if (t >= total) return;
-  const int s = (int)(t % p.splits);
-  const int bh = (int)(t / p.splits);
-  const int b = bh / p.hq;
-  const int h = bh % p.hq;
+  if (t >= (int64_t)p.splits * p.hq) return;
+  const int share = (int)(t % p.splits);
+  const int h = (int)(t / p.splits);
   const int kh = h / p.group;
-  int64_t start;
-  int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
-  n_kv = window_rows(n_kv, p.window, &start);
+  int64_t total = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    int64_t st;
+    total += decode_blocks(decode_rows(p, b, &st));
+  }
+  const int parts = total < p.splits ? (int)total : p.splits;
+  if (share >= parts) return;
+  const int64_t first = share_begin(share, total, parts);
+  const int64_t last = share_begin(share + 1, total, parts);
   const int64_t row_stride = (int64_t)p.hkv * D;
-  const float* kbase = static_cast<const float*>(p.k) + start * row_stride + (int64_t)kh * D;
-  const float* vbase = static_cast<const float*>(p.v) + start * row_stride + (int64_t)kh * D;
-  int j0 = s * p.split_rows;
-  int j1 = (s == p.splits - 1) ? n_kv : j0 + p.split_rows;  // the last split takes any remainder
-  if (j1 > n_kv) j1 = n_kv;
-  const float* qsrc = static_cast<const float*>(p.q) + ((int64_t)b * p.hq + h) * D;
-  float qr[D];
+  int64_t pre = 0;
+  for (int b = 0; b < p.batch && pre < last; ++b) {
+    int64_t start;
+    const int32_t n_kv = decode_rows(p, b, &start);
+    const int u = decode_blocks(n_kv);
+    if (u > 0 && pre + u > first) {
+      const int64_t lo = (first > pre ? first : pre) - pre;
+      const int64_t hi = (last < pre + u ? last : pre + u) - pre;
+      if (lo == 0 && h == 0) {
+        p.decode_meta[2 * b + 0] = share + b;
+        p.decode_meta[2 * b + 1] = (int32_t)(share_of_block(pre + u - 1, total, parts) - share + 1);
+      }
+      const int j0 = (int)(lo * kDecodeBlockRows);
+      const int j1 = hi * kDecodeBlockRows < n_kv ? (int)(hi * kDecodeBlockRows) : n_kv;
+      const float* kbase = static_cast<const float*>(p.k) + start * row_stride + (int64_t)kh * D;
+      const float* vbase = static_cast<const float*>(p.v) + start * row_stride + (int64_t)kh * D;
+      const float* qsrc = static_cast<const float*>(p.q) + ((int64_t)b * p.hq + h) * D;
+      float qr[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) qr[i] = qsrc[i];
-  float acc[D];
+      for (int i = 0; i < D; ++i) qr[i] = qsrc[i];
+      float acc[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) acc[i] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  if (j0 < j1) accumulate_rows<D>(qr, kbase, vbase, row_stride, j0, j1, p.scale_log2, m, l, acc);
-  const int64_t slot = ((int64_t)b * p.hq + h) * p.splits + s;
-  float* po = p.part_o + slot * D;
+      for (int i = 0; i < D; ++i) acc[i] = 0.f;
+      float m = -INFINITY, l = 0.f;
+      accumulate_rows<D>(qr, kbase, vbase, row_stride, j0, j1, p.scale_log2, m, l, acc);
+      const int64_t ps = (int64_t)h * p.slots + share + b;
+      float* po = p.part_o + ps * D;
 #pragma unroll
-  for (int i = 0; i < D; ++i) po[i] = acc[i];
-  p.part_ml[2 * slot + 0] = m;
-  p.part_ml[2 * slot + 1] = l;
+      for (int i = 0; i < D; ++i) po[i] = acc[i];
+      p.part_ml[2 * ps + 0] = m;
+      p.part_ml[2 * ps + 1] = l;
+    }
+    pre += u;
+  }
 }
 
 }  // namespace
@@ -145,7 +164,7 @@ hipError_t launch_prefill_f32(const AttnParams& p, int head_dim, int grid, hipSt
 }
 
 hipError_t launch_decode_split_f32(const AttnParams& p, int head_dim, hipStream_t stream) {
-  const int64_t total = (int64_t)p.batch * p.hq * p.splits;
+  const int64_t total = (int64_t)p.splits * p.hq;
   const dim3 grid((unsigned)((total + 63) / 64));
   if (head_dim == 64)
     hipLaunchKernelGGL(decode_split_f32_kernel<64>, grid, dim3(64), 0, stream, p);

@@ -4,9 +4,11 @@
 // step (page "YOCO", section "KV Cache 与计算量分析": repeated reads of the
 // shared KV make its bandwidth the critical path), so this kernel is bound by
 // HBM reads of K^ and V^. Design points:
-//  * one workgroup = (row split, KV head, sequence); it reads each cache row of
-//    its split exactly once, for ALL query heads of the KV group (<= 16 per
-//    workgroup), so GQA costs no extra traffic;
+//  * one workgroup = (share of the rows, KV head): the 128-row blocks of all
+//    sequences are cut into equal shares, so the workgroups are balanced for
+//    any mix of lengths; it reads each cache row of its share exactly once, for
+//    ALL query heads of the KV group (<= 16 per workgroup), so GQA costs no
+//    extra traffic;
 //  * K^ rows go straight from HBM into MFMA A operands (16 B per lane, no LDS):
 //    S^T[key][head] = K^ . Q^T with v_mfma_f32_16x16x32_bf16, query heads padded
 //    to 16 columns;
@@ -100,30 +102,25 @@ __device__ __forceinline__ void dec_load(DecRegs<D, U>& r, const __bf16* kbase, 
   }
 }
 
+// LDS: per-wave transposed V^ tiles; reused for the cross-wave combine at the end
 template <int D, int U>
-__global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
-  const int split = blockIdx.x;
-  const int kh = blockIdx.y / p.head_chunks;
-  const int hc = blockIdx.y % p.head_chunks;
-  const int b = blockIdx.z;
+struct DecLds {
+  static constexpr int kVtBytes = kDecWaves * U * D * kVtStride * 2;
+  static constexpr int kCombBytes = kDecWaves * 16 * (D + 2) * 4;
+  static constexpr int kBytes = kVtBytes > kCombBytes ? kVtBytes : kCombBytes;
+};
+
+// Rows j0 .. j1-1 of sequence b (cache rows from `start`), all query heads of
+// KV head kh's chunk hc: leaves the partial (m, l, O) of every head in its
+// slot (h * p.slots + slot).
+template <int D, int U>
+__device__ __forceinline__ void decode_piece(const AttnParams& p, char* lds, int b, int64_t start, int j0, int j1,
+                                             int kh, int hc, int slot) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-
-  // LDS: per-wave transposed V^ tiles; reused for the cross-wave combine at the end
-  constexpr int kVtBytes = kDecWaves * U * D * kVtStride * 2;
-  constexpr int kCombBytes = kDecWaves * 16 * (D + 2) * 4;
-  constexpr int kLdsBytes = kVtBytes > kCombBytes ? kVtBytes : kCombBytes;
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   __bf16* vt = reinterpret_cast<__bf16*>(lds) + wave * (U * D * kVtStride);
-
-  int64_t start;
-  int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
-  n_kv = window_rows(n_kv, p.window, &start);   // sliding window: the last `window` rows
-  const int j0 = split * p.split_rows;
-  int j1 = (split == p.splits - 1) ? n_kv : j0 + p.split_rows;
-  if (j1 > n_kv) j1 = n_kv;
 
   const int h0 = kh * p.group + hc * 16;
   const int nh = p.group - hc * 16 < 16 ? p.group - hc * 16 : 16;
@@ -151,6 +148,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
   float l = 0.f;        // this lane's share of the running sum of weights
 
   constexpr int kStep = kDecWaves * U * 16;
+  static_assert(kDecodeBlockRows % kStep == 0, "pieces start at an iteration boundary");
   int base = j0 + wave * U * 16;
   DecRegs<D, U> cur;
 #if YOCO_DEC_PREFETCH
@@ -284,8 +282,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
       L = fmaf(wml[(w * 16 + hh) * 2 + 1], sc[w], L);
     }
     if (hh < nh) {
-      const int64_t slot = ((int64_t)b * p.hq + h0 + hh) * p.splits + split;
-      float* po = p.part_o + slot * D + d0;
+      const int64_t ps = (int64_t)(h0 + hh) * p.slots + slot;
+      float* po = p.part_o + ps * D + d0;
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
         float o = 0.f;
@@ -294,17 +292,102 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(AttnParams p) {
         po[i] = o;
       }
       if ((threadIdx.x & 15) == 0) {
-        p.part_ml[2 * slot + 0] = M;
-        p.part_ml[2 * slot + 1] = L;
+        p.part_ml[2 * ps + 0] = M;
+        p.part_ml[2 * ps + 1] = L;
       }
     }
+  }
+}
+
+// Minimum workgroups per CU the register budget must allow (1: no limit; the
+// kernel needs about 228 VGPRs, two workgroups per CU).
+#ifndef YOCO_DEC_OCC
+#define YOCO_DEC_OCC 1
+#endif
+
+// Balanced split-K: the 128-row blocks of all sequences, in sequence order, are
+// cut into `parts` contiguous shares of (nearly) equal size, one per
+// workgroup of each (KV head, head chunk) column, so every workgroup streams
+// the same number of rows whatever the mix of lengths. A share can span
+// several sequences: each piece of it leaves its own partial, in slot
+// share + sequence (distinct for every piece of a column). The workgroup that
+// holds a sequence's first block records where its pieces are for the merge.
+template <int D, int U>
+__global__ __launch_bounds__(256, YOCO_DEC_OCC) void decode_split_bf16_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[DecLds<D, U>::kBytes];
+  const int share = blockIdx.x;
+  const int kh = blockIdx.y / p.head_chunks;
+  const int hc = blockIdx.y % p.head_chunks;
+  const int lane = threadIdx.x & 63;
+
+  // every wave counts the sequences' blocks (the same loads, cached) and finds
+  // the sequence holding this share's first block: no LDS, no barrier. The
+  // first 64 sequences' rows, first pool rows and prefix stay in registers.
+  int64_t start0;
+  const int32_t n0 = decode_rows(p, lane, &start0);
+  const int u0 = decode_blocks(n0);
+  const int incl0 = wave_incl_scan_i32(u0);
+  int64_t total = __builtin_amdgcn_readlane(incl0, 63);
+  for (int c0 = 64; c0 < p.batch; c0 += 64) {
+    int64_t st;
+    total += wave_sum_i32(decode_blocks(decode_rows(p, c0 + lane, &st)));
+  }
+  total = uniform_i64(total);
+  const int parts = total < p.splits ? (int)total : p.splits;
+  if (share >= parts) return;
+  const int64_t first = share_begin(share, total, parts);
+  const int64_t last = share_begin(share + 1, total, parts);
+  int b = p.batch;
+  int64_t pre = total;
+  int64_t carry = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+    int64_t st;
+    const int u = c0 == 0 ? u0 : decode_blocks(decode_rows(p, c0 + lane, &st));
+    const int incl = c0 == 0 ? incl0 : wave_incl_scan_i32(u);
+    const int64_t before = carry + incl - u;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(u > 0 && before <= first && first < before + u);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      b = c0 + l;
+      pre = carry + __builtin_amdgcn_readlane(incl - u, l);
+      break;
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  pre = uniform_i64(pre);
+
+  for (; b < p.batch && pre < last; ++b) {
+    int64_t start;
+    int32_t n_kv;
+    if (b < 64) {   // from the scan's registers
+      n_kv = __builtin_amdgcn_readlane(n0, b);
+      start = (int64_t)(((uint64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)start0 >> 32), b) << 32) |
+                        __builtin_amdgcn_readlane((uint32_t)start0, b));
+    } else {
+      n_kv = decode_rows(p, b, &start);
+    }
+    const int u = decode_blocks(n_kv);
+    if (u > 0) {
+      const int64_t lo = (first > pre ? first : pre) - pre;
+      const int64_t hi = (last < pre + u ? last : pre + u) - pre;
+      if (lo == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        const int64_t s_last = share_of_block(pre + u - 1, total, parts);
+        p.decode_meta[2 * b + 0] = share + b;
+        p.decode_meta[2 * b + 1] = (int32_t)(s_last - share + 1);
+      }
+      const int j1 = hi * kDecodeBlockRows < n_kv ? (int)(hi * kDecodeBlockRows) : n_kv;
+      decode_piece<D, U>(p, lds, b, start, (int)(lo * kDecodeBlockRows), j1, kh, hc, share + b);
+      __syncthreads();  // the combine's LDS reads are done before the next piece's tiles
+    }
+    pre += u;
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)p.splits, (unsigned)(p.hkv * p.head_chunks), (unsigned)p.batch);
+  const dim3 grid((unsigned)p.splits, (unsigned)(p.hkv * p.head_chunks));
   if (head_dim == 64)
     hipLaunchKernelGGL((decode_split_bf16_kernel<64, YOCO_DEC_U>), grid, dim3(256), 0, stream, p);
   else

@@ -1,10 +1,13 @@
-// Decode merge: combine the per-split partial softmax states of one query.
+// Decode merge: combine the partial softmax states of one query.
 //
-// Each split s of the shared-cache rows left (m_s, l_s, O_s): its running max
-// of the base-2 scores, its sum of weights exp2(t - m_s) and its unnormalised
-// weighted sum of V rows. The exact softmax over all rows is then
+// Each piece s of a sequence's rows (one share of the balanced split) left
+// (m_s, l_s, O_s): its running max of the base-2 scores, its sum of weights
+// exp2(t - m_s) and its unnormalised weighted sum of V rows. The exact softmax
+// over all rows is then
 //   M = max_s m_s,  L = sum_s l_s exp2(m_s - M),  O = sum_s O_s exp2(m_s - M) / L,
-// and LSE = (M + log2 L) ln 2. Splits with no rows carry m_s = -inf and weigh 0.
+// and LSE = (M + log2 L) ln 2. The pieces of sequence b sit in consecutive
+// slots, which the split pass recorded (first slot, count); a sequence with no
+// rows gets O = 0 and LSE = -inf.
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
@@ -27,13 +30,21 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams 
   __shared__ float part_o[kMergeGroups][kMergeDims];
   __shared__ float part_l[kMergeGroups];
   const int bh = blockIdx.x;  // b * hq + h
+  const int b = bh / p.hq;
+  const int h = bh % p.hq;
   const int d0 = blockIdx.y * kMergeDims;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)bh * p.splits;
+  // the sequence's rows and where the split pass left its pieces (loaded together)
+  int64_t start;
+  const int32_t n = decode_rows(p, b, &start);
+  const int32_t s0 = p.decode_meta[2 * b + 0];
+  int pieces = p.decode_meta[2 * b + 1];
+  if (n == 0 || s0 < 0 || pieces < 1 || (int64_t)s0 + pieces > p.slots) pieces = 0;   // (stale when n == 0)
+  const int64_t base = (int64_t)h * p.slots + (pieces > 0 ? s0 : 0);
   const float* ml = p.part_ml + 2 * base;
 
   float mx = -INFINITY;
-  for (int s = tid; s < p.splits; s += kMergeThreads) mx = fmaxf(mx, ml[2 * s]);
+  for (int s = tid; s < pieces; s += kMergeThreads) mx = fmaxf(mx, ml[2 * s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if ((tid & 63) == 0) red[tid >> 6] = mx;
@@ -48,7 +59,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams 
   if (M != -INFINITY) {
     const float* po = p.part_o + base * D + d0 + d;
 #pragma unroll 8
-    for (int s = g; s < p.splits; s += kMergeGroups) {
+    for (int s = g; s < pieces; s += kMergeGroups) {
       const float ms = ml[2 * s];
       const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
       lsum = fmaf(ml[2 * s + 1], w, lsum);

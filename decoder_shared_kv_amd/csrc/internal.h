@@ -27,12 +27,14 @@ struct AttnParams {
   int32_t window;             // sliding window in positions (0: none, plain causal)
   // prefill grid
   int32_t pos_blocks;         // position blocks covering max_q_len
-  // decode split plan
+  // decode split plan: the row blocks of all sequences are cut into `splits`
+  // equal shares per column (bf16: KV head x head chunk; f32: query head)
   int32_t splits;
-  int32_t split_rows;
+  int32_t slots;              // partial slots per query head: splits + batch
   int32_t head_chunks;        // query-head chunks of <= 16 per KV head (decode)
-  float* part_o;              // [B, Hq, splits, D] unnormalised partial outputs
-  float* part_ml;             // [B, Hq, splits, 2] (running max in base 2, sum of weights)
+  float* part_o;              // [Hq, slots, D] unnormalised partial outputs
+  float* part_ml;             // [Hq, slots, 2] (running max in base 2, sum of weights)
+  int32_t* decode_meta;       // [B, 2]: each sequence's first partial slot and its number of pieces
 };
 
 struct AppendParams {
@@ -177,6 +179,61 @@ __device__ __forceinline__ int32_t window_rows(int32_t n, int32_t window, int64_
     return window;
   }
   return n;
+}
+
+// Decode work unit: blocks of 128 rows of one sequence (a multiple of every
+// decode kernel's rows per iteration).
+constexpr int kDecodeBlockRows = 128;
+
+// Rows of sequence b that its decode query sees (0 for b >= batch) and the
+// pool row of the first of them.
+__device__ __forceinline__ int32_t decode_rows(const AttnParams& p, int b, int64_t* start) {
+  *start = 0;
+  if (b >= p.batch) return 0;
+  return window_rows(readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, start), p.window, start);
+}
+__device__ __forceinline__ int decode_blocks(int32_t rows) { return (rows + kDecodeBlockRows - 1) / kDecodeBlockRows; }
+
+// The balanced decode split. Each column cuts the `total` blocks of all
+// sequences into parts = min(shares planned, total) shares, so none is empty.
+// Share w of `parts` equal shares of `total` blocks starts at block
+// floor(w * total / parts); block x belongs to the last share starting at or
+// before it, share floor(((x + 1) * parts - 1) / total). Both quotients are
+// taken in fp64 (an emulated int64 division costs ~100 instructions): the
+// products are exact and a correctly rounded quotient of integers floors to
+// the exact result while total * parts < 2^52 (parts <= 4096 here, so up to
+// 2^40 blocks).
+__host__ __device__ inline int64_t share_begin(int64_t w, int64_t total, int parts) {
+  return (int64_t)((double)(w * total) / (double)parts);
+}
+__host__ __device__ inline int64_t share_of_block(int64_t x, int64_t total, int parts) {
+  return (int64_t)((double)((x + 1) * parts - 1) / (double)total);
+}
+
+// A value equal in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Wave-wide integer sum and inclusive prefix sum (64 lanes, all active).
+__device__ __forceinline__ int wave_incl_scan_i32(int x);
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan_i32(x), 63);
+}
+// The scan runs on DPP lane moves (no LDS): shifts right by 1, 2, 4, 8 within
+// each row of 16 lanes (lanes shifted in read 0), then the last lane of row 0
+// is added to row 1, of row 2 to row 3 (row_bcast:15, rows 1 and 3), and the
+// last lane of row 1 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
 }  // namespace yoco

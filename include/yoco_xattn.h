@@ -120,14 +120,17 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
  * Call after yoco_kv_append: sequence b's query sits at position seq_len[b]-1
  * and attends rows 0 .. seq_len[b]-1 (every Cross-Decoder layer re-reads the
  * shared cache: page "YOCO", section "KV Cache 与计算量分析", cost table).
- * Rows are split across workgroups (split-K) and merged by log-sum-exp.
+ * Rows are split across workgroups (split-K) and merged by log-sum-exp: the
+ * 128-row blocks of all sequences together are cut into equal shares, one per
+ * workgroup of each KV head (a share may span several sequences), so every
+ * workgroup reads the same number of rows whatever the mix of lengths.
  *   q          [device] [B, Hq, head_dim]
  *   max_kv_len [host] sizing hint for the split plan: the longest sequence's
- *              rows; longer sequences are still computed in full (the last split
- *              takes the remainder)
+ *              rows; the kernels count the rows on the device, so every row is
+ *              computed whatever the hints say
  *   total_kv_len [host] sizing hint: the rows of all sequences together, or 0
- *              for B * max_kv_len; rows per split are chosen so that about a
- *              thousand workgroups hold rows, whatever the length mix
+ *              for B * max_kv_len (values above B * max_kv_len count as that);
+ *              the number of shares follows it (at most 512 or 1024 workgroups)
  *   out        [device] [B, Hq, head_dim]; a sequence with no rows gets O = 0
  *   lse        [device] fp32 [B, Hq] or NULL; -inf for a sequence with no rows
  *   workspace  [device] >= yoco_xattn_workspace_size(dims, max_kv_len) bytes,
@@ -303,10 +306,13 @@ yoco_status yoco_gret_decode(const yoco_gret_dims* dims, const void* q, const vo
                              const float* gamma, float* state, void* out, void* stream);
 
 /* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len (any
- * total_kv_len, any smaller max_kv_len). */
+ * total_kv_len, any smaller max_kv_len): per query head one fp32 partial
+ * (head_dim + 2 values) per share and sequence, and two int32 per sequence. */
 yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes);
 
-/* [host] Number of row splits yoco_xattn_decode uses (for reports and tests). */
+/* [host] The split plan yoco_xattn_decode uses (for reports and tests):
+ * *splits = shares per KV head (bf16) or per query head (fp32),
+ * *rows_per_split = rows of one share for rows as the hints describe them. */
 yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len,
                                      int64_t total_kv_len, int32_t* splits,
                                      int32_t* rows_per_split);

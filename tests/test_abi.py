@@ -207,15 +207,26 @@ def test_gret_argument_checks(lib):
 
 
 def test_split_plan():
-    # decode: 8 x 131072 rows, Hkv=2 -> 16 (sequence, KV head) units, ~1024 workgroups in total
+    # bf16: 512 workgroups over one or two (KV head, head chunk) columns, 1024
+    # over more; each share is one equal part of all sequences' 128-row blocks
     s, r = dk.decode_splits(8, 16, 2, 128, X.torch.bfloat16, 131072)
-    assert s * r >= 131072 and r % 128 == 0 and 512 <= s * 16 <= 2048
+    assert s == 256 and r == 4096
     s, r = dk.decode_splits(1, 16, 2, 128, X.torch.bfloat16, 1048640, 1048640)
-    assert s * r >= 1048640 and (s - 1) * r < 1048640 and 512 <= s * 2 <= 2048
+    assert s == 256 and s * r >= 1048640 and r % 128 == 0
+    s, r = dk.decode_splits(4, 32, 4, 128, X.torch.bfloat16, 131072)
+    assert s == 256 and r == 2048
+    # few blocks: one share per block, never a planned-empty share
     s, r = dk.decode_splits(1, 4, 1, 64, X.torch.float32, 1)
     assert s == 1 and r == 128
     s, r = dk.decode_splits(3, 32, 1, 128, X.torch.bfloat16, 0)
     assert s == 1
+    s, r = dk.decode_splits(2, 16, 2, 128, X.torch.bfloat16, 1000, 1300)
+    assert s == 11 and r == 128
+    # a total hint above B x max_kv_len counts as B x max_kv_len
+    assert dk.decode_splits(2, 16, 2, 128, X.torch.bfloat16, 1000, 10 ** 9) == (16, 128)
+    # g = 32: two head chunks per KV head
+    s, r = dk.decode_splits(1, 32, 1, 128, X.torch.bfloat16, 1 << 20)
+    assert s == 256
 
 
 def test_workspace_is_monotone_and_bounds_every_plan():
@@ -225,18 +236,20 @@ def test_workspace_is_monotone_and_bounds_every_plan():
         ws = dk.workspace_size(8, 16, 2, 128, torch.bfloat16, n)
         assert ws >= prev, (n, ws)
         prev = ws
-        for total in [0, n, 2 * n + 5, 8 * n, 3 * n // 2]:
+        for total in [0, n, 2 * n + 5, 8 * n, 3 * n // 2, 100 * n + 7]:
             for m in {n, n // 2, max(n - 1, 0)}:
                 s, r = dk.decode_splits(8, 16, 2, 128, torch.bfloat16, m, total)
-                assert s * r >= max(m, 1) and ws >= 8 * 16 * s * (128 + 2) * 4, (n, m, total, s, r, ws)
+                # partials [Hq, shares + B, d + 2] fp32 and [B, 2] int32
+                assert s * r >= max(m, 1) and ws >= 16 * (s + 8) * (128 + 2) * 4 + 8 * 8, (n, m, total, s, r, ws)
 
 
 def test_split_plan_counts_all_rows():
     import torch
-    # 16 ragged sequences: rows per split follow the total, not B x the longest
+    # 16 ragged sequences: the shares follow the total rows; every workgroup of a
+    # column gets the same number of blocks, so the ~1024 workgroups are balanced
     lens = [13257, 14478, 45818, 11785, 13140, 8156, 31001, 13071, 23276, 22166, 17936, 22454, 5776, 11113, 5199, 18047]
     s, r = dk.decode_splits(16, 32, 8, 128, torch.bfloat16, max(lens), sum(lens))
-    busy = sum(-(-n // r) for n in lens) * 8
-    assert 768 <= busy <= 1400, (s, r, busy)
+    blocks = -(-sum(lens) // 128)
+    assert s * 8 == 1024 and r == -(-blocks // s) * 128, (s, r)
     s0, r0 = dk.decode_splits(16, 32, 8, 128, torch.bfloat16, max(lens), 0)
-    assert r0 > r
+    assert s0 == s and r0 > r

@@ -94,7 +94,7 @@ def test_decode_empty_sequence():
 
 
 def test_decode_max_kv_len_underestimate_still_exact():
-    """max_kv_len is a sizing hint: the last split takes any remainder."""
+    """max_kv_len is a sizing hint: the kernels count the rows themselves."""
     say("decode with an under-estimated max_kv_len")
     c = synth.make_decode_case([3000], 16, 2, 128, 1, 1, "bf16", seed=4, std=1.0)
     cache = device_cache(c.k_pool, c.v_pool, c.seq_start, c.seq_len, c.seq_cap)
@@ -102,6 +102,37 @@ def test_decode_max_kv_len_underestimate_still_exact():
     ref, _ = oracle.decode_ref(synth.to_f64(c.q[0, 0]), synth.to_f32(c.k_pool), synth.to_f32(c.v_pool),
                                c.seq_start.numpy(), c.seq_len.numpy(), c.scale)
     parity.check(out, ref, "bf16", discriminating=True)
+
+
+_MIXED = (0, 5, 129, 0, 0, 300, 1, 128, 127, 0, 7000, 256, 2)
+_MANY = tuple(int(x) for x in np.random.default_rng(5).integers(0, 400, size=100))
+
+
+@pytest.mark.parametrize("lens,hints,dtype", [
+    (_MIXED, "true", "bf16"),       # one block per share, empty sequences between
+    (_MIXED, "under", "bf16"),      # one share for everything: a share spans every sequence
+    (_MIXED, "over", "bf16"),       # far more shares than blocks: most shares empty
+    (_MANY, "true", "bf16"),        # 100 sequences: the block count runs over two scan chunks
+    (_MANY, "under", "bf16"),
+    (_MIXED, "under", "f32"),
+    (_MIXED, "over", "f32"),
+])
+def test_decode_balanced_shares(lens, hints, dtype):
+    """The balanced split: shares of equal block counts over all sequences,
+    whatever the hints say, with every sequence's pieces merged exactly."""
+    say(f"decode balanced shares {dtype} hints={hints} B={len(lens)}")
+    c = synth.make_decode_case(list(lens), 16, 2, 128, 1, 1, dtype, seed=len(lens), std=1.0, cap_extra=2)
+    cache = device_cache(c.k_pool, c.v_pool, c.seq_start, c.seq_len, c.seq_cap)
+    mx, tot = max(lens), sum(lens)
+    kw = {"true": dict(max_kv_len=mx, total_kv_len=tot), "under": dict(max_kv_len=1, total_kv_len=1),
+          "over": dict(max_kv_len=200000, total_kv_len=0)}[hints]
+    out, lse = run_decode(cache, c.q[0, 0], c.scale, **kw)
+    ref, ref_lse = oracle.decode_ref(synth.to_f64(c.q[0, 0]), synth.to_f32(c.k_pool), synth.to_f32(c.v_pool),
+                                     c.seq_start.numpy(), c.seq_len.numpy(), c.scale)
+    empty = np.array(lens) == 0
+    assert np.all(out[empty] == 0.0) and np.all(np.isneginf(lse[empty]))
+    parity.check(out[~empty], ref[~empty], dtype, discriminating=True, what="decode out")
+    parity.check_lse(lse, ref_lse, dtype, what="decode lse")
 
 
 # --------------------------------------------------------------------------- append
