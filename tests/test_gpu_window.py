@@ -19,11 +19,12 @@ from gpu_util import DEV, device_cache, f64, run_decode, run_prefill, say
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_window(case, window, layer=0):
+def run_prefill_window(case, window, layer=0, max_q=None):
     cache = device_cache(case.k_pool, case.v_pool, case.seq_start, case.seq_len, case.seq_cap)
     q = case.q[layer].to(DEV)
     lse = torch.full((q.shape[1], case.total_q), float("nan"), device=DEV)
-    max_q = int((case.cu_seqlens[1:] - case.cu_seqlens[:-1]).max())
+    if max_q is None:
+        max_q = int((case.cu_seqlens[1:] - case.cu_seqlens[:-1]).max())
     out = dk.xattn_prefill_window(cache, q, case.cu_seqlens.to(DEV), max_q, window, case.scale, lse=lse)
     torch.cuda.synchronize()
     return f64(out), lse.cpu().numpy().astype(np.float64)
@@ -51,6 +52,26 @@ def test_window_prefill(lens, window, hq, hkv, d, dtype):
     e = parity.check(out, ref, dtype, discriminating=True, what="window prefill")
     parity.check_lse(lse, ref_lse, dtype, what="window prefill lse")
     say(f"  max-abs {e['max_abs']:.2e} row-rel {e['row_rel']:.2e}")
+
+
+@pytest.mark.parametrize("lens,window,hq,hkv,d", [
+    ((1000, 300, 64, 1, 0, 517), 64, 16, 4, 128),   # short, single-row and empty sequences
+    ((5, 130, 64, 2000), 100, 8, 2, 128),
+    ((700, 129), 33, 6, 3, 64),
+])
+def test_window_grid_hint(lens, window, hq, hkv, d):
+    """max_q_len only sizes the grid: with a hint of 1 every workgroup walks all
+    position blocks of its unit in turn, and each row comes out bitwise as with
+    one workgroup per block; both match the oracle (short and single-row
+    sequences, an empty one, head_dim 64)."""
+    say(f"window grid hint lens={lens} C={window} hq={hq} hkv={hkv} d={d}")
+    c = synth.make_prefill_case(list(lens), hq, hkv, d, 1, "bf16", seed=sum(lens) + 3 * window, std=1.0, cap_extra=3)
+    out, lse = run_prefill_window(c, window)
+    out1, lse1 = run_prefill_window(c, window, max_q=1)
+    assert np.array_equal(out, out1) and np.array_equal(lse, lse1, equal_nan=True)
+    ref, ref_lse = ref_prefill(c, window)
+    parity.check(out, ref, "bf16", discriminating=True, what="window grid hint")
+    parity.check_lse(lse, ref_lse, "bf16", what="window grid hint lse")
 
 
 def test_window_one_is_own_row():
