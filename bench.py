@@ -289,22 +289,23 @@ def main():
 
 
 def device_info(torch, dev):
-    """CU count and a read probe: torch's sum over 2 GiB of bf16 (a plain streaming
-    read, for context beside the 8 TB/s published figure)."""
+    """CU count and a copy probe: torch's device copy of 1 GiB (bytes read plus
+    bytes written per second), for context beside the 8 TB/s published figure."""
     props = torch.cuda.get_device_properties(dev)
-    x = torch.ones(1 << 30, dtype=torch.bfloat16, device=dev)
+    a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
     for _ in range(2):
-        x.sum()
+        b.copy_(a)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(5):
-        x.sum()
+        b.copy_(a)
     e1.record()
     torch.cuda.synchronize()
-    gbs = 5 * x.numel() * 2 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del x
+    gbs = 5 * 2 * a.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
     return {"name": props.name, "compute_units": props.multi_processor_count,
-            "read_probe_GBps": gbs, "read_probe": "torch sum over 2 GiB of bf16, 5 passes"}
+            "copy_probe_GBps": gbs, "copy_probe": "torch device copy of 1 GiB, 5 passes, read + write bytes"}
 
 
 def bench_decode_1m(args, torch, dk, synth, dev):
