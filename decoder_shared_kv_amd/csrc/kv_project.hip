@@ -46,6 +46,7 @@ __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 12
 __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kPStages * kPStage];
   __shared__ int64_t prow[kPM];     // pool row of each tile row, -1: not written
+  __shared__ float ss_part[2][kPM]; // sums of squares of each row, two halves of k
   __shared__ float inv_rms[kPM];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
 
@@ -54,9 +55,15 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
   const int wave = tid >> 6;
   const int wm = wave >> 1;          // 0..3: rows wm*64 ..
   const int wn = wave & 1;           // 0..1: columns wn*64 ..
+  // XCD-aware raster: workgroup i runs on XCD i % 8; each XCD takes a
+  // contiguous range of tiles in row-block-major order, so the resident
+  // workgroups of an XCD share their X row blocks in its L2
   const int n_tiles = p.n_cols / kPN;
-  const int nt = blockIdx.x % n_tiles;
-  const int mt = blockIdx.x / n_tiles;
+  const int grid = (int)gridDim.x;
+  const int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+  const int tile = xcd * (grid / kXcds) + min(xcd, grid % kXcds) + j;
+  const int nt = tile % n_tiles;
+  const int mt = tile / n_tiles;
   const int64_t m0 = (int64_t)mt * kPM;
   const int n0 = nt * kPN;
 
@@ -147,8 +154,9 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      if (wn == 0) {
-        // sum of squares of this lane's 8 values of row r (k half hf)
+      if ((kk >> 1) == wn) {
+        // sum of squares of this lane's 8 values of row r (k half hf); the two
+        // waves that read the same rows take half of the k steps each
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -160,13 +168,13 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
       }
     }
   }
-  if (wn == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float tot = ss[i] + __shfl_xor(ss[i], 32);
-      if (hf == 0) inv_rms[wm * 64 + 32 * i + qr] = 1.0f / sqrtf(tot / (float)p.k_dim + p.eps);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const float tot = ss[i] + __shfl_xor(ss[i], 32);
+    if (hf == 0) ss_part[wn][wm * 64 + 32 * i + qr] = tot;
   }
+  __syncthreads();
+  if (tid < kPM) inv_rms[tid] = 1.0f / sqrtf((ss_part[0][tid] + ss_part[1][tid]) / (float)p.k_dim + p.eps);
   __syncthreads();
 
   // epilogue: lane holds column n0 + wn*64 + 32j + qr, rows 8(r/4) + 4hf + r%4 of block i
@@ -191,6 +199,224 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
         dst[pr * hd + nc] = (__bf16)val;
       }
     }
+  }
+}
+
+// Wide tile (n_cols a multiple of 256): 256 rows x 256 columns per workgroup,
+// 32 k per stage through 4 stages (32 KB each), so each row block of X is read
+// half as often as with 128 columns and every byte brought into LDS feeds
+// twice the MFMA work. The product is formed transposed, C^T = W' X^T (A = W'
+// rows, B = X rows), so a lane ends up with 4 consecutive output columns per
+// register group; the tile is staged in LDS (the stages' 128 KB) and written
+// as whole rows, 16 bytes per lane. Waves: 4 (rows) x 2 (columns), each
+// 64 rows x 128 columns (2 x 4 MFMA blocks).
+constexpr int kWM = 256;
+constexpr int kWN = 256;
+constexpr int kWK = 32;
+constexpr int kWStages = 4;
+constexpr int kWXBytes = kWM * kWK * 2;     // 16 KB
+constexpr int kWWBytes = kWN * kWK * 2;     // 16 KB
+constexpr int kWStage = kWXBytes + kWWBytes;
+constexpr int kWXLoads = kWM * kWK / 8 / kPThreads;   // 2
+constexpr int kWWLoads = kWN * kWK / 8 / kPThreads;   // 2
+static_assert(kWStages * kWStage == kWM * kWN * 2, "the output tile is staged in the stages");
+
+// 16-byte chunk c (of 4) of row r of a [rows][32 k] tile: rows r and r + 4q fall
+// on different chunks within each 16 rows, so 16 lanes reading one chunk of 16
+// consecutive rows hit distinct banks
+__device__ __forceinline__ uint32_t swz32(int r, int c) { return (uint32_t)(r * 64 + 16 * (c ^ ((r >> 2) & 3))); }
+// 16-byte chunk c (of 32) of row r of the [256][256] bf16 output staging tile
+__device__ __forceinline__ uint32_t swz_out(int r, int c) { return (uint32_t)(r * 512 + 16 * (c ^ (r & 31))); }
+
+__global__ __launch_bounds__(kPThreads, 1) void kv_project_wide_kernel(ProjectParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kWStages * kWStage];
+  __shared__ int64_t prow[kWM];
+  __shared__ float ss_part[2][kWM];
+  __shared__ float inv_rms[kWM];
+  YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wt = wave >> 1;          // 0..3: rows wt*64 ..
+  const int wn = wave & 1;           // 0..1: columns wn*128 ..
+  const int n_tiles = p.n_cols / kWN;
+  const int grid = (int)gridDim.x;
+  const int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+  const int tile = xcd * (grid / kXcds) + min(xcd, grid % kXcds) + j;
+  const int nt = tile % n_tiles;
+  const int mt = tile / n_tiles;
+  const int64_t m0 = (int64_t)mt * kWM;
+  const int n0 = nt * kWN;
+
+  if (tid < kWM) {
+    const int64_t t = m0 + tid;
+    int64_t dst = -1;
+    if (t < p.total_rows) {
+      int lo = 0, hi = p.batch;       // find b with cu[b] <= t < cu[b + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu_seqlens[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int b = lo;
+      const int64_t c0 = p.cu_seqlens[b], c1 = p.cu_seqlens[b + 1];
+      const int64_t len = p.seq_len[b], cap = p.seq_cap[b], start = p.seq_start[b];
+      const bool fits = t >= c0 && t < c1 && c1 <= p.total_rows && len >= 0 && start >= 0 &&
+                        len + (c1 - c0) <= cap && start + len + (c1 - c0) <= p.pool_rows;
+      if (fits) dst = start + len + (t - c0);
+    }
+    prow[tid] = dst;
+  }
+  // the row lookups' loads are done: from here on the only loads in flight are
+  // the tile copies, which the loop awaits by count (a load of the compiler's
+  // own still pending at the loop would make it wait for everything there)
+  wait_vm_lgkm0<0>();
+
+  // this thread's chunks: chunk q = i * threads + tid -> tile row q / 4, slot q % 4
+  uint32_t xoff[kWXLoads], woff[kWWLoads];
+  const uint32_t wave_lds = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64 * 16;
+#pragma unroll
+  for (int i = 0; i < kWXLoads; ++i) {
+    const int q = i * kPThreads + tid;
+    int64_t row = m0 + q / 4;
+    if (row >= p.total_rows) row = p.total_rows - 1;     // rows past the end repeat the last one
+    const int c = (q % 4) ^ (((q / 4) >> 2) & 3);        // the chunk that belongs at this LDS slot
+    xoff[i] = (uint32_t)((row - m0) * p.k_dim * 2 + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kWWLoads; ++i) {
+    const int q = i * kPThreads + tid;
+    const int c = (q % 4) ^ (((q / 4) >> 2) & 3);
+    woff[i] = (uint32_t)((q / 4) * p.k_dim * 2 + c * 16);
+  }
+  const char* xbase = static_cast<const char*>(p.x) + m0 * p.k_dim * 2;
+  const char* wbase = static_cast<const char*>(p.w) + (int64_t)n0 * p.k_dim * 2;
+  const int k_steps = p.k_dim / kWK;
+
+  auto issue = [&](int ks) {
+    const uint32_t st = wave_lds + (ks % kWStages) * kWStage;
+    const char* xb = xbase + (int64_t)ks * kWK * 2;
+    const char* wb = wbase + (int64_t)ks * kWK * 2;
+#pragma unroll
+    for (int i = 0; i < kWXLoads; ++i) dma16(xb, xoff[i], st + i * kPThreads * 16);
+#pragma unroll
+    for (int i = 0; i < kWWLoads; ++i) dma16(wb, woff[i], st + kWXBytes + i * kPThreads * 16);
+  };
+  constexpr int L = kWXLoads + kWWLoads;
+
+#pragma unroll
+  for (int s = 0; s < kWStages - 1; ++s)
+    if (s < k_steps) issue(s);
+
+  // acc[tb][nb]: C^T block (output columns 32 nb .., rows 32 tb ..) of this wave
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[tb][nb] = f32x16{};
+  float ss[2] = {0.f, 0.f};
+  const int qr = lane & 31, hf = lane >> 5;
+
+  for (int ks = 0; ks < k_steps; ++ks) {
+    // stage ks is in when at most the stages requested after it are in flight
+    const int ahead = min(kWStages - 2, k_steps - 1 - ks);
+    if (ahead >= 2) wait_vm_lgkm0<2 * L>();
+    else if (ahead == 1) wait_vm_lgkm0<L>();
+    else wait_vm_lgkm0<0>();
+    barrier_only();   // stage ks is in for every thread; stage (ks - 1) % S is free
+    if (ks + kWStages - 1 < k_steps) issue(ks + kWStages - 1);
+    const YOCO_LDS char* xs = smem + (ks % kWStages) * kWStage;
+    const YOCO_LDS char* ws = xs + kWXBytes;
+    // all operand reads of the stage first (both 16-k steps), then the MFMAs,
+    // so the second step's reads are in flight during the first step's MFMAs
+    bf16x8 xb[kWK / 16][2], wa[kWK / 16][4];
+#pragma unroll
+    for (int kk = 0; kk < kWK / 16; ++kk) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        xb[kk][tb] = *reinterpret_cast<const YOCO_LDS bf16x8*>(xs + swz32(wt * 64 + 32 * tb + qr, 2 * kk + hf));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        wa[kk][nb] = *reinterpret_cast<const YOCO_LDS bf16x8*>(ws + swz32(wn * 128 + 32 * nb + qr, 2 * kk + hf));
+    }
+#pragma unroll
+    for (int kk = 0; kk < kWK / 16; ++kk) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[tb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[kk][nb], xb[kk][tb], acc[tb][nb], 0, 0, 0);
+    }
+    // sum of squares of this lane's 8 values of row qr (k half hf); the two
+    // waves that read the same rows take one 16-k step each
+#pragma unroll
+    for (int kk = 0; kk < kWK / 16; ++kk) {
+      if (kk != wn) continue;   // wave-uniform; constant indices keep xb in registers
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 v2 = {xb[kk][tb][2 * e], xb[kk][tb][2 * e + 1]};
+          ss[tb] = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss[tb], false);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const float tot = ss[tb] + __shfl_xor(ss[tb], 32);
+    if (hf == 0) ss_part[wn][wt * 64 + 32 * tb + qr] = tot;
+  }
+  wait_vm_lgkm0<0>();
+  __syncthreads();   // every wave is done with the stages: they become the output tile
+  if (tid < kWM) inv_rms[tid] = 1.0f / sqrtf((ss_part[0][tid] + ss_part[1][tid]) / (float)p.k_dim + p.eps);
+  __syncthreads();
+
+  // stage: lane holds output row t = wt*64 + 32tb + qr, columns
+  // wn*128 + 32nb + 8g + 4hf .. +3 in registers 4g .. 4g + 3
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int t = wt * 64 + 32 * tb + qr;
+    const float s = inv_rms[t];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * 128 + 32 * nb + 8 * g;     // 16-byte chunk col / 8, half hf
+        const u32x2 v = {pack2(acc[tb][nb][4 * g + 0] * s, acc[tb][nb][4 * g + 1] * s),
+                         pack2(acc[tb][nb][4 * g + 2] * s, acc[tb][nb][4 * g + 3] * s)};
+        *reinterpret_cast<YOCO_LDS u32x2*>(smem + swz_out(t, col / 8) + 8 * hf) = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  // write whole rows: 32 lanes per row, 16 bytes (8 columns) each
+  const int hd = p.n_cols / 2;                 // K^ columns, then V^ columns
+#pragma unroll 4
+  for (int it = 0; it < kWM * 32 / kPThreads; ++it) {
+    const int q = it * kPThreads + tid;
+    const int t = q / 32, c = q % 32;
+    const int64_t pr = prow[t];
+    if (pr < 0) continue;
+    const int n = n0 + 8 * c;
+    const bool is_v = n >= hd;
+    const int nc = is_v ? n - hd : n;
+    u32x4 v = *reinterpret_cast<const YOCO_LDS u32x4*>(smem + swz_out(t, c));
+    const __bf16* bottom = static_cast<const __bf16*>(is_v ? p.v1 : p.k1);
+    if (bottom != nullptr) {
+      const float a1 = is_v ? p.av1 : p.ak1, a2 = is_v ? p.av2 : p.ak2;
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(bottom + (m0 + t) * hd + nc);
+      const bf16x8 x8 = __builtin_bit_cast(bf16x8, v), b8 = __builtin_bit_cast(bf16x8, bv);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack2(p.lam * (a1 * (float)b8[2 * e] + a2 * (float)x8[2 * e]),
+                     p.lam * (a1 * (float)b8[2 * e + 1] + a2 * (float)x8[2 * e + 1]));
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    __bf16* dst = static_cast<__bf16*>(is_v ? p.v : p.k);
+    *reinterpret_cast<u32x4*>(dst + pr * hd + nc) = v;
   }
 }
 
@@ -314,6 +540,10 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const __bf16* gain, const 
 hipError_t launch_kv_project(const ProjectParams& p, hipStream_t stream) {
   if (p.total_rows > 0 && p.total_rows <= kSmallRows) {
     hipLaunchKernelGGL(kv_project_small_kernel, dim3(p.n_cols / 16), dim3(64 * kSmallWaves), 0, stream, p);
+  } else if (p.total_rows > 0 && p.n_cols % kWN == 0 && p.k_dim % kWK == 0) {
+    const int64_t m_tiles = (p.total_rows + kWM - 1) / kWM;
+    const int64_t grid = m_tiles * (p.n_cols / kWN);
+    hipLaunchKernelGGL(kv_project_wide_kernel, dim3((unsigned)grid), dim3(kPThreads), 0, stream, p);
   } else if (p.total_rows > 0) {
     const int64_t m_tiles = (p.total_rows + kPM - 1) / kPM;
     const int64_t grid = m_tiles * (p.n_cols / kPN);
