@@ -44,11 +44,13 @@ __device__ __forceinline__ float sum_xor16(float x) { const f32x2 r = lane_pair1
 // transposing read of one wave covers 8 rows x 64 bytes; with these values its
 // 16-lane groups (32 banks) and its 32-lane halves (64 banks) both hit distinct
 // banks (checked exhaustively over the read pattern on the host).
+// (D = 128: 0, 4, 10, 14 for r mod 4 = 0..3, as arithmetic: a table indexed at
+// run time would be a memory load, which the compiler then awaits with
+// everything else in flight.)
 template <int D>
 __device__ __forceinline__ int v_swizzle(int r) {
   if constexpr (D == 128) {
-    constexpr int t[4] = {0, 4, 10, 14};
-    return t[r & 3];
+    return 4 * (r & 3) + 2 * ((r >> 1) & 1);
   } else {
     return 2 * (r & 3);
   }
