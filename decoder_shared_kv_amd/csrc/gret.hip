@@ -121,8 +121,10 @@ __device__ __forceinline__ ChunkInfo chunk_info(const GretParams& p, int b, int 
 // 1. per-chunk state contribution U^T[dv][dk] and total decay
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kGThreads, 1) void gret_state_kernel(GretParams p) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kGC * D * 2];
+__global__ __launch_bounds__(kGThreads, 2) void gret_state_kernel(GretParams p) {
+  constexpr int kQ = kGC / 4;                        // rows per quarter
+  constexpr int kQBytes = kQ * D * 2;                // one matrix's quarter
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * kQBytes];   // 2 stages x (K, V)
   __shared__ __attribute__((aligned(16))) float wgt[kGC];
   __shared__ float wsum[4];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
@@ -136,19 +138,22 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_state_kernel(GretParams p) 
   const float a_last = wsum[0] + wsum[1] + wsum[2] + wsum[3];   // gates past the end count 1
   if (tid < kGC) wgt[tid] = tid < ci.n ? exp2f(a_last - A) : 0.f;
   if (tid == 0) p.chunk_decay[((int64_t)b * p.heads + h) * p.max_chunks + c] = exp2f(a_last);
+  wait_vm_lgkm0<0>();   // the gates are in: from here on only the tile copies are in flight
 
-  // K and V of the chunk in two halves of 128 rows: the second half's copies
-  // overlap the first half's MFMAs. Half f of a matrix sits at its tile rows 128 f.
-  const uint32_t kl = (uint32_t)(uintptr_t)smem, vl = kl + kGC * D * 2;
-  constexpr int kHalf = kGC / 2;
-  constexpr int LH = 2 * (kHalf * D / 8 / kGThreads);          // copies per thread and half
+  // K and V of the chunk in quarters of 64 rows through two stages (64 KB of LDS,
+  // so two workgroups share a CU and one's copies overlap the other's MFMAs)
+  const uint32_t base = (uint32_t)(uintptr_t)smem;
+  constexpr int LQ = 2 * (kQ * D / 8 / kGThreads);   // copies per thread and quarter
   const __bf16* kg = static_cast<const __bf16*>(p.k);
   const __bf16* vg = static_cast<const __bf16*>(p.v);
-#pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    load_tile<D, true>(kg, ci.row0, ci.n, kHalf * f, kHalf, p.heads, h, kl + kHalf * f * D * 2);
-    load_tile<D, true>(vg, ci.row0, ci.n, kHalf * f, kHalf, p.heads, h, vl + kHalf * f * D * 2);
-  }
+  auto issue = [&](int f) {
+    const uint32_t st = base + (f & 1) * 2 * kQBytes;
+    load_tile<D, true>(kg, ci.row0, ci.n, kQ * f, kQ, p.heads, h, st);
+    load_tile<D, true>(vg, ci.row0, ci.n, kQ * f, kQ, p.heads, h, st + kQBytes);
+  };
+  const int n_q = (ci.n + kQ - 1) / kQ;              // quarters holding rows
+  issue(0);
+  if (n_q > 1) issue(1);
 
   // output blocks (dv block i, dk block j) of 32 x 32; D = 128: 16 blocks, two per
   // wave (same i); D = 64: 4 blocks, waves 0..3
@@ -161,33 +166,40 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_state_kernel(GretParams p) 
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = f32x16{};
   const int hf = lane >> 5;
-  const YOCO_LDS char* kt = smem;
-  const YOCO_LDS char* vt = smem + kGC * D * 2;
-  for (int s = 0; s < kGC / 16; ++s) {
-    if (s == 0 || s == kGC / 32) {
-      // the half that begins here is in (the first half: with the second's copies in flight)
-      if (s == 0) wait_vm_lgkm0<LH>(); else wait_vm_lgkm0<0>();
-      barrier_only();
-    }
-    // k-step s: keys base + {0..3, 8..11} + 4h with base = 16 s (two 4-key runs per lane)
-    if (idle) continue;
-    const int base = 16 * s;
-    const bf16x8 av = read_tr<D>(vt, base, bi, lane);                 // V^T rows dv, 8 keys
-    const f32x4 w0 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (base + 4 * hf));
-    const f32x4 w1 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (base + 8 + 4 * hf));
+  for (int f = 0; f < n_q; ++f) {
+    // quarter f is in when at most the next one's copies are in flight
+    if (f + 1 < n_q) wait_vm_lgkm0<LQ>(); else wait_vm_lgkm0<0>();
+    barrier_only();
+    const YOCO_LDS char* kt = smem + (f & 1) * 2 * kQBytes;
+    const YOCO_LDS char* vt = kt + kQBytes;
+    if (!idle) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int bj = (blk0 + e) % NB;
-      const bf16x8 kb = read_tr<D>(kt, base, bj, lane);               // K columns dk, same 8 keys
-      uint32_t wv[4];
+      for (int s4 = 0; s4 < kQ / 16; ++s4) {
+        // keys 16 s + {0..3, 8..11} + 4h of the chunk, s = 4f + s4 (two 4-key runs per lane)
+        const int base_q = 16 * s4;               // row within the quarter
+        const int key = kQ * f + base_q;          // row within the chunk
+        const bf16x8 av = read_tr<D>(vt, base_q, bi, lane);            // V^T rows dv, 8 keys
+        const f32x4 w0 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (key + 4 * hf));
+        const f32x4 w1 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (key + 8 + 4 * hf));
 #pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const f32x4 ww = z == 0 ? w0 : w1;
-        wv[2 * z] = pack2((float)kb[4 * z + 0] * ww[0], (float)kb[4 * z + 1] * ww[1]);
-        wv[2 * z + 1] = pack2((float)kb[4 * z + 2] * ww[2], (float)kb[4 * z + 3] * ww[3]);
+        for (int e = 0; e < PER; ++e) {
+          const int bj = (blk0 + e) % NB;
+          const bf16x8 kb = read_tr<D>(kt, base_q, bj, lane);          // K columns dk, same 8 keys
+          uint32_t wv[4];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const f32x4 ww = z == 0 ? w0 : w1;
+            wv[2 * z] = pack2((float)kb[4 * z + 0] * ww[0], (float)kb[4 * z + 1] * ww[1]);
+            wv[2 * z + 1] = pack2((float)kb[4 * z + 2] * ww[2], (float)kb[4 * z + 3] * ww[3]);
+          }
+          const bf16x8 kw = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, kw, acc[e], 0, 0, 0);
+        }
       }
-      const bf16x8 kw = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-      acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, kw, acc[e], 0, 0, 0);
+    }
+    if (f + 2 < n_q) {
+      barrier_only();   // every wave is done with stage f & 1
+      issue(f + 2);
     }
   }
   if (idle) return;
