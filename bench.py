@@ -216,6 +216,7 @@ def main():
         step(False)
     torch.cuda.synchronize()
     pre_ms, dec_ms = 0.0, 0.0
+    pre_steps, dec_steps = [], []
     dec_bytes = 0.0
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -224,12 +225,20 @@ def main():
             dec_bytes += wd.layers * decode_bytes(lens_now, wd.kv_heads, wd.q_heads, wd.head_dim)
         ev[3 if "decode" not in skip else 1].synchronize()
         if "prefill" not in skip:
-            pre_ms += ev[0].elapsed_time(ev[1])
+            pre_steps.append(ev[0].elapsed_time(ev[1]))
+            pre_ms += pre_steps[-1]
         if "decode" not in skip:
-            dec_ms += ev[2].elapsed_time(ev[3])
+            dec_steps.append(ev[2].elapsed_time(ev[3]))
+            dec_ms += dec_steps[-1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert int(flag.item()) == 0, "append overflowed"
+
+    def spread(t):
+        import numpy as np
+        t = np.asarray(t, dtype=np.float64)
+        return {"n": int(t.size), "median_ms": float(np.median(t)), "min_ms": float(t.min()),
+                "p90_ms": float(np.percentile(t, 90))}
 
     def call_stats(call, reps=CALL_REPS):
         """Per-call spread after the timed region: one event pair around each of
@@ -262,6 +271,7 @@ def main():
                            **traffic_fields("prefill_bf16_kernel<128>", layer_s),
                            "kernel": "prefill_bf16_kernel<128>", "avg_launch_ms": layer_s * 1e3,
                            "algorithmic_per_launch": flops_layer}
+        res["prefill_steps"] = {**spread(pre_steps), "what": f"{wp.layers} layer calls per step"}
         res["prefill_calls"] = call_stats(
             lambda i: dk.xattn_prefill(pcache, qs[i % wp.layers], cu, n, pc.scale, out=out_p, lse=lse_p))
     if "decode" not in skip:
@@ -275,6 +285,7 @@ def main():
                                                                                     call_s),
                                       "kernel": "decode_split_bf16_kernel<128, 2> + decode_merge_kernel "
                                                 "(one call: both launches, timed together)"},
+                         "steps": {**spread(dec_steps), "what": f"one append and {wd.layers} layer calls per step"},
                          "calls": call_stats(
                              lambda i: dk.xattn_decode(dcache, qd[i % wd.layers], max(lens_now), dc.scale, ws,
                                                        out=out_d, lse=lse_d))}
