@@ -17,8 +17,8 @@
 //    16 keys, so P^T never moves between lanes; V^ is transposed once through a
 //    small wave-private LDS tile to become the A operand (V^T);
 //  * online softmax in the base-2 domain, per lane, with two cross-lane max
-//    reductions per iteration; the partial (max, sum, unnormalised O) of the
-//    split is merged by decode_merge;
+//    reductions per iteration; the partial (max, sum, unnormalised O) of each
+//    piece of a share is merged by decode_merge;
 //  * nontemporal 16-byte loads: the cache is streamed once per call.
 #include <hip/hip_bf16.h>
 
@@ -172,7 +172,7 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, char* lds, int
       for (int kk = 0; kk < D / 32; ++kk)
         s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[u][kk]), qf[kk], s[u], 0, 0, 0);
     }
-    // scale to base 2, mask rows past the split end, block max
+    // scale to base 2, mask rows past the piece's end, block max
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -248,7 +248,7 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, char* lds, int
 #endif
   }
 
-  // combine the four waves of this split
+  // combine the four waves of this piece
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   __syncthreads();  // every wave is done with its V^ tile before the LDS is reused

@@ -18,11 +18,11 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 16;                            // dims per workgroup
-constexpr int kMergeGroups = kMergeThreads / kMergeDims;  // split groups per workgroup
+constexpr int kMergeGroups = kMergeThreads / kMergeDims;  // piece groups per workgroup
 
 // One workgroup per (sequence, query head, 16-dim chunk): many workgroups even
-// for one long sequence. The split maxima are reduced by the whole workgroup;
-// then 16 groups of 16 threads each sum a strided subset of the splits (with
+// for one long sequence. The pieces' maxima are reduced by the whole workgroup;
+// then 16 groups of 16 threads each sum a strided subset of the pieces (with
 // independent loads in flight), and the groups are added in LDS.
 template <int D, typename OutT>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams p) {
