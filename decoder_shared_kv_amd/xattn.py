@@ -202,6 +202,9 @@ def workspace_size(batch: int, q_heads: int, kv_heads: int, head_dim: int, dtype
 
 def decode_splits(batch: int, q_heads: int, kv_heads: int, head_dim: int, dtype: torch.dtype, max_kv_len: int,
                   total_kv_len: int = 0):
+    """(shares, rows per share) of the decode plan for these hints: every KV head
+    (bf16; query head for fp32) cuts the 128-row blocks of all sequences into
+    `shares` equal shares, one workgroup each."""
     lib = load_library()
     dims = make_dims(batch, q_heads, kv_heads, head_dim, dtype, 1.0)
     s, r = ctypes.c_int32(0), ctypes.c_int32(0)
@@ -223,7 +226,8 @@ def xattn_decode(cache: SharedKV, q: torch.Tensor, max_kv_len: int, scale: float
     """One query per sequence (q [B, Hq, d]) against the whole shared cache; returns out.
 
     max_kv_len / total_kv_len are the host-side sizing hints of the split plan
-    (the longest sequence's rows, all sequences' rows; 0 = B * max_kv_len)."""
+    (the longest sequence's rows, all sequences' rows; 0 = B * max_kv_len); the
+    kernels count the rows on the device, so wrong hints cost speed, not rows."""
     lib = load_library()
     batch, hq, _ = q.shape
     if out is None:
