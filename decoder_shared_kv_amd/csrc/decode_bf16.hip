@@ -29,11 +29,12 @@ namespace yoco {
 
 namespace {
 
-// Tuning knobs (measured on MI355X at 8 x 131072 and 1 x 1048576 rows): two
-// 16-key blocks per wave and iteration, no register double buffer (the freed
-// registers buy occupancy, which keeps more loads in flight), nontemporal loads.
+// Tuning knobs (measured on MI355X at 8 x 131072, 4 x 131072, 16 x 17292 and
+// 1 x 1048576 rows with the balanced split): one 16-key block per wave and
+// iteration (1-4% ahead of two, three and four blocks are slower still), no
+// register double buffer, nontemporal loads.
 #ifndef YOCO_DEC_U
-#define YOCO_DEC_U 2
+#define YOCO_DEC_U 1
 #endif
 #ifndef YOCO_DEC_PREFETCH
 #define YOCO_DEC_PREFETCH 0
