@@ -203,7 +203,8 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
 }
 
 // Wide tile (n_cols a multiple of 256): 256 rows x 256 columns per workgroup,
-// 32 k per stage through 4 stages (32 KB each), so each row block of X is read
+// 64 k per stage through 2 stages (64 KB each; 32 k through 4 stages measured
+// 5-7% slower: twice the barriers), so each row block of X is read
 // half as often as with 128 columns and every byte brought into LDS feeds
 // twice the MFMA work. The product is formed transposed, C^T = W' X^T (A = W'
 // rows, B = X rows), so a lane ends up with 4 consecutive output columns per
@@ -212,19 +213,23 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_kernel(ProjectParams 
 // 64 rows x 128 columns (2 x 4 MFMA blocks).
 constexpr int kWM = 256;
 constexpr int kWN = 256;
-constexpr int kWK = 32;
-constexpr int kWStages = 4;
-constexpr int kWXBytes = kWM * kWK * 2;     // 16 KB
-constexpr int kWWBytes = kWN * kWK * 2;     // 16 KB
+#ifndef YOCO_PROJ_WK
+#define YOCO_PROJ_WK 64
+#endif
+constexpr int kWK = YOCO_PROJ_WK;
+constexpr int kWStages = 128 / kWK;          // 128 KB of stages
+constexpr int kWCpr = kWK / 8;              // 16-byte chunks per tile row
+constexpr int kWXBytes = kWM * kWK * 2;
+constexpr int kWWBytes = kWN * kWK * 2;
 constexpr int kWStage = kWXBytes + kWWBytes;
-constexpr int kWXLoads = kWM * kWK / 8 / kPThreads;   // 2
-constexpr int kWWLoads = kWN * kWK / 8 / kPThreads;   // 2
+constexpr int kWXLoads = kWM * kWK / 8 / kPThreads;
+constexpr int kWWLoads = kWN * kWK / 8 / kPThreads;
 static_assert(kWStages * kWStage == kWM * kWN * 2, "the output tile is staged in the stages");
 
-// 16-byte chunk c (of 4) of row r of a [rows][32 k] tile: rows r and r + 4q fall
-// on different chunks within each 16 rows, so 16 lanes reading one chunk of 16
-// consecutive rows hit distinct banks
-__device__ __forceinline__ uint32_t swz32(int r, int c) { return (uint32_t)(r * 64 + 16 * (c ^ ((r >> 2) & 3))); }
+// XOR applied to the 16-byte chunks of tile row r so that 16 lanes reading one
+// chunk of 16 consecutive rows hit distinct banks (rows of 64 or 128 bytes)
+__device__ __forceinline__ int wswz(int r) { return kWK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+__device__ __forceinline__ uint32_t swz32(int r, int c) { return (uint32_t)(r * (kWK * 2) + 16 * (c ^ wswz(r))); }
 // 16-byte chunk c (of 32) of row r of the [256][256] bf16 output staging tile
 __device__ __forceinline__ uint32_t swz_out(int r, int c) { return (uint32_t)(r * 512 + 16 * (c ^ (r & 31))); }
 
@@ -272,22 +277,22 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_wide_kernel(ProjectPa
   // own still pending at the loop would make it wait for everything there)
   wait_vm_lgkm0<0>();
 
-  // this thread's chunks: chunk q = i * threads + tid -> tile row q / 4, slot q % 4
+  // this thread's chunks: chunk q = i * threads + tid -> tile row q / cpr, slot q % cpr
   uint32_t xoff[kWXLoads], woff[kWWLoads];
   const uint32_t wave_lds = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64 * 16;
 #pragma unroll
   for (int i = 0; i < kWXLoads; ++i) {
     const int q = i * kPThreads + tid;
-    int64_t row = m0 + q / 4;
+    int64_t row = m0 + q / kWCpr;
     if (row >= p.total_rows) row = p.total_rows - 1;     // rows past the end repeat the last one
-    const int c = (q % 4) ^ (((q / 4) >> 2) & 3);        // the chunk that belongs at this LDS slot
+    const int c = (q % kWCpr) ^ wswz(q / kWCpr);         // the chunk that belongs at this LDS slot
     xoff[i] = (uint32_t)((row - m0) * p.k_dim * 2 + c * 16);
   }
 #pragma unroll
   for (int i = 0; i < kWWLoads; ++i) {
     const int q = i * kPThreads + tid;
-    const int c = (q % 4) ^ (((q / 4) >> 2) & 3);
-    woff[i] = (uint32_t)((q / 4) * p.k_dim * 2 + c * 16);
+    const int c = (q % kWCpr) ^ wswz(q / kWCpr);
+    woff[i] = (uint32_t)((q / kWCpr) * p.k_dim * 2 + c * 16);
   }
   const char* xbase = static_cast<const char*>(p.x) + m0 * p.k_dim * 2;
   const char* wbase = static_cast<const char*>(p.w) + (int64_t)n0 * p.k_dim * 2;
@@ -320,8 +325,8 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_wide_kernel(ProjectPa
   for (int ks = 0; ks < k_steps; ++ks) {
     // stage ks is in when at most the stages requested after it are in flight
     const int ahead = min(kWStages - 2, k_steps - 1 - ks);
-    if (ahead >= 2) wait_vm_lgkm0<2 * L>();
-    else if (ahead == 1) wait_vm_lgkm0<L>();
+    if (kWStages >= 4 && ahead >= 2) wait_vm_lgkm0<(kWStages >= 4 ? 2 * L : 0)>();
+    else if (kWStages >= 3 && ahead >= 1) wait_vm_lgkm0<(kWStages >= 3 ? L : 0)>();
     else wait_vm_lgkm0<0>();
     barrier_only();   // stage ks is in for every thread; stage (ks - 1) % S is free
     if (ks + kWStages - 1 < k_steps) issue(ks + kWStages - 1);
@@ -348,10 +353,10 @@ __global__ __launch_bounds__(kPThreads, 1) void kv_project_wide_kernel(ProjectPa
           acc[tb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[kk][nb], xb[kk][tb], acc[tb][nb], 0, 0, 0);
     }
     // sum of squares of this lane's 8 values of row qr (k half hf); the two
-    // waves that read the same rows take one 16-k step each
+    // waves that read the same rows take half of the 16-k steps each
 #pragma unroll
     for (int kk = 0; kk < kWK / 16; ++kk) {
-      if (kk != wn) continue;   // wave-uniform; constant indices keep xb in registers
+      if ((2 * kk) / (kWK / 16) != wn) continue;   // wave-uniform; constant indices keep xb in registers
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
