@@ -1,0 +1,15 @@
+"""The round-end smoke check (__graft_entry__.smoke) runs as a GPU test too, so
+that a break in it shows up with the other GPU tests."""
+import os
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+
+def test_smoke():
+    import __graft_entry__
+    __graft_entry__.smoke()
