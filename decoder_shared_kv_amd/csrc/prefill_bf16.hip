@@ -25,6 +25,10 @@
 // side: K^ row r keeps chunk c at c ^ (r mod chunks-per-row), V^ row r at
 // c ^ v_swizzle(r mod 4); both make the reads bank-conflict-free.
 //
+// Softmax: online, with the running reference moved lazily (only when a row's
+// max passed it by a slack) and the max itself taken only when the weights
+// computed against the current reference could be too large (see sv_step).
+//
 // Pipeline: tile t + S - 1 is requested while tile t is computed, so a tile has
 // S - 1 tile-compute times to arrive. One workgroup barrier per tile. Within a
 // tile each wave keeps its LDS operand reads a few MFMAs ahead (scheduling
@@ -52,6 +56,7 @@ constexpr int kStages = YOCO_PREFILL_STAGES;
 
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kRescaleSlack = 8.0f;   // base-2 growth of the running max tolerated before a rescale
+constexpr float kWeightCap = 65536.0f;  // largest sum of one lane's half-tile weights taken without a max
 
 // Wait until at most `ahead` (< kStages - 1) tiles of L loads each are still in flight.
 template <int L>
@@ -175,7 +180,10 @@ __device__ __forceinline__ bf16x8 read_v(const YOCO_LDS char* vs, const ReadOffs
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-constexpr int kReadsAhead = 4;  // LDS operand reads kept in flight ahead of the MFMAs
+#ifndef YOCO_PREFILL_RA
+#define YOCO_PREFILL_RA 4
+#endif
+constexpr int kReadsAhead = YOCO_PREFILL_RA;  // LDS operand reads kept in flight ahead of the MFMAs
 
 // S^T = K^ Q^T of one 64-key tile for one wave (16 or 8 MFMAs, two chains).
 template <int D>
@@ -195,31 +203,41 @@ __device__ __forceinline__ void qk_step(const YOCO_LDS char* ks, const ReadOffs<
   }
 }
 
-// Online-softmax bookkeeping of one tile: mask, row max, lazy rescale of the
-// running state. Returns -m for the exponentials. MASK: 0 none, 1 keys past the
-// row's position (causal), 2 also keys before its window.
-template <int D, int MASK>
-__device__ __forceinline__ float softmax_max(f32x16 (&s)[2], f32x16 (&acc)[D / 32], float& m, float& l, int key0,
-                                             int pos, int window, float c, int hf) {
-  // register r of chain kb holds key key0 + 32kb + 8(r/4) + 4hf + r%4; keys past
-  // the row's (clamped) position pos, or before pos - window + 1, are masked:
-  // compares with constants per register
-  const int lim = pos - key0 - 4 * hf;
-  const int lim_lo = lim - window + 1;
-  float mx = -INFINITY;
+// Causal (MASK 1) and window (MASK 2) masks of a tile: register r of chain kb
+// holds key key0 + 32kb + 8(r/4) + 4hf + r%4; keys past the row's (clamped)
+// position pos, or before pos - window + 1, become -inf (compares with
+// constants per register).
+template <int MASK>
+__device__ __forceinline__ void apply_mask(f32x16 (&s)[2], int key0, int pos, int window, int hf) {
+  if constexpr (MASK != 0) {
+    const int lim = pos - key0 - 4 * hf;
+    const int lim_lo = lim - window + 1;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rel = kb * 32 + 8 * (r >> 2) + (r & 3);
-      if constexpr (MASK == 1) {
-        if (rel > lim) s[kb][r] = -INFINITY;
-      } else if constexpr (MASK == 2) {
-        if (rel > lim || rel < lim_lo) s[kb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int rel = kb * 32 + 8 * (r >> 2) + (r & 3);
+        if constexpr (MASK == 1) {
+          if (rel > lim) s[kb][r] = -INFINITY;
+        } else {
+          if (rel > lim || rel < lim_lo) s[kb][r] = -INFINITY;
+        }
       }
-      mx = fmaxf(mx, s[kb][r]);
     }
   }
+}
+
+// Row max over chains kb0..1 of a tile and the lazy rescale of the running
+// state: the reference m moves (and l, acc shrink by exp2(m - m_new)) only
+// where the row's max passed m + slack. Returns -m for the exponentials.
+template <int D>
+__device__ __forceinline__ float rescale_to_max(const f32x16 (&s)[2], int kb0, f32x16 (&acc)[D / 32], float& m,
+                                                float& l, float c) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = kb0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
   // lanes l and l ^ 32 hold the two key halves of one query row; the exchange
   // stays out of LDS, so it waits on none of the operand reads in flight
   mx = max_xor32(mx);
@@ -239,13 +257,14 @@ __device__ __forceinline__ float softmax_max(f32x16 (&s)[2], f32x16 (&acc)[D / 3
 }
 
 // P^T word w[kb][cc][i]: the weights of S^T registers 8cc + 2i and 8cc + 2i + 1
-// of chain kb, as two bf16; adds them (unrounded) to the row sum.
-__device__ __forceinline__ void softmax_word(const f32x16 (&s)[2], uint32_t (&w)[2][2][4], float& l, float c,
-                                             float neg_m, int kb, int cc, int i) {
+// of chain kb, as two bf16. Returns their unrounded fp32 sum (the row sum is
+// kept from unrounded weights, so the LSE stays fp32-accurate).
+__device__ __forceinline__ float softmax_word(const f32x16 (&s)[2], uint32_t (&w)[2][2][4], float c, float neg_m,
+                                              int kb, int cc, int i) {
   const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i], c, neg_m));
   const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * cc + 2 * i + 1], c, neg_m));
   w[kb][cc][i] = pack2(e0, e1);
-  l += e0 + e1;   // fp32 sum of the unrounded weights keeps the LSE fp32-accurate
+  return e0 + e1;
 }
 
 // PV step j of a tile: (kb, cc, t) with the dim tile t fastest, so consecutive
@@ -261,6 +280,17 @@ __device__ __forceinline__ void pv_index(int j, int& kb, int& cc, int& t) {
 // Softmax and O^T += V^T P^T of one tile whose S^T is in s. The exponentials
 // of keys 32..63 are spread between the PV MFMAs of keys 0..31, which run
 // while they issue.
+//
+// The weights of each 32-key half are first taken against the row's current
+// reference m, without a max. Their sum bounds every one of them, so where a
+// lane's half sums to at most kWeightCap every weight is at most that, well
+// inside fp32 and bf16 range; softmax does not depend on the reference. Only if
+// some lane's half sums to more (or to inf or NaN) does the wave take the row
+// max of the tile (or of its second half), move m where it grew past the slack,
+// and redo that half's exponentials; a wave with a row that has no reference
+// yet (m = -inf) takes the max at once. Either way the weights that reach the
+// MFMAs and the row sum use one m, and the running max itself is no longer
+// computed on most tiles (about 20 VALU instructions per tile and wave fewer).
 template <int D, int MASK>
 __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<D>& ro, f32x16 (&s)[2],
                                         f32x16 (&acc)[D / 32], float& m, float& l, int key0, int pos, int window,
@@ -276,17 +306,40 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
     va[j] = read_v<D>(vs, ro, kb, cc, t);
   }
   sched_fence();
-  const float neg_m = softmax_max<D, MASK>(s, acc, m, l, key0, pos, window, c, hf);
+  apply_mask<MASK>(s, key0, pos, window, hf);
   uint32_t w[2][2][4];
+  // a row without a reference yet (m = -inf: its first keys) takes the max first
+  bool exact = __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
+  float neg_m = -m;
+  float la;
+  for (;;) {   // at most twice: after a rescale the weights are taken as they are
+    if (exact) neg_m = rescale_to_max<D>(s, 0, acc, m, l, c);
+    la = 0.f;
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
+    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) softmax_word(s, w, l, c, neg_m, 0, cc, i);
+      for (int i = 0; i < 4; ++i) la += softmax_word(s, w, c, neg_m, 0, cc, i);
+    if (exact || __builtin_amdgcn_ballot_w64(!(la <= kWeightCap)) == 0) break;
+    exact = true;
+  }
+  l += la;
+  float lb = 0.f;
   sched_fence();
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     int kb, cc, t;
     pv_index<D>(j, kb, cc, t);
+    if (j == NV / 2) {
+      // the second half's weights are checked before its first MFMA
+      if (__builtin_amdgcn_ballot_w64(!(lb <= kWeightCap)) != 0) {
+        neg_m = rescale_to_max<D>(s, 1, acc, m, l, c);
+        lb = 0.f;
+#pragma unroll
+        for (int wi = 0; wi < 8; ++wi) lb += softmax_word(s, w, c, neg_m, 1, wi >> 2, wi & 3);
+      }
+      l += lb;
+      sched_fence();
+    }
     if (j + RA < NV) {
       int kb2, cc2, t2;
       pv_index<D>(j + RA, kb2, cc2, t2);
@@ -299,7 +352,7 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
 #pragma unroll
       for (int q = 0; q < 8 / (NV / 2); ++q) {
         const int wi = j * (8 / (NV / 2)) + q;
-        softmax_word(s, w, l, c, neg_m, 1, wi >> 2, wi & 3);
+        lb += softmax_word(s, w, c, neg_m, 1, wi >> 2, wi & 3);
       }
     }
     sched_fence();

@@ -46,6 +46,40 @@ def test_prefill_bf16(lens, hq, hkv, d, std, disc):
     say(f"  max-abs {e['max_abs']:.2e} row-rel {e['row_rel']:.2e}")
 
 
+# Key rows scaled up at chosen positions make the running row max jump in the
+# middle of a row: by a few units, by tens (past any bound on weights taken
+# against the old reference) and by hundreds (exp2 overflows there), in the first
+# (offset < 32) and in the second half of a 64-key tile, and at a tile's first
+# and last key.
+_JUMPS = {100: 4.0, 101: 4.0, 102: 4.0, 230: 16.0, 384: 8.0, 650: 30.0, 703: 100.0, 767: 60.0}
+
+
+def _with_jumps(c, jumps=_JUMPS):
+    k = c.k_pool.to(torch.float32)
+    for b in range(c.seq_start.numel()):
+        s0, n = int(c.seq_start[b]), int(c.seq_len[b])
+        for pos, f in jumps.items():
+            if pos < n:
+                k[s0 + pos] *= f
+    c.k_pool = k.to(c.k_pool.dtype)
+    return c
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,dtype", [
+    ((1000,), 8, 2, 128, "bf16"),
+    ((800, 720), 4, 1, 64, "bf16"),
+])
+def test_prefill_running_max_jumps(lens, hq, hkv, d, dtype):
+    say(f"prefill {dtype} with score jumps lens={lens} hq={hq} hkv={hkv} d={d}")
+    c = _with_jumps(synth.make_prefill_case(list(lens), hq, hkv, d, 1, dtype, seed=77 + d, std=1.0, cap_extra=3))
+    out, lse = run_prefill(c)
+    ref, ref_lse = _oracle_prefill(c)
+    assert np.isfinite(out).all()
+    e = parity.check(out, ref, dtype, discriminating=True, what="prefill out (jumps)")
+    parity.check_lse(lse, ref_lse, dtype, what="prefill lse (jumps)")
+    say(f"  max-abs {e['max_abs']:.2e} row-rel {e['row_rel']:.2e}")
+
+
 @pytest.mark.parametrize("lens,hq,hkv,d", [((256,), 4, 1, 64), ((100, 37), 8, 2, 128), ((70,), 4, 4, 64)])
 def test_prefill_f32(lens, hq, hkv, d):
     say(f"prefill f32 lens={lens} hq={hq} hkv={hkv} d={d}")

@@ -54,6 +54,23 @@ def test_window_prefill(lens, window, hq, hkv, d, dtype):
     say(f"  max-abs {e['max_abs']:.2e} row-rel {e['row_rel']:.2e}")
 
 
+@pytest.mark.parametrize("window", [100, 700])
+def test_window_prefill_running_max_jumps(window):
+    # key rows scaled up mid-tile: the row max jumps by units, tens and hundreds
+    # inside the band, and drops again once the scaled rows leave it
+    say(f"window prefill bf16 with score jumps C={window}")
+    c = synth.make_prefill_case([1000], 8, 2, 128, 1, "bf16", seed=5 + window, std=1.0, cap_extra=2)
+    k = c.k_pool.to(torch.float32)
+    for pos, f in {100: 4.0, 230: 16.0, 650: 30.0, 703: 100.0, 767: 60.0}.items():
+        k[int(c.seq_start[0]) + pos] *= f
+    c.k_pool = k.to(torch.bfloat16)
+    out, lse = run_prefill_window(c, window)
+    ref, ref_lse = ref_prefill(c, window)
+    assert np.isfinite(out).all()
+    parity.check(out, ref, "bf16", discriminating=True, what="window prefill (jumps)")
+    parity.check_lse(lse, ref_lse, "bf16", what="window prefill lse (jumps)")
+
+
 @pytest.mark.parametrize("lens,window,hq,hkv,d", [
     ((1000, 300, 64, 1, 0, 517), 64, 16, 4, 128),   # short, single-row and empty sequences
     ((5, 130, 64, 2000), 100, 8, 2, 128),
