@@ -648,18 +648,27 @@ def bench_ragged(args, torch, dk, synth, dev):
         dk.xattn_decode(cache, qd[0, 0], maxq + w.decode_steps, pc.scale, ws, out=outd, total_kv_len=sum(lens))
     torch.cuda.synchronize()
     nbytes = 0.0
+    # one event before each decode call and one after it: the call (split +
+    # merge) is timed apart from the step's append, which is its own entry point
+    ec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(w.decode_steps)]
     e[2].record()
     for s in range(w.decode_steps):
         dk.kv_append(cache, kn[s], vn[s], flag)
         lens = [x + 1 for x in lens]
+        ec[s][0].record()
         dk.xattn_decode(cache, qd[s, 0], maxq + w.decode_steps, pc.scale, ws, out=outd, total_kv_len=sum(lens))
+        ec[s][1].record()
         nbytes += decode_bytes(lens, w.kv_heads, w.q_heads, w.head_dim)
     e[3].record()
     torch.cuda.synchronize()
     dms = e[2].elapsed_time(e[3])
+    call_ms = [a.elapsed_time(b) for a, b in ec]
+    cms = sum(call_ms)
     assert int(flag.item()) == 0
     tfl = flops / (pre_ms / 1e3) / 1e12
-    gbs = nbytes / (dms / 1e3) / 1e9
+    gbs = nbytes / (cms / 1e3) / 1e9
+    gbs_step = nbytes / (dms / 1e3) / 1e9
     print(json.dumps({
         "metric": METRIC, "value": tfl, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": pre_ms + dms / w.decode_steps, "higher_is_better": True, "scaling": "weak",
@@ -668,7 +677,11 @@ def bench_ragged(args, torch, dk, synth, dev):
                    "global_batch": 16, "seq_len": maxq, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": tfl, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tfl / BF16_DENSE_PEAK_TFLOPS, "traffic": None, "avg_launch_ms": pre_ms},
-        "decode": {"value": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "avg_call_ms": dms / w.decode_steps}}),
+        "decode": {"value": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "avg_call_ms": cms / w.decode_steps,
+                   "what": "per decode call (split + merge launches), bytes of the call over its time",
+                   "call_median_ms": float(sorted(call_ms)[len(call_ms) // 2]), "call_min_ms": min(call_ms),
+                   "steps": {"GB/s": gbs_step, "frac": gbs_step / HBM_PEAK_GBS, "avg_step_ms": dms / w.decode_steps,
+                             "what": "append + decode call per step, bytes of the call over the step"}}}),
         flush=True)
 
 

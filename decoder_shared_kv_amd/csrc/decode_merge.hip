@@ -5,35 +5,54 @@
 // exp2(t - m_s) and its unnormalised weighted sum of V rows. The exact softmax
 // over all rows is then
 //   M = max_s m_s,  L = sum_s l_s exp2(m_s - M),  O = sum_s O_s exp2(m_s - M) / L,
-// and LSE = (M + log2 L) ln 2. The pieces of sequence b sit in consecutive
-// slots, which the split pass recorded (first slot, count); a sequence with no
-// rows gets O = 0 and LSE = -inf.
+// and LSE = (M + log2 L) ln 2. The pieces of sequence b sit in
+// consecutive slots, which the split pass recorded (first slot, count); a
+// sequence with no rows gets O = 0 and LSE = -inf.
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
+#include "tile_common.h"
 
 namespace yoco {
 
 namespace {
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeDims = 16;                            // dims per workgroup
-constexpr int kMergeGroups = kMergeThreads / kMergeDims;  // piece groups per workgroup
 
-// One workgroup per (sequence, query head, 16-dim chunk): many workgroups even
-// for one long sequence. The pieces' maxima are reduced by the whole workgroup;
-// then 16 groups of 16 threads each sum a strided subset of the pieces (with
-// independent loads in flight), and the groups are added in LDS.
-template <int D, typename OutT>
+// One workgroup per (sequence, query head, chunk of DW dims); threads hold V
+// dims each (V = 1 or 4), so a piece group has DW / V threads and the
+// workgroup 256 V / DW groups. The maxima of all pieces first (every thread
+// loads some, reduced across the workgroup), then group g's sums over pieces
+// g, g + G, ... against that max (the maxima again, from cache), added across
+// the groups in LDS. Few pieces per sequence (many
+// sequences): 64 dims, 4 per thread, fewer and fuller workgroups; many pieces
+// (few long sequences): 16 dims, 1 per thread, more workgroups.
+template <int V>
+struct MergeVec;
+template <>
+struct MergeVec<1> {
+  typedef float T;
+};
+template <>
+struct MergeVec<4> {
+  typedef f32x4 T;
+};
+
+template <int D, int DW, int V, typename OutT>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams p) {
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ float part_o[kMergeGroups][kMergeDims];
-  __shared__ float part_l[kMergeGroups];
+  typedef typename MergeVec<V>::T VecT;
+  constexpr int TPG = DW / V;                     // threads per piece group
+  constexpr int G = kMergeThreads / TPG;          // piece groups
+  static_assert(D % DW == 0 && kMergeThreads % TPG == 0, "dim chunks");
+  __shared__ __attribute__((aligned(16))) float red_o[G][DW];
+  __shared__ __attribute__((aligned(16))) float red_ml[G][2];
   const int bh = blockIdx.x;  // b * hq + h
   const int b = bh / p.hq;
   const int h = bh % p.hq;
-  const int d0 = blockIdx.y * kMergeDims;
+  const int d0 = blockIdx.y * DW;
   const int tid = threadIdx.x;
+  const int g = tid / TPG;
+  const int dl = V * (tid % TPG);   // first of this thread's dims within the chunk
   // the sequence's rows and where the split pass left its pieces (loaded together)
   int64_t start;
   const int32_t n = decode_rows(p, b, &start);
@@ -42,67 +61,80 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams 
   if (n == 0 || s0 < 0 || pieces < 1 || (int64_t)s0 + pieces > p.slots) pieces = 0;   // (stale when n == 0)
   const int64_t base = (int64_t)h * p.slots + (pieces > 0 ? s0 : 0);
   const float* ml = p.part_ml + 2 * base;
+  const float* po = p.part_o + base * D + d0 + dl;
 
-  float mx = -INFINITY;
-  for (int s = tid; s < pieces; s += kMergeThreads) mx = fmaxf(mx, ml[2 * s]);
+  // the sequence's max over all pieces, by every thread of the workgroup
+  float m = -INFINITY;
+  for (int s = tid; s < pieces; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) red_ml[tid >> 6][0] = m;
   __syncthreads();
-  float M = red[0];
+  float M = red_ml[0][0];
 #pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
-
-  const int g = tid / kMergeDims;
-  const int d = tid % kMergeDims;
-  float o = 0.f, lsum = 0.f;
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red_ml[w][0]);
+  // the weighted sums against it
+  float l = 0.f;
+  VecT o = {};
   if (M != -INFINITY) {
-    const float* po = p.part_o + base * D + d0 + d;
-#pragma unroll 8
-    for (int s = g; s < pieces; s += kMergeGroups) {
+#pragma unroll 4
+    for (int s = g; s < pieces; s += G) {
       const float ms = ml[2 * s];
       const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      lsum = fmaf(ml[2 * s + 1], w, lsum);
-      o = fmaf(po[(int64_t)s * D], w, o);
+      l = fmaf(ml[2 * s + 1], w, l);
+      o += *reinterpret_cast<const VecT*>(po + (int64_t)s * D) * w;
     }
   }
-  part_o[g][d] = o;
-  if (d == 0) part_l[g] = lsum;
+  if (tid % TPG == 0) red_ml[g][1] = l;
+  *reinterpret_cast<VecT*>(&red_o[g][dl]) = o;
   __syncthreads();
-  if (tid < kMergeDims) {
-    float os = 0.f, ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMergeGroups; ++i) {
-      os += part_o[i][tid];
-      ls += part_l[i];
+  if (tid < TPG) {
+    float L = 0.f;
+    VecT O = {};
+#pragma unroll 8
+    for (int i = 0; i < G; ++i) {
+      L += red_ml[i][1];
+      O += *reinterpret_cast<const VecT*>(&red_o[i][dl]);
     }
-    const float res = ls > 0.f ? os / ls : 0.f;
-    OutT* dst = static_cast<OutT*>(p.out) + (int64_t)bh * D + d0 + tid;
-    if constexpr (sizeof(OutT) == 2) {
-      *dst = __float2bfloat16(res);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    OutT* dst = static_cast<OutT*>(p.out) + (int64_t)bh * D + d0 + dl;
+    if constexpr (V == 4) {
+      if constexpr (sizeof(OutT) == 2) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(O[0] * inv, O[1] * inv), pack2(O[2] * inv, O[3] * inv));
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = O * inv;
+      }
     } else {
-      *dst = res;
+      if constexpr (sizeof(OutT) == 2) {
+        *dst = __float2bfloat16(O * inv);
+      } else {
+        *dst = O * inv;
+      }
     }
     if (tid == 0 && blockIdx.y == 0 && p.lse != nullptr)
-      p.lse[bh] = ls > 0.f ? (M + log2f(ls)) * 0.6931471805599453f : -INFINITY;
+      p.lse[bh] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
   }
+}
+
+template <int D, typename OutT>
+void launch_merge_d(const AttnParams& p, hipStream_t stream) {
+  const bool many = p.splits >= 32 * p.batch;   // pieces per sequence, roughly
+  const dim3 block(kMergeThreads);
+  if (many)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 16, 1, OutT>), dim3(p.batch * p.hq, D / 16), block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, 64, 4, OutT>), dim3(p.batch * p.hq, D / 64), block, 0, stream, p);
 }
 
 }  // namespace
 
 hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.batch * p.hq), (unsigned)(head_dim / kMergeDims));
-  const dim3 block(kMergeThreads);
   if (dtype == 1) {
-    if (head_dim == 64)
-      hipLaunchKernelGGL((decode_merge_kernel<64, __hip_bfloat16>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<128, __hip_bfloat16>), grid, block, 0, stream, p);
+    if (head_dim == 64) launch_merge_d<64, __hip_bfloat16>(p, stream);
+    else launch_merge_d<128, __hip_bfloat16>(p, stream);
   } else {
-    if (head_dim == 64)
-      hipLaunchKernelGGL((decode_merge_kernel<64, float>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<128, float>), grid, block, 0, stream, p);
+    if (head_dim == 64) launch_merge_d<64, float>(p, stream);
+    else launch_merge_d<128, float>(p, stream);
   }
   return hipGetLastError();
 }
