@@ -9,7 +9,9 @@
 //    any mix of lengths; it reads each cache row of its share exactly once, for
 //    ALL query heads of the KV group (<= 16 per workgroup), so GQA costs no
 //    extra traffic;
-//  * K^ rows go straight from HBM into MFMA A operands (16 B per lane, no LDS):
+//  * K^ rows go from HBM into MFMA A operands (16 B per lane), straight into
+//    their operand layout or, with four or more KV heads, as whole rows
+//    rearranged through a wave-private LDS tile:
 //    S^T[key][head] = K^ . Q^T with v_mfma_f32_16x16x32_bf16, query heads padded
 //    to 16 columns;
 //  * the accumulator layout of S^T (lane = head, 4 consecutive keys per lane)
@@ -69,24 +71,51 @@ constexpr int kVtStride = 20;  // 16 keys + 4 pad (bf16 elements) per transposed
 __device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
 
-// Per-lane register tile of one iteration: U blocks of 16 keys.
+// Per-lane register tile of one iteration: U blocks of 16 keys. K^ and V^ are
+// loaded alike, whole rows per instruction (16 lanes x D/16 dims cover one
+// row, the 4 lane groups 4 consecutive rows): a probe of this load against
+// the MFMA operand layout (64 bytes of each of 16 rows per instruction)
+// measured 6.6-7.0 TB/s against 5.5-6.0. Both are then rearranged through a
+// small wave-private LDS tile.
+//
+// Whole-row K^ loads pay an LDS round trip per block; they win with four or
+// more KV heads (rows of one head 1 KB or more apart: +2-5%) and lose ~3% at
+// two (1M rows, 16 x 2 heads), so KR = 1 is used from four KV heads on and the
+// MFMA-layout loads (kd) below that.
 template <int D, int U>
 struct DecRegs {
-  uint4 k[U][D / 32];       // A operand of S^T: key (lane & 15), 8 dims at 32*kk + 8*(lane >> 4)
-  uint32_t v[U][4][D / 32]; // 4 consecutive keys x D/16 dims (as D/32 dwords) for the V^ transpose
+  uint4 kd[U][D / 32];      // KR = 0: A operand of S^T, key (lane & 15), 8 dims at 32*kk + 8*(lane >> 4)
+  uint32_t k[U][4][D / 32]; // KR = 1: keys 4*(lane >> 4) + i, dims (lane & 15) * D/16 .. +D/16 (as D/32 dwords)
+  uint32_t v[U][4][D / 32]; // V^, whole rows as for KR = 1
 };
 
-template <int D, int U>
+template <int D, int U, int KR>
 __device__ __forceinline__ void dec_load(DecRegs<D, U>& r, const __bf16* kbase, const __bf16* vbase,
                                          int64_t row_stride, int base, int last, int lane) {
   const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    int key = base + 16 * u + col;
-    key = key < last ? key : last;
-    const __bf16* src = kbase + (int64_t)key * row_stride + 8 * grp;
+    if constexpr (KR) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) r.k[u][kk] = stream_load16(src + 32 * kk);
+      for (int i = 0; i < 4; ++i) {
+        int kkey = base + 16 * u + 4 * grp + i;
+        kkey = kkey < last ? kkey : last;
+        const int64_t off = (int64_t)kkey * row_stride + col * (D / 16);
+        if constexpr (D == 128) {
+          const uint4 x = stream_load16(kbase + off);
+          r.k[u][i][0] = x.x; r.k[u][i][1] = x.y; r.k[u][i][2] = x.z; r.k[u][i][3] = x.w;
+        } else {
+          const uint2 x = stream_load8(kbase + off);
+          r.k[u][i][0] = x.x; r.k[u][i][1] = x.y;
+        }
+      }
+    } else {
+      int key = base + 16 * u + col;
+      key = key < last ? key : last;
+      const __bf16* src = kbase + (int64_t)key * row_stride + 8 * grp;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) r.kd[u][kk] = stream_load16(src + 32 * kk);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int vkey = base + 16 * u + 4 * grp + i;
@@ -104,17 +133,26 @@ __device__ __forceinline__ void dec_load(DecRegs<D, U>& r, const __bf16* kbase, 
 }
 
 // LDS: per-wave transposed V^ tiles; reused for the cross-wave combine at the end
-template <int D, int U>
+template <int D, int U, int KR>
 struct DecLds {
   static constexpr int kVtBytes = kDecWaves * U * D * kVtStride * 2;
+  static constexpr int kKtBytes = KR ? kDecWaves * U * 16 * D * 2 : 0;   // row-major K^ blocks, after the V^T tiles
   static constexpr int kCombBytes = kDecWaves * 16 * (D + 2) * 4;
-  static constexpr int kBytes = kVtBytes > kCombBytes ? kVtBytes : kCombBytes;
+  static constexpr int kBytes = kVtBytes + kKtBytes > kCombBytes ? kVtBytes + kKtBytes : kCombBytes;
 };
+
+// K^ block in LDS: 16 rows of D/8 16-byte chunks, chunk c of row r stored at
+// c ^ (r mod D/8), so that both the whole-row writes and the operand reads
+// (16 rows x 4 chunks per instruction) spread over all banks.
+template <int D>
+__device__ __forceinline__ int kt_chunk(int r, int c) {
+  return c ^ (r & (D / 8 - 1));
+}
 
 // Rows j0 .. j1-1 of sequence b (cache rows from `start`), all query heads of
 // KV head kh's chunk hc: leaves the partial (m, l, O) of every head in its
 // slot (h * p.slots + slot).
-template <int D, int U>
+template <int D, int U, int KR>
 __device__ __forceinline__ void decode_piece(const AttnParams& p, char* lds, int b, int64_t start, int j0, int j1,
                                              int kh, int hc, int slot) {
   const int lane = threadIdx.x & 63;
@@ -122,6 +160,7 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, char* lds, int
   const int col = lane & 15;
   const int grp = lane >> 4;
   __bf16* vt = reinterpret_cast<__bf16*>(lds) + wave * (U * D * kVtStride);
+  char* kt = lds + DecLds<D, U, KR>::kVtBytes + wave * (U * 16 * D * 2);
 
   const int h0 = kh * p.group + hc * 16;
   const int nh = p.group - hc * 16 < 16 ? p.group - hc * 16 : 16;
@@ -153,25 +192,59 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, char* lds, int
   int base = j0 + wave * U * 16;
   DecRegs<D, U> cur;
 #if YOCO_DEC_PREFETCH
-  if (base < j1) dec_load<D, U>(cur, kbase, vbase, row_stride, base, j1 - 1, lane);
+  if (base < j1) dec_load<D, U, KR>(cur, kbase, vbase, row_stride, base, j1 - 1, lane);
 #endif
   for (; base < j1; base += kStep) {
 #if YOCO_DEC_PREFETCH
     DecRegs<D, U> nxt;
     const bool more = base + kStep < j1;
-    if (more) dec_load<D, U>(nxt, kbase, vbase, row_stride, base + kStep, j1 - 1, lane);
+    if (more) dec_load<D, U, KR>(nxt, kbase, vbase, row_stride, base + kStep, j1 - 1, lane);
 #else
-    dec_load<D, U>(cur, kbase, vbase, row_stride, base, j1 - 1, lane);
+    dec_load<D, U, KR>(cur, kbase, vbase, row_stride, base, j1 - 1, lane);
 #endif
 
     // S^T = K^ . Q^T, 16 keys x 16 heads per block
     f32x4 s[U];
+    if constexpr (KR) {
+      // K^ block -> wave-private LDS (row-major, swizzled chunks), then back as
+      // the A operand: key (lane & 15), 8 dims at 32*kk + 8*(lane >> 4)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[u][kk]), qf[kk], s[u], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * grp + i;
+          char* row = kt + (u * 16 + r) * (D * 2);
+          if constexpr (D == 128) {
+            *reinterpret_cast<uint4*>(row + 16 * kt_chunk<D>(r, col)) =
+                make_uint4(cur.k[u][i][0], cur.k[u][i][1], cur.k[u][i][2], cur.k[u][i][3]);
+          } else {
+            *reinterpret_cast<uint2*>(row + 16 * kt_chunk<D>(r, col >> 1) + 8 * (col & 1)) =
+                make_uint2(cur.k[u][i][0], cur.k[u][i][1]);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* row = kt + (u * 16 + col) * (D * 2);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+          const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * kt_chunk<D>(col, 4 * kk + grp));
+          s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], s[u], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+          s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.kd[u][kk]), qf[kk], s[u], 0,
+                                                         0, 0);
+      }
     }
     // scale to base 2, mask rows past the piece's end, block max
     float mx = -INFINITY;
@@ -313,9 +386,9 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, char* lds, int
 // several sequences: each piece of it leaves its own partial, in slot
 // share + sequence (distinct for every piece of a column). The workgroup that
 // holds a sequence's first block records where its pieces are for the merge.
-template <int D, int U>
+template <int D, int U, int KR>
 __global__ __launch_bounds__(256, YOCO_DEC_OCC) void decode_split_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[DecLds<D, U>::kBytes];
+  __shared__ __attribute__((aligned(16))) char lds[DecLds<D, U, KR>::kBytes];
   const int share = blockIdx.x;
   const int kh = blockIdx.y / p.head_chunks;
   const int hc = blockIdx.y % p.head_chunks;
@@ -378,7 +451,7 @@ __global__ __launch_bounds__(256, YOCO_DEC_OCC) void decode_split_bf16_kernel(At
         p.decode_meta[2 * b + 1] = (int32_t)(s_last - share + 1);
       }
       const int j1 = hi * kDecodeBlockRows < n_kv ? (int)(hi * kDecodeBlockRows) : n_kv;
-      decode_piece<D, U>(p, lds, b, start, (int)(lo * kDecodeBlockRows), j1, kh, hc, share + b);
+      decode_piece<D, U, KR>(p, lds, b, start, (int)(lo * kDecodeBlockRows), j1, kh, hc, share + b);
       __syncthreads();  // the combine's LDS reads are done before the next piece's tiles
     }
     pre += u;
@@ -389,10 +462,14 @@ __global__ __launch_bounds__(256, YOCO_DEC_OCC) void decode_split_bf16_kernel(At
 
 hipError_t launch_decode_split_bf16(const AttnParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid((unsigned)p.splits, (unsigned)(p.hkv * p.head_chunks));
-  if (head_dim == 64)
-    hipLaunchKernelGGL((decode_split_bf16_kernel<64, YOCO_DEC_U>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_split_bf16_kernel<128, YOCO_DEC_U>), grid, dim3(256), 0, stream, p);
+  const bool krow = p.hkv >= 4;
+  if (head_dim == 64) {
+    if (krow) hipLaunchKernelGGL((decode_split_bf16_kernel<64, YOCO_DEC_U, 1>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_bf16_kernel<64, YOCO_DEC_U, 0>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (krow) hipLaunchKernelGGL((decode_split_bf16_kernel<128, YOCO_DEC_U, 1>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_bf16_kernel<128, YOCO_DEC_U, 0>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
