@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
           float pv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float d = exp2f(Aj - am[e]);
+            const float d = __builtin_amdgcn_exp2f(Aj - am[e]);   // below 2^-126: 0 or denormal, as the product vanishes
             pv[e] = (m0 + e <= j_row) ? s[kb][4 * g4 + e] * d : 0.f;
           }
           w[kb][g4 >> 1][2 * (g4 & 1)] = pack2(pv[0], pv[1]);
