@@ -281,9 +281,9 @@ def main():
         res["decode"] = {"value": gbs, "unit": "GB/s", "avg_call_ms": call_s * 1e3,
                          "algorithmic_bytes_per_call": dec_bytes / calls,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": gbs / HBM_PEAK_GBS, **traffic_fields("decode_split_bf16_kernel<128, 1>",
+                                      "frac": gbs / HBM_PEAK_GBS, **traffic_fields("decode_split_bf16_kernel<128, 1, 0>",
                                                                                     call_s),
-                                      "kernel": "decode_split_bf16_kernel<128, 1> + decode_merge_kernel "
+                                      "kernel": "decode_split_bf16_kernel<128, 1, 0> + decode_merge_kernel "
                                                 "(one call: both launches, timed together)"},
                          "steps": {**spread(dec_steps), "what": f"one append and {wd.layers} layer calls per step"},
                          "calls": call_stats(
@@ -364,7 +364,7 @@ def bench_decode_1m(args, torch, dk, synth, dev):
         "config": {"workload": "decode: B=1 N=1048576 (+64 appends) Hq=16 Hkv=2 d=128, 64 steps x 16 layers",
                    "global_batch": 1, "seq_len": 1048576, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "kernel": "decode_split_bf16_kernel<128, 1> + decode_merge_kernel",
+                     "traffic": None, "kernel": "decode_split_bf16_kernel<128, 1, 0> + decode_merge_kernel",
                      "avg_call_ms": ms / calls, "algorithmic_bytes_per_call": nbytes / calls},
         "total_ms": ms}), flush=True)
 

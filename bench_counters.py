@@ -32,8 +32,8 @@ OUT = os.path.join(ROOT, "gpurun_out", "counters")
 # kernel name prefix -> source files whose hash identifies it
 KERNELS = {
     "prefill_bf16_kernel<128>": ["prefill_bf16.hip", "internal.h", "lds_copy.h", "tile_common.h"],
-    "decode_split_bf16_kernel<128, 1>": ["decode_bf16.hip", "internal.h", "tile_common.h"],
-    "decode_merge_kernel<128, __hip_bfloat16>": ["decode_merge.hip", "internal.h"],
+    "decode_split_bf16_kernel<128, 1, 0>": ["decode_bf16.hip", "internal.h", "tile_common.h"],
+    "decode_merge_kernel<128, 16, 1, __hip_bfloat16>": ["decode_merge.hip", "internal.h", "tile_common.h"],
 }
 
 RUNS = {
