@@ -102,6 +102,9 @@ def test_prefill_f32(lens, hq, hkv, d):
     ((3000, 17), 16, 2, 128, "bf16", 128 ** -0.5),
     ((255, 40), 4, 1, 64, "f32", 1.0),
     ((1000,), 8, 2, 128, "f32", 1.0),
+    ((20000,), 8, 1, 64, "bf16", 1.0),           # one long sequence: many pieces per sequence in the merge
+    ((20000,), 8, 2, 128, "f32", 1.0),           # the same for fp32 storage
+    ((3000, 2500), 32, 8, 64, "bf16", 1.0),      # eight KV heads (whole-row K^ loads), head_dim 64
 ])
 def test_decode(lens, hq, hkv, d, dtype, std):
     say(f"decode {dtype} lens={lens} hq={hq} hkv={hkv} d={d} std={std}")
