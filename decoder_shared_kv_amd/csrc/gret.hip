@@ -440,43 +440,60 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// decode: one recurrent step per (sequence, head)
+// decode: one recurrent step, S <- g S + k^T v and o = q S (fp32 state)
 // ---------------------------------------------------------------------------
+// A workgroup owns 32 state columns (dv) of one (sequence, head): 8 lanes of 4
+// columns cover the block's 128 bytes of a state row, and 32 row groups take
+// every 32nd dk row from their own. Each thread issues all of its state loads
+// before using any, so the step costs about one memory round trip; the row
+// groups' partial outputs are added in LDS.
+constexpr int kDecCols = 32;                       // state columns per workgroup
+constexpr int kDecGroups = 256 / (kDecCols / 4);   // row groups
+
 template <int D>
 __global__ __launch_bounds__(256) void gret_decode_kernel(GretParams p) {
-  constexpr int kParts = 256 / D;                 // threads per state column
-  constexpr int kRows = D / kParts;               // dk rows per thread
-  __shared__ float qk[2][D];
-  __shared__ float part[kParts][D];
-  const int h = blockIdx.x, b = blockIdx.y;
+  constexpr int kRows = D / kDecGroups;            // dk rows per thread
+  __shared__ f32x4 part[kDecGroups][kDecCols / 4];
+  const int cb = blockIdx.x % (D / kDecCols);
+  const int h = blockIdx.x / (D / kDecCols), b = blockIdx.y;
   const int64_t bh = (int64_t)b * p.heads + h;
   const int tid = threadIdx.x;
+  const int c4 = tid & 7, grp = tid >> 3;
+  const int col = cb * kDecCols + 4 * c4;
   const __bf16* q = static_cast<const __bf16*>(p.q) + bh * D;
   const __bf16* k = static_cast<const __bf16*>(p.k) + bh * D;
   const __bf16* v = static_cast<const __bf16*>(p.v) + bh * D;
-  if (tid < D) {
-    qk[0][tid] = (float)q[tid];
-    qk[1][tid] = (float)k[tid];
-  }
-  __syncthreads();
-  const int col = tid % D, part_i = tid / D;
-  const float g = p.gamma[bh];
-  const float vv = (float)v[col];
-  float* st = p.state_out + bh * D * D;
-  float o = 0.f;
-#pragma unroll 8
-  for (int i = part_i * kRows; i < (part_i + 1) * kRows; ++i) {
-    const float s = fmaf(g, st[i * D + col], qk[1][i] * vv);
-    st[i * D + col] = s;
-    o = fmaf(qk[0][i], s, o);
-  }
-  part[part_i][col] = o;
-  __syncthreads();
-  if (tid < D) {
-    float sum = 0.f;
+  float* st = p.state_out + bh * D * D + col;
+  f32x4 s[kRows];
+  float qi[kRows], ki[kRows];
 #pragma unroll
-    for (int i = 0; i < kParts; ++i) sum += part[i][tid];
-    static_cast<__bf16*>(p.out)[bh * D + tid] = (__bf16)sum;
+  for (int r = 0; r < kRows; ++r) {
+    const int i = grp + kDecGroups * r;
+    s[r] = *reinterpret_cast<const f32x4*>(st + (int64_t)i * D);
+    qi[r] = (float)q[i];
+    ki[r] = (float)k[i];
+  }
+  const float g = p.gamma[bh];
+  float vv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = (float)v[col + e];
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[r][e] = fmaf(g, s[r][e], ki[r] * vv[e]);
+      o[e] = fmaf(qi[r], s[r][e], o[e]);
+    }
+    *reinterpret_cast<f32x4*>(st + (int64_t)(grp + kDecGroups * r) * D) = s[r];
+  }
+  part[grp][c4] = o;
+  __syncthreads();
+  if (tid < kDecCols) {
+    float sum = 0.f;
+#pragma unroll 8
+    for (int g2 = 0; g2 < kDecGroups; ++g2) sum += part[g2][tid >> 2][tid & 3];
+    static_cast<__bf16*>(p.out)[bh * D + cb * kDecCols + tid] = (__bf16)sum;
   }
 }
 
@@ -498,7 +515,7 @@ hipError_t launch_gret_prefill(const GretParams& p, int head_dim, hipStream_t st
 }
 
 hipError_t launch_gret_decode(const GretParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.heads, p.batch);
+  const dim3 grid((unsigned)(p.heads * (head_dim / kDecCols)), (unsigned)p.batch);
   if (head_dim == 64)
     hipLaunchKernelGGL(gret_decode_kernel<64>, grid, dim3(256), 0, stream, p);
   else

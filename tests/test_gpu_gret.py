@@ -90,6 +90,31 @@ def test_gret_decode_steps():
         assert err <= 1e-5, f"decode state step {step}: {err:.2e}"   # the step is fp32 throughout
 
 
+@pytest.mark.parametrize("batch,heads,d", [
+    (8, 16, 128),    # the decode benchmark's shape
+    (5, 3, 64),      # head_dim 64
+    (1, 1, 128),
+])
+def test_gret_decode_shapes(batch, heads, d):
+    say(f"gret decode B={batch} H={heads} d={d}: two steps from a random state")
+    g = torch.Generator().manual_seed(batch * 100 + heads + d)
+    st0 = torch.randn(batch, heads, d, d, generator=g) * 0.3
+    state = st0.to(DEV)
+    cur = st0.double().numpy()
+    for step in range(2):
+        qd = (torch.randn(batch, heads, d, generator=g) * d ** -0.25).to(torch.bfloat16)
+        kd = (torch.randn(batch, heads, d, generator=g) * d ** -0.25).to(torch.bfloat16)
+        vd = torch.randn(batch, heads, d, generator=g).to(torch.bfloat16)
+        gd = (0.5 + 0.5 * torch.rand(batch, heads, generator=g)).float()
+        out = dk.gret_decode(qd.to(DEV), kd.to(DEV), vd.to(DEV), gd.to(DEV), state)
+        torch.cuda.synchronize()
+        ref, cur = oracle.gret_decode_ref(synth.to_f64(qd), synth.to_f64(kd), synth.to_f64(vd), gd.double().numpy(),
+                                          cur)
+        parity.check(f64(out), ref, "bf16", discriminating=True, what=f"gret decode step {step}")
+        err = np.abs(state.cpu().numpy() - cur).max() / np.abs(cur).max()
+        assert err <= 1e-5, f"decode state step {step}: {err:.2e}"   # the step is fp32 throughout
+
+
 def test_gret_prefill_then_decode_equals_longer_prefill():
     """Decode of row n from the state after rows 0..n-1 = row n of the prefill of n + 1 rows."""
     lens, heads, d = [513], 2, 128
