@@ -18,13 +18,15 @@ namespace yoco {
 namespace {
 
 constexpr int kMergeThreads = 256;
+constexpr int kRegPieces = 4;   // pieces per thread group held in registers
 
 // One workgroup per (sequence, query head, chunk of DW dims); threads hold V
 // dims each (V = 1 or 4), so a piece group has DW / V threads and the
-// workgroup 256 V / DW groups. The maxima of all pieces first (every thread
-// loads some, reduced across the workgroup), then group g's sums over pieces
-// g, g + G, ... against that max (the maxima again, from cache), added across
-// the groups in LDS. Few pieces per sequence (many
+// workgroup 256 V / DW groups. Group g sums pieces g, g + G, ... against the
+// max over all pieces (reduced across the workgroup); its first pieces are
+// loaded together with their maxima, so a sequence with up to 4 G pieces
+// costs one round of loads after its slot record. The groups' sums are added
+// in LDS. Few pieces per sequence (many
 // sequences): 64 dims, 4 per thread, fewer and fuller workgroups; many pieces
 // (few long sequences): 16 dims, 1 per thread, more workgroups.
 template <int V>
@@ -63,9 +65,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams 
   const float* ml = p.part_ml + 2 * base;
   const float* po = p.part_o + base * D + d0 + dl;
 
-  // the sequence's max over all pieces, by every thread of the workgroup
+  // group g's first kRegPieces pieces (g, g + G, ...) go into registers with
+  // their maxima in one round of loads; the maxima of any further pieces are
+  // read by every thread of the workgroup. The workgroup's max over both is the
+  // sequence's max M.
+  float ms_r[kRegPieces], ls_r[kRegPieces];
+  VecT o_r[kRegPieces];
   float m = -INFINITY;
-  for (int s = tid; s < pieces; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
+#pragma unroll
+  for (int i = 0; i < kRegPieces; ++i) {
+    const int s = g + G * i;
+    ms_r[i] = -INFINITY;
+    ls_r[i] = 0.f;
+    o_r[i] = VecT{};
+    if (s < pieces) {
+      ms_r[i] = ml[2 * s];
+      ls_r[i] = ml[2 * s + 1];
+      o_r[i] = *reinterpret_cast<const VecT*>(po + (int64_t)s * D);
+    }
+    m = fmaxf(m, ms_r[i]);
+  }
+  for (int s = G * kRegPieces + tid; s < pieces; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   if ((tid & 63) == 0) red_ml[tid >> 6][0] = m;
@@ -73,12 +93,18 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(AttnParams 
   float M = red_ml[0][0];
 #pragma unroll
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red_ml[w][0]);
-  // the weighted sums against it
+  // the weighted sums against it, in piece order
   float l = 0.f;
   VecT o = {};
   if (M != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < kRegPieces; ++i) {
+      const float w = ms_r[i] == -INFINITY ? 0.f : exp2f(ms_r[i] - M);
+      l = fmaf(ls_r[i], w, l);
+      o += o_r[i] * w;
+    }
 #pragma unroll 4
-    for (int s = g; s < pieces; s += G) {
+    for (int s = g + G * kRegPieces; s < pieces; s += G) {
       const float ms = ml[2 * s];
       const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
       l = fmaf(ml[2 * s + 1], w, l);

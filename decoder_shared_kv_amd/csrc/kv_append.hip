@@ -11,6 +11,17 @@ namespace yoco {
 
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int b = blockIdx.x;
+  const int n16 = p.row_bytes / 16;
+  const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(p.k_new) + (int64_t)b * p.row_bytes);
+  const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(p.v_new) + (int64_t)b * p.row_bytes);
+  // the first 16-byte pieces of the new rows are requested together with the
+  // sequence's record (they do not depend on it)
+  const int i0 = threadIdx.x;
+  uint4 k0 = make_uint4(0, 0, 0, 0), v0 = make_uint4(0, 0, 0, 0);
+  if (i0 < n16) {
+    k0 = ks[i0];
+    v0 = vs[i0];
+  }
   const int64_t start = p.seq_start[b];
   const int32_t len = p.seq_len[b];
   const int32_t cap = p.seq_cap[b];
@@ -23,12 +34,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     return;
   }
   const int64_t row = start + slot;
-  const int n16 = p.row_bytes / 16;
-  const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(p.k_new) + (int64_t)b * p.row_bytes);
-  const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(p.v_new) + (int64_t)b * p.row_bytes);
   uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(p.k) + row * p.row_bytes);
   uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(p.v) + row * p.row_bytes);
-  for (int i = threadIdx.x; i < n16; i += blockDim.x) {
+  if (i0 < n16) {
+    kd[i0] = k0;
+    vd[i0] = v0;
+  }
+  for (int i = i0 + (int)blockDim.x; i < n16; i += blockDim.x) {
     kd[i] = ks[i];
     vd[i] = vs[i];
   }

@@ -175,10 +175,15 @@ def test_decode_balanced_shares(lens, hints, dtype):
 # --------------------------------------------------------------------------- append
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_append_writes_row_and_flags_overflow(dtype):
-    say(f"kv_append {dtype}")
-    c = synth.make_decode_case([5, 9, 2], 8, 2, 64, 1, 1, dtype, seed=11, std=1.0)
+@pytest.mark.parametrize("dtype,hkv,d", [
+    ("bf16", 2, 64),
+    ("f32", 2, 64),
+    ("bf16", 16, 128),   # 4 KB rows: one 16-byte piece per thread
+    ("f32", 24, 128),    # 12 KB rows: three pieces per thread
+])
+def test_append_writes_row_and_flags_overflow(dtype, hkv, d):
+    say(f"kv_append {dtype} hkv={hkv} d={d}")
+    c = synth.make_decode_case([5, 9, 2], 4 * hkv if hkv < 8 else hkv, hkv, d, 1, 1, dtype, seed=11 + hkv, std=1.0)
     cap = c.seq_cap.clone()
     cap[1] = 9   # sequence 1 is full
     cache = device_cache(c.k_pool, c.v_pool, c.seq_start, c.seq_len, cap)
