@@ -253,3 +253,19 @@ def test_split_plan_counts_all_rows():
     assert s * 8 == 1024 and r == -(-blocks // s) * 128, (s, r)
     s0, r0 = dk.decode_splits(16, 32, 8, 128, torch.bfloat16, max(lens), 0)
     assert s0 == s and r0 > r
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library the binding raises; there is no other path to fall back on."""
+    import subprocess
+    import sys
+    code = ("import decoder_shared_kv_amd.xattn as x\n"
+            "try:\n"
+            "    x.load_library('/nonexistent/libyoco_xattn.so')\n"
+            "except OSError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('loaded')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "is not built" in r.stdout
