@@ -1,7 +1,7 @@
 """HBM traffic of the benchmark's kernels from rocprofv3 counters.
 
-`python bench_counters.py collect` (on a GPU machine) runs, each in a process
-of its own under rocprofv3:
+`python bench_counters.py collect <dir>` (on a GPU machine) runs, each in a
+process of its own under rocprofv3, with its raw output under <dir>:
   * FETCH_SIZE, then WRITE_SIZE, of `bench.py --skip decode` (the prefill kernel)
     and of `bench.py --skip prefill` (the decode kernels);
   * the same two counters of `bench.py --copy-probe` (a plain 1 GiB device copy),
@@ -27,7 +27,6 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "decoder_shared_kv_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-OUT = os.path.join(ROOT, "gpurun_out", "counters")
 
 # kernel name prefix -> source files whose hash identifies it
 KERNELS = {
@@ -52,18 +51,19 @@ def source_hash(files):
     return h.hexdigest()
 
 
-def command(run, counter):
-    d = os.path.join(OUT, f"{run}_{counter}")
+def command(run, counter, out):
+    d = os.path.join(out, f"{run}_{counter}")
     return ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", d, "-o", "run", "--",
             sys.executable, os.path.join(ROOT, "bench.py"), *RUNS[run]], d
 
 
-def collect():
-    os.makedirs(OUT, exist_ok=True)
+def collect(out):
+    out = os.path.abspath(out)
+    os.makedirs(out, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp")
     for run in RUNS:
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            cmd, d = command(run, counter)
+            cmd, d = command(run, counter, out)
             print(f"[counters] {run} {counter}", flush=True)
             t = time.time()
             r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=240)
@@ -71,7 +71,7 @@ def collect():
                 print(r.stdout[-2000:], r.stderr[-2000:], file=sys.stderr)
                 raise SystemExit(f"rocprofv3 failed for {run} {counter}")
             print(f"[counters]   done in {time.time() - t:.0f} s", flush=True)
-    summarize(OUT)
+    summarize(out)
 
 
 def _per_kernel(path, counter):
@@ -113,7 +113,7 @@ def summarize(src_dir):
     with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
         json.dump(result, f, indent=1)
     lines = ["HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE; one counter per run)",
-             "command: python bench_counters.py collect   (runs, per counter and workload:",
+             "command: python bench_counters.py collect <dir>   (runs, per counter and workload:",
              "  rocprofv3 --pmc <COUNTER> --output-format csv -d <dir> -o run -- python bench.py <args>)",
              "workload args: " + "; ".join(f"{k}: {' '.join(v)}" for k, v in RUNS.items()),
              f"calibration (plain 1 GiB device copy): FETCH_SIZE x {cal['FETCH_SIZE']:.1f} B/KiB, "
@@ -141,8 +141,8 @@ def traffic_for(prefix):
 
 
 if __name__ == "__main__":
-    if len(sys.argv) >= 2 and sys.argv[1] == "collect":
-        collect()
+    if len(sys.argv) >= 3 and sys.argv[1] == "collect":
+        collect(sys.argv[2])
     elif len(sys.argv) >= 3 and sys.argv[1] == "summarize":
         summarize(sys.argv[2])
     else:

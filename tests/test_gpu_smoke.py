@@ -1,5 +1,5 @@
-"""The round-end smoke check (__graft_entry__.smoke) runs as a GPU test too, so
-that a break in it shows up with the other GPU tests."""
+"""The smoke check (__graft_entry__.smoke) also runs as a GPU test, so that a
+break in it shows up with the other GPU tests."""
 import os
 import sys
 
