@@ -32,9 +32,19 @@ constexpr int kGT = 64;            // keys per LDS tile in the output kernel
 constexpr int kGThreads = 512;     // 8 waves, 32 rows each
 constexpr float kLogGateFloor = -126.0f;
 
+// LDS barrier that leaves the tile copies in flight: waits for this wave's own
+// LDS accesses (lgkmcnt 0, vmcnt left at its maximum), then s_barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  barrier_only();
+}
+
 // inclusive prefix sum of 256 values held by threads 0..255 (one each); every
 // thread of the workgroup must call it. Returns the sum up to and including
-// this thread's value (threads >= 256 get garbage).
+// this thread's value (threads >= 256 get garbage). kWaitAll: the barrier also
+// waits for every memory access in flight (__syncthreads); otherwise copies
+// to LDS may stay in flight across it.
+template <bool kWaitAll = true>
 __device__ __forceinline__ float chunk_prefix(float x, float* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -43,7 +53,8 @@ __device__ __forceinline__ float chunk_prefix(float x, float* wsum) {
     if (lane >= o) x += y;
   }
   if (lane == 63 && wave < 4) wsum[wave] = x;
-  __syncthreads();
+  if constexpr (kWaitAll) __syncthreads();
+  else lds_barrier();
   float add = 0.f;
   for (int w = 0; w < wave && w < 4; ++w) add += wsum[w];
   return x + add;
@@ -268,16 +279,39 @@ __global__ __launch_bounds__(256) void gret_scan_kernel(GretParams p) {
 // ---------------------------------------------------------------------------
 // 3. outputs of one chunk
 // ---------------------------------------------------------------------------
+// LDS of the output kernel (head_dim D): every K/V tile of the chunk has its
+// own stage, Q^ and the incoming state come in by the load unit too and their
+// space is handed to tiles 1, 2 (Q^) and 3 (state) once read:
+//   [0, T)          tile 0
+//   [T, 3T)         Q^ rows of the chunk, then tiles 1 and 2
+//   [3T, 4T)        S_c^T, then tile 3
+//   [4T, 4T + 1 KB) the gates, then their prefix A
+template <int D>
+struct OutLds {
+  static constexpr int kTile = kGT * D * 2;        // one K or V tile
+  static constexpr int kStage = 2 * kTile;          // K then V
+  static constexpr int kQ = kStage;                 // Q^ area (2 stages)
+  static constexpr int kS = 3 * kStage;             // state area (stage 3)
+  static constexpr int kA = 4 * kStage;             // gates / prefix
+  static constexpr int kBytes = kA + kGC * 4;
+  static_assert(kGC * D * 2 == 2 * kStage, "the chunk's Q^ rows fill two stages");
+  static_assert(D * D * 2 <= kStage, "the state fits a stage");
+};
+__device__ __forceinline__ uint32_t out_stage_off(int t, int stage) {
+  return (uint32_t)(t == 0 ? 0 : t * stage);   // tiles 1, 2 in the Q^ area, 3 in the state area
+}
+
 template <int D>
 __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
-  constexpr int kTile = kGT * D * 2;          // one K or V tile
-  constexpr int kStage = 2 * kTile;
+  typedef OutLds<D> LY;
+  constexpr int kTile = LY::kTile;
+  constexpr int kStage = LY::kStage;
   constexpr int kOStride = D + 8;
-  static_assert(8 * 32 * kOStride * 2 <= 2 * kStage + D * D * 2, "staging fits");
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kStage + D * D * 2];
-  __shared__ __attribute__((aligned(16))) float A_lds[kGC];
+  static_assert(8 * 32 * kOStride * 2 <= LY::kS, "output staging fits tiles 0..2");
+  __shared__ __attribute__((aligned(16))) char smem_raw[LY::kBytes];
   __shared__ float wsum[4];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
+  YOCO_LDS float* A_lds = (YOCO_LDS float*)(smem + LY::kA);
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const ChunkInfo ci = chunk_info(p, b, c);
   if (ci.n == 0) return;
@@ -285,36 +319,47 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   const int qj = lane & 31, hf = lane >> 5;
   const int H = p.heads;
   const uint32_t base_lds = (uint32_t)(uintptr_t)smem;
-  const uint32_t s_lds = base_lds + 2 * kStage;      // S_c^T [dv][dk], row_slot layout
   const int n_tiles = (ci.n + kGT - 1) / kGT;
   const __bf16* kg = static_cast<const __bf16*>(p.k);
   const __bf16* vg = static_cast<const __bf16*>(p.v);
   const int64_t bh = (int64_t)b * H + h;
   const bool has_state = c > 0 || p.state_in != nullptr;
-
-  // incoming state (bf16 [dv][dk] in the workspace) and the first two K/V tiles
-  if (has_state) {
-    constexpr int cpr = D / 8;
-    const __bf16* sg = reinterpret_cast<const __bf16*>(p.chunk_in) + (bh * p.max_chunks + c) * (D * D);
-    const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
-    for (int i = 0; i < D * cpr / kGThreads; ++i) {
-      const int q = i * kGThreads + tid;
-      const int r = q / cpr, slot = q % cpr;
-      dma16(sg + r * D + 8 * (slot ^ (r & (cpr - 1))), s_lds + (i * kGThreads + wv * 64) * 16);
-    }
-  }
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int t) {
-    const uint32_t st = base_lds + (t & 1) * kStage;
+    const uint32_t st = base_lds + out_stage_off(t, kStage);
     const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
     load_tile<D, false>(kg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st);
     load_tile<D, true>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile);
   };
-  issue(0);
-  if (n_tiles > 1) issue(1);
 
-  // decay prefix A_j (base 2) of the chunk's rows
-  const float a = log2_gate(p.gamma, ci.row0 + tid, h, H, tid < ci.n);
-  const float A = chunk_prefix(a, wsum);
+  // copies, in this order: the gates (one dword per row), the incoming state
+  // (bf16 [dv][dk] in the workspace), Q^ (row_slot layout), tile 0
+  if (tid < kGC) {
+    const int r = tid < ci.n ? tid : ci.n - 1;
+    dma4(p.gamma + (ci.row0 + r) * H + h, base_lds + LY::kA + wv * 256);
+  }
+  if (has_state) {
+    constexpr int cpr = D / 8;
+    const __bf16* sg = reinterpret_cast<const __bf16*>(p.chunk_in) + (bh * p.max_chunks + c) * (D * D);
+    for (int i = 0; i < D * cpr / kGThreads; ++i) {
+      const int q = i * kGThreads + tid;
+      const int r = q / cpr, slot = q % cpr;
+      dma16(sg + r * D + 8 * (slot ^ (r & (cpr - 1))), base_lds + LY::kS + (i * kGThreads + wv * 64) * 16);
+    }
+  }
+  load_tile<D, false>(static_cast<const __bf16*>(p.q), ci.row0, ci.n, 0, kGC, H, h, base_lds + LY::kQ);
+  issue(0);
+  constexpr int L = 2 * (kGT * D / 8 / kGThreads);   // copies per thread and tile
+  wait_vm_lgkm0<L>();   // all but tile 0
+  barrier_only();
+
+  // decay prefix A_j (base 2) of the chunk's rows, in place of the gates
+  float a = 0.f;
+  if (tid < kGC && tid < ci.n) {
+    const float l = __log2f(A_lds[tid]);
+    a = l > kLogGateFloor ? l : kLogGateFloor;
+  }
+  const float A = chunk_prefix<false>(a, wsum);
   if (tid < kGC) A_lds[tid] = A;
 
   // Q^T as the B operand: query row qj of this wave, dims 16kk + 8hf .. +7
@@ -322,13 +367,14 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   const int j_load = j_row < ci.n ? j_row : ci.n - 1;
   bf16x8 qf[D / 16];
   {
-    const __bf16* qsrc = static_cast<const __bf16*>(p.q) + ((ci.row0 + j_load) * H + h) * D + 8 * hf;
+    const YOCO_LDS char* qs = smem + LY::kQ;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qsrc + 16 * kk));
+      qf[kk] = *reinterpret_cast<const YOCO_LDS bf16x8*>(qs + row_slot<D>(j_load, 2 * kk + hf));
   }
-  wait_vm_lgkm0<0>();
-  __syncthreads();   // state, first tiles and A in LDS (the second tile too: all waited)
+  lds_barrier();   // Q^ read by every wave (its area takes tiles 1 and 2); A in LDS
+  if (n_tiles > 1) issue(1);
+  if (n_tiles > 2) issue(2);
 
   const bool wave_active = 32 * wave < ci.n;
   const float Aj = A_lds[j_load];
@@ -337,7 +383,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
   if (has_state && wave_active) {
     // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j
-    const YOCO_LDS char* sl = smem + 2 * kStage;
+    const YOCO_LDS char* sl = smem + LY::kS;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
@@ -350,18 +396,24 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] *= e;
   }
+  if (n_tiles > 3) {
+    lds_barrier();   // the state is read by every wave: its area takes tile 3
+    issue(3);
+  }
 
-  // intra-chunk term, tile by tile
-  constexpr int L = 2 * (kGT * D / 8 / kGThreads);   // copies per thread and tile
+  // intra-chunk term, tile by tile; tile t is in when at most the copies of
+  // the tiles requested after it (n_tiles - 1 - t of them) are in flight
+  static_assert(kGC / kGT == 4, "the waits below assume four tiles per chunk");
   for (int t = 0; t < n_tiles; ++t) {
-    if (t > 0) {
-      // tile t is in when at most the copies of tile t + 1 (if requested) are in flight
-      if (t + 1 < n_tiles) wait_vm_lgkm0<L>(); else wait_vm_lgkm0<0>();
-      barrier_only();
-    }
+    const int after = n_tiles - 1 - t;
+    if (after >= 3) wait_vm_lgkm0<3 * L>();
+    else if (after == 2) wait_vm_lgkm0<2 * L>();
+    else if (after == 1) wait_vm_lgkm0<L>();
+    else wait_vm_lgkm0<0>();
+    barrier_only();
     const int key0 = t * kGT;
     if (wave_active && key0 <= j_row) {
-      const YOCO_LDS char* ks = smem + (t & 1) * kStage;
+      const YOCO_LDS char* ks = smem + out_stage_off(t, kStage);
       const YOCO_LDS char* vs = ks + kTile;
       // S^T[m][j] = K Q^T: two 32-key chains
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -406,10 +458,6 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
           }
         }
       }
-    }
-    if (t + 2 < n_tiles) {
-      barrier_only();   // every wave is done with stage t & 1 (its reads fed MFMAs already)
-      issue(t + 2);
     }
   }
   wait_vm_lgkm0<0>();

@@ -26,8 +26,8 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
-// 16-byte-per-lane HBM -> LDS copies by the load unit: lane l's 16 bytes land
-// at dst + 16 l (dst is wave-uniform). Written as asm so that the compiler does
+// HBM -> LDS copies by the load unit: 16 bytes per lane (lane l's land at
+// dst + 16 l; dst is wave-uniform), or 4 (dma4). Written as asm so that the compiler does
 // not count them among its own LDS events (which would make it wait for every
 // LDS read to finish before the next MFMA); their completion is awaited
 // explicitly with s_waitcnt vmcnt before the workgroup barrier of their tile.
@@ -44,6 +44,10 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t dst) {
 __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t dst) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(base)
                : "memory", "m0");
+}
+// 4 bytes per lane (lane l's dword lands at dst + 4 l), per-lane 64-bit source address
+__device__ __forceinline__ void dma4(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dword %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
