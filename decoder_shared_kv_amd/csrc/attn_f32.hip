@@ -83,8 +83,10 @@ __global__ __launch_bounds__(kPrefillF32Rows) void prefill_f32_kernel(AttnParams
 #pragma unroll
     for (int i = 0; i < D; ++i) acc[i] = 0.f;
     float m = -INFINITY, l = 0.f;
+    // a row whose position has no cache row of its own (more query rows than
+    // cache rows) sees no rows: O = 0, LSE = -inf
     int vis = r + offset + 1;
-    if (vis > n_kv) vis = n_kv;
+    if (vis > n_kv) vis = 0;
     // sliding window: rows vis - window .. vis - 1 only
     const int lo = p.window > 0 && vis > p.window ? vis - p.window : 0;
     accumulate_rows<D>(qr, kbase, vbase, row_stride, lo, vis, p.scale_log2, m, l, acc);

@@ -419,8 +419,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     const int wg_last_key = min(wg_last_row + offset, n_kv - 1);
     const int n_tiles = wg_last_key >= 0 ? wg_last_key / kBN + 1 : 0;
     const int r0 = pw * pos_per_wg + pbl * kPrefillRowsPerWave;
-    const int my_pos = min(r0 + qj + offset, n_kv - 1);   // rows past the last cache row see every row
-    const bool wave_active = r0 < n_q;
+    // a row whose position has no cache row of its own (more query rows than
+    // cache rows) gets the empty result, O = 0 and LSE = -inf: its own row is
+    // written before any Cross-Decoder layer reads the cache, so nothing else
+    // is defined for it; the clamp only keeps its (discarded) masking in range
+    const int my_pos = min(r0 + qj + offset, n_kv - 1);
+    const bool own_row = r0 + qj + offset < n_kv;
+    const bool wave_active = r0 < n_q && r0 + offset < n_kv;
     const int wave_max_pos = min(r0 + kPrefillRowsPerWave, n_q) - 1 + offset;
     // tiles below full_tiles need no causal mask for any row of this wave
     const int full_tiles = min((r0 + offset + 1) / kBN, n_kv / kBN);
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
 
     // Epilogue: normalise, stage the wave's 32 x D output tile in LDS, then
     // store whole rows with 16-byte writes.
-    const float l_tot = sum_xor32(l);
+    const float l_tot = own_row ? sum_xor32(l) : 0.f;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)smem + wave * (kPrefillRowsPerWave * kOStride);
 #pragma unroll

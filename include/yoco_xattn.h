@@ -98,8 +98,12 @@ yoco_status yoco_kv_append(const yoco_dims* dims, const yoco_kv_cache* cache,
  * Sequence b's queries are packed rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of
  * q. With n = its readable cache rows and m = its query rows, query row r sits
  * at position r + max(n - m, 0) (r itself when m == n, the full-prompt case)
- * and attends rows 0 .. that position. Rows of queries whose position has no
- * readable row (n == 0) get O = 0 and LSE = -inf.
+ * and attends rows 0 .. that position. A query row whose position is n or
+ * later (more query rows than readable rows, n == 0 included) has no K^,V^ row
+ * of its own in the cache: a token's row is written before any Cross-Decoder
+ * layer reads (page "YOCO", section "Decode：新 token 仍需经过两部分"), so no
+ * attention is defined for it, and it gets the empty key set's result,
+ * O = 0 and LSE = -inf.
  *   q          [device] [total_q, Hq, head_dim]
  *   cu_seqlens_q [device] int32 [B+1], non-decreasing, cu_seqlens_q[B] <= total_q
  *   max_q_len  [host] sizing hint for the grid (longer sequences are still

@@ -36,7 +36,10 @@ Readings where the pages are silent (each is listed in the design notes):
 * The mask is inclusive (j <= i) and exact (masked rows carry zero weight).
 * Prefill queries and keys index the same positions; a chunk of m new query
   rows after n cached rows (m <= n) sits at the last m positions; a decode
-  query sits at position seq_len - 1 after its row was appended.
+  query sits at position seq_len - 1 after its row was appended. With more
+  query rows than cache rows (m > n) the queries start at position 0 and those
+  at positions n and later, whose own row is not in the cache, get the empty
+  result (O = 0, LSE = -inf).
 * No positional transform inside the cross-attention.
 * LSE is the natural-log log-sum-exp of the scaled scores; an empty sequence
   yields O = 0 and LSE = -inf.
@@ -61,6 +64,7 @@ __all__ = [
     "visible_rows",
     "window_start",
     "prefill_position",
+    "has_own_row",
     "decode_position",
     "scores",
     "softmax_weights",
@@ -97,10 +101,21 @@ def prefill_position(r: int, n_q: int, n_kv: int) -> int:
 
     The queries are the last n_q positions of the sequence (a full prompt when
     n_q == n_kv; a chunk of new tokens after the cached ones otherwise); with
-    more queries than rows they start at position 0 and those past the last row
-    see every row.
+    more queries than rows they start at position 0.
     """
-    return min(r + max(n_kv - n_q, 0), n_kv - 1)
+    return r + max(n_kv - n_q, 0)
+
+
+def has_own_row(p: int, n_kv: int) -> bool:
+    """Whether the token at position p has its K̂,V̂ row among the n_kv cache rows.
+
+    A token's row is written before any Cross-Decoder layer reads the cache
+    ("YOCO", section "Decode：新 token 仍需经过两部分"), so a query whose own row
+    is not there has no defined attention. Such a row gets the result of an
+    empty key set: O = 0 and LSE = -inf (the convention for a sequence with no
+    rows).
+    """
+    return p < n_kv
 
 
 def decode_position(n: int) -> int:
@@ -171,7 +186,8 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start
     q: [total_q, Hq, d]; k_pool, v_pool: [rows, Hkv, d]. Query row r of sequence b
     (packed row cu_seqlens[b] + r) sits at position prefill_position(r, m, n) (m
     query rows, n = seq_len[b] cache rows: r itself for a full prompt) and sees
-    cache rows seq_start[b] + 0 .. seq_start[b] + that position (at most n rows).
+    cache rows seq_start[b] + 0 .. seq_start[b] + that position; a row whose
+    position has no cache row of its own (has_own_row) gets O = 0, LSE = -inf.
     `rows` (optional) restricts the work to {b: [r, ...]}; rows not computed are NaN.
     `window` > 0 restricts each query to the rows of its window (sliding-window
     attention). Returns out [total_q, Hq, d] and lse [Hq, total_q] (float64).
@@ -193,10 +209,14 @@ def prefill_ref(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, seq_start
             kh = kv_head_of(h, hq, hkv)
             kb = k_pool[s0:s0 + n, kh, :]
             vb = v_pool[s0:s0 + n, kh, :]
-            for i in range(0, want.size, block):
-                r = want[i:i + block]
-                pos = np.array([prefill_position(int(x), m, n) for x in r], dtype=np.int64)
-                o, l = attend_rows(q[q0 + r, h, :], pos, kb, vb, scale, window)
+            pos_all = np.array([prefill_position(int(x), m, n) for x in want], dtype=np.int64)
+            own = np.array([has_own_row(int(p), n) for p in pos_all], dtype=bool)
+            out[q0 + want[~own], h, :] = 0.0
+            lse[h, q0 + want[~own]] = -np.inf
+            want_own, pos_own = want[own], pos_all[own]
+            for i in range(0, want_own.size, block):
+                r = want_own[i:i + block]
+                o, l = attend_rows(q[q0 + r, h, :], pos_own[i:i + block], kb, vb, scale, window)
                 out[q0 + r, h, :] = o
                 lse[h, q0 + r] = l
     return out, lse

@@ -278,14 +278,21 @@ def check_chunked_prefill():
         tv = torch.from_numpy(np.ascontiguousarray(v[s0:s0 + n])).permute(1, 0, 2)[None]
         ts = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), enable_gqa=True, scale=0.45)
         assert np.max(np.abs(ts[0].permute(1, 0, 2).numpy() - o[cu[b]:cu[b + 1]])) <= 1e-12, ("chunk vs sdpa", b)
-    # more query rows than cache rows: rows past the last cache row see every row
+    # more query rows than cache rows (m > n): the queries start at position 0;
+    # the first n rows are the prompt's prefill, and a row at position n or later
+    # has no K^,V^ row of its own in the cache (a token's row is written before
+    # any Cross-Decoder layer reads: "YOCO", section "Decode：新 token 仍需经过两部分"),
+    # so it gets the empty key set's result, O = 0 and LSE = -inf
     q2, k2, v2, st2, ln2, cu2 = _chunk_case(rng, (5,), (8,), 2, 1, 4)
-    o2, _ = ox.prefill_ref(q2, k2, v2, st2, ln2, cu2, 0.7)
-    o2f, _ = ox.prefill_ref(q2[:5], k2, v2, st2, ln2, np.array([0, 5]), 0.7)
-    assert np.max(np.abs(o2[:5] - o2f)) <= 1e-14
-    for r in range(5, 8):
-        od2, _ = ox.decode_ref(q2[r:r + 1], k2, v2, st2, ln2, 0.7)
-        assert np.max(np.abs(o2[r] - od2[0])) <= 1e-14
+    o2, l2 = ox.prefill_ref(q2, k2, v2, st2, ln2, cu2, 0.7)
+    o2f, l2f = ox.prefill_ref(q2[:5], k2, v2, st2, ln2, np.array([0, 5]), 0.7)
+    assert np.max(np.abs(o2[:5] - o2f)) <= 1e-14 and np.max(np.abs(l2[:, :5] - l2f)) <= 1e-14
+    assert np.all(o2[5:] == 0.0) and np.all(np.isneginf(l2[:, 5:])), "rows without their own cache row"
+    # the same rows requested one by one
+    o3, l3 = ox.prefill_ref(q2, k2, v2, st2, ln2, cu2, 0.7, rows={0: [4, 5, 7]})
+    assert np.max(np.abs(o3[[4, 5, 7]] - o2[[4, 5, 7]])) <= 1e-14
+    assert np.array_equal(np.isneginf(l3[:, [4, 5, 7]]), np.isneginf(l2[:, [4, 5, 7]]))
+    assert np.max(np.abs(l3[:, 4] - l2[:, 4])) <= 1e-14
     # (ii) one-row chunk = decode
     od, ld = ox.decode_ref(q[cu[1]:cu[2]], k, v, st[1:2], ln[1:2], 0.45)
     assert np.max(np.abs(od[0] - o[cu[1]])) <= 1e-14 and np.max(np.abs(ld[0] - l[:, cu[1]])) <= 1e-14

@@ -1,6 +1,7 @@
 """Chunked prefill / multi-token decode: m new query rows per sequence against a
 shared cache of n >= m rows (queries at the last m positions), and the m > n
-corner, against the fp64 oracle."""
+corner (rows at positions n and later have no cache row of their own and get
+O = 0, LSE = -inf), against the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -23,6 +24,8 @@ def _ref(c):
     ((3000,), (200,), 16, 2, 128, "bf16"),        # g = 8, chunk spans several tiles with a ragged tail
     ((777, 90), (33, 90), 6, 3, 64, "bf16"),       # head_dim 64, g = 2
     ((50,), (80,), 8, 2, 128, "bf16"),             # more query rows than cache rows
+    ((20, 100), (90, 30), 4, 2, 64, "bf16"),       # m > n beside a plain chunk; whole waves without rows
+    ((30,), (45,), 4, 1, 64, "f32"),               # m > n, fp32 path
     ((300, 40), (17, 40), 4, 1, 64, "f32"),
 ])
 def test_chunked_prefill(kv, qn, hq, hkv, d, dtype):
@@ -30,6 +33,8 @@ def test_chunked_prefill(kv, qn, hq, hkv, d, dtype):
     c = synth.make_chunk_case(list(kv), list(qn), hq, hkv, d, dtype, seed=sum(kv) + sum(qn), std=1.0, cap_extra=3)
     out, lse = run_prefill(c)
     ref, ref_lse = _ref(c)
+    missing = np.isneginf(ref_lse)
+    assert np.all(np.isneginf(lse[missing])), "rows without their own cache row: LSE = -inf"
     e = parity.check(out, ref, dtype, discriminating=True, what="chunked prefill")
     parity.check_lse(lse, ref_lse, dtype, what="chunked prefill lse")
     say(f"  max-abs {e['max_abs']:.2e} row-rel {e['row_rel']:.2e}")

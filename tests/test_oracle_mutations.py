@@ -222,8 +222,8 @@ MUTATIONS = {
     "lse_drops_max": ("log_sum_exp", lambda m, z: np.log(z)),
     "lse_log2": ("log_sum_exp", lambda m, z: m + np.log2(z)),
     "prefill_position_shift": ("prefill_position", lambda r, m, n: r + max(n - m, 0) + 1),
-    "prefill_position_no_clamp_to_last_row": ("prefill_position", lambda r, m, n: r + max(n - m, 0) if r < n
-                                               else n),
+    "rows_past_cache_see_every_row": ("has_own_row", lambda p, n: True),
+    "last_own_row_treated_as_missing": ("has_own_row", lambda p, n: p < n - 1),
     "chunk_aligned_top_left": ("prefill_position", lambda r, m, n: r),
     "chunk_offset_off_by_one": ("prefill_position", lambda r, m, n: r + max(n - m - 1, 0)),
     "decode_position_before_append": ("decode_position", lambda n: n - 2),
