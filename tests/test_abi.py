@@ -269,3 +269,43 @@ def test_missing_library_fails_loudly():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert "raised:" in r.stdout and "is not built" in r.stdout
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding checks dtype, shape, device and contiguity before any ABI
+    call (all cases here fail before the library is reached)."""
+    import torch
+    k = torch.zeros(16, 2, 64, dtype=torch.bfloat16)
+    meta = dict(seq_start=torch.zeros(1, dtype=torch.int64), seq_len=torch.ones(1, dtype=torch.int32),
+                seq_cap=torch.full((1,), 16, dtype=torch.int32))
+    good = dk.SharedKV(k, k.clone(), **meta)
+    cases = [
+        dk.SharedKV(k, k.clone().to(torch.float32), **meta),                       # v dtype
+        dk.SharedKV(k, k.clone()[:8], **meta),                                      # v shape
+        dk.SharedKV(k, k.clone().transpose(0, 1).contiguous().transpose(0, 1), **meta),  # v strided
+        dk.SharedKV(k, k.clone(), **{**meta, "seq_start": torch.zeros(1, dtype=torch.int32)}),
+        dk.SharedKV(k, k.clone(), **{**meta, "seq_len": torch.ones(1, dtype=torch.int64)}),
+        dk.SharedKV(k, k.clone(), **{**meta, "seq_cap": torch.ones(2, dtype=torch.int32)}),
+    ]
+    for c in cases:
+        with pytest.raises(dk.YocoError):
+            c.validate()
+    q = torch.zeros(4, 4, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(dk.YocoError):      # q in another dtype than the cache
+        dk.xattn_prefill(good, q.float(), cu, 4, 0.1)
+    with pytest.raises(dk.YocoError):      # q not contiguous
+        dk.xattn_prefill(good, torch.zeros(4, 64, 4, dtype=torch.bfloat16).transpose(1, 2), cu, 4, 0.1)
+    with pytest.raises(dk.YocoError):      # int64 cu_seqlens
+        dk.xattn_prefill(good, q, cu.long(), 4, 0.1)
+    with pytest.raises(dk.YocoError):      # lse of the wrong shape
+        dk.xattn_prefill(good, q, cu, 4, 0.1, lse=torch.zeros(4, 5))
+    with pytest.raises(dk.YocoError):      # decode: one query row per sequence
+        dk.xattn_decode(good, q, 4, 0.1, torch.zeros(64, dtype=torch.uint8))
+    with pytest.raises(dk.YocoError):      # decode workspace of the wrong dtype
+        dk.xattn_decode(good, q[:1], 4, 0.1, torch.zeros(64, dtype=torch.float32))
+    with pytest.raises(dk.YocoError):      # appended rows of the wrong shape
+        dk.kv_append(good, torch.zeros(1, 2, 32, dtype=torch.bfloat16), torch.zeros(1, 2, 32, dtype=torch.bfloat16))
+    with pytest.raises(dk.YocoError):      # gRet gates in bf16
+        dk.gret_decode(q[:1], q[:1], q[:1], torch.zeros(1, 4, dtype=torch.bfloat16),
+                       torch.zeros(1, 4, 64, 64))
