@@ -8,6 +8,13 @@ One step = one pass of the whole path over seeded synthetic input resident in HB
 `value` is the prefill rate (algorithmic causal flops 4*d*Hq*N(N+1)/2 per layer
 over the measured time); the decode rate (K^ and V^ bytes read once per call plus
 Q and O, over the measured call time) is reported beside it in `decode`.
+The default run also times, each with its own roofline block:
+  * `decode_1m`: the long-context decode, 1 x 1048576 rows, 64 steps of one
+    append and 16 layer calls;
+  * `ragged`: 16 prompts of log-uniform lengths in [4096, 65536) (Hq=32,
+    Hkv=8): their causal prefill, then 32 decode steps;
+and reports a streaming-read probe of the device (`device.read_probe_GBps`)
+and the pages' own model-level claims as context (`context`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --workload decode_1m     (long-context decode, 64 steps x 16 layers)
@@ -18,6 +25,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --workload gret          (gated retention: chunkwise prefill of 32K rows x 16 heads,
                                                   recurrent decode steps for 8 sequences)
        python bench.py --copy-probe             (plain copy kernel of known size, for counter scaling)
+       python bench.py --skip decode_1m,ragged  (leave legs out: prefill, decode, decode_1m, ragged)
 """
 from __future__ import annotations
 
@@ -35,6 +43,25 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 CALL_REPS = 32               # back-to-back calls for the per-call median / min / p90
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "decode HBM GB/s (% peak) @128K-1M; prefill TFLOP/s (% MFMA peak) @32K"
+PROBE_LIB = os.path.join(ROOT, "decoder_shared_kv_amd", "lib", "libyoco_probe.so")
+
+# The pages' end-to-end claims for whole YOCO models, restated (page "YOCO 深度技术分析",
+# liuhc.cn, section 3.4 inference-efficiency table). The pages state no hardware,
+# precision or kernel for any of them: context beside the kernel figures, not targets.
+PUBLISHED_CONTEXT = {
+    "note": "model-level claims of the pages for whole YOCO models against a Transformer; hardware, precision "
+            "and kernels not stated; context only, not comparable with the kernel rates above",
+    "source": "YOCO 深度技术分析 (liuhc.cn), section 3.4",
+    "claims": [
+        {"what": "KV cache memory per token", "factor": "about 80x smaller", "workload": "65B model",
+         "hardware": "not stated"},
+        {"what": "prefill latency", "factor": "2.87x faster", "workload": "32K context", "hardware": "not stated"},
+        {"what": "prefill latency", "factor": "71.8x faster (Transformer about 300 s)", "workload": "1M context",
+         "hardware": "not stated"},
+        {"what": "decode throughput", "factor": "9.6x higher (4.5 to 43.1 tokens/s)", "workload": "512K context",
+         "hardware": "not stated"},
+    ],
+}
 
 
 def log(msg):
@@ -291,7 +318,18 @@ def main():
                                                        out=out_d, lse=lse_d))}
         if "prefill" in skip:
             res.update({"value": gbs, "unit": "GB/s"})
+    # the other legs run on their own inputs: free these first (the closures
+    # above hold these names, so they are rebound rather than deleted)
+    pc = pcache = qs = out_p = lse_p = dc = dcache = ws = qd = None  # noqa: F841
+    torch.cuda.empty_cache()
+    if "decode_1m" not in skip:
+        res["decode_1m"] = leg_decode_1m(args, torch, dk, synth, dev)
+        torch.cuda.empty_cache()
+    if "ragged" not in skip:
+        res["ragged"] = leg_ragged(args, torch, dk, synth, dev)
+        torch.cuda.empty_cache()
     res["device"] = device_info(torch, dev)
+    res["context"] = PUBLISHED_CONTEXT
     if not args.no_cpu_baseline:
         import oracle
         log("timing the oracle on the host")
@@ -299,10 +337,44 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def read_probe(torch, dev):
+    """Streaming-read rate of the device: the probe kernel (lib/libyoco_probe.so)
+    reads a 2 GiB buffer (8x the Infinity Cache) with 16-byte nontemporal loads,
+    5 passes per grid size; the best grid's rate is reported."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.yoco_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.yoco_probe_read.restype = ctypes.c_int
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    grids = (1024, 2048, 4096, 8192)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    rates = {}
+    for grid in grids:
+        assert lib.yoco_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            lib.yoco_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        rates[grid] = 5 * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf, sink
+    best = max(rates, key=rates.get)
+    return {"read_probe_GBps": rates[best],
+            "read_probe": f"read_probe_kernel: 2 GiB, 16-byte nontemporal loads, 256 threads x {best} workgroups "
+                          f"(best of grids {list(grids)}: " + ", ".join(f"{g}: {r:.0f}" for g, r in rates.items())
+                          + " GB/s)"}
+
+
 def device_info(torch, dev):
-    """CU count and a copy probe: torch's device copy of 1 GiB (bytes read plus
-    bytes written per second), for context beside the 8 TB/s published figure."""
+    """CU count, a streaming-read probe, and a copy probe: torch's device copy of
+    1 GiB (bytes read plus bytes written per second), for context beside the
+    8 TB/s published figure."""
     props = torch.cuda.get_device_properties(dev)
+    probe = read_probe(torch, dev)
     a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     for _ in range(2):
@@ -315,15 +387,31 @@ def device_info(torch, dev):
     torch.cuda.synchronize()
     gbs = 5 * 2 * a.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
     del a, b
-    return {"name": props.name, "compute_units": props.multi_processor_count,
+    return {"name": props.name, "compute_units": props.multi_processor_count, **probe,
             "copy_probe_GBps": gbs, "copy_probe": "torch device copy of 1 GiB, 5 passes, read + write bytes"}
 
 
-def bench_decode_1m(args, torch, dk, synth, dev):
+def call_spread(torch, call, reps=CALL_REPS):
+    """Per-call spread: one event pair around each of `reps` back-to-back calls."""
+    import numpy as np
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"calls": reps, "median_ms": float(np.median(t)), "min_ms": float(t.min()),
+            "p90_ms": float(np.percentile(t, 90))}
+
+
+def leg_decode_1m(args, torch, dk, synth, dev):
+    """The long-context decode: 1 x 1048576 rows, 64 steps of one append and 16
+    layer calls (the cache grows to 1048640 rows), timed as one region."""
     w = synth.WORKLOADS["decode_1m"]
     t = time.perf_counter()
     c, cache = make_decode(dk, synth, dev, w, 0)
-    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
+    log(f"decode 1m inputs ready in {time.perf_counter() - t:.1f} s")
     q = c.q.to(dev)
     kn, vn = c.k_new.to(dev), c.v_new.to(dev)
     max_len = int(c.seq_len.max()) + w.decode_steps
@@ -333,7 +421,7 @@ def bench_decode_1m(args, torch, dk, synth, dev):
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     # warm-up on a copy of the metadata so that the timed run starts from the initial cache
     saved = cache.seq_len.clone()
-    for _ in range(min(args.warmup, 2)):
+    for _ in range(max(1, min(args.warmup, 2))):
         dk.kv_append(cache, kn[0], vn[0], flag)
         dk.xattn_decode(cache, q[0, 0], max_len, c.scale, ws, out=out, lse=lse)
     torch.cuda.synchronize()
@@ -357,16 +445,30 @@ def bench_decode_1m(args, torch, dk, synth, dev):
     assert int(flag.item()) == 0
     gbs = nbytes / (ms / 1e3) / 1e9
     calls = w.decode_steps * w.layers
+    spread = call_spread(torch, lambda i: dk.xattn_decode(cache, q[-1, i % w.layers], max_len, c.scale, ws,
+                                                          out=out, lse=lse))
+    last_bytes = decode_bytes(lens, w.kv_heads, w.q_heads, w.head_dim)
+    spread["median_GBps"] = last_bytes / (spread["median_ms"] / 1e3) / 1e9
+    res = {"value": gbs, "unit": "GB/s", "total_ms": ms, "wall_ms": wall * 1e3, "steps": w.decode_steps,
+           "layers": w.layers, "avg_call_ms": ms / calls, "algorithmic_bytes_per_call": nbytes / calls,
+           "workload": "decode: B=1 N=1048576 (+64 appends) Hq=16 Hkv=2 d=128, 64 steps x (append + 16 layers)",
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                        "kernel": "decode_split_bf16_kernel<128, 1, 0> + decode_merge_kernel (+ the step's "
+                                  "kv_append_kernel inside the timed region)"},
+           "calls": {**spread, "what": f"{CALL_REPS} back-to-back decode calls at {lens[0]} rows"}}
+    del c, cache, q, kn, vn, ws
+    return res
+
+
+def bench_decode_1m(args, torch, dk, synth, dev):
+    leg = leg_decode_1m(args, torch, dk, synth, dev)
     print(json.dumps({
-        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": w.decode_steps, "warmup": 2,
-        "ms_per_step": wall * 1e3 / w.decode_steps, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": leg["value"], "unit": "GB/s", "n_gpus": 1, "steps": leg["steps"], "warmup": 2,
+        "ms_per_step": leg["wall_ms"] / leg["steps"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1)/sqrt(128) bf16)",
-        "config": {"workload": "decode: B=1 N=1048576 (+64 appends) Hq=16 Hkv=2 d=128, 64 steps x 16 layers",
-                   "global_batch": 1, "seq_len": 1048576, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "kernel": "decode_split_bf16_kernel<128, 1, 0> + decode_merge_kernel",
-                     "avg_call_ms": ms / calls, "algorithmic_bytes_per_call": nbytes / calls},
-        "total_ms": ms}), flush=True)
+        "config": {"workload": leg["workload"], "global_batch": 1, "seq_len": 1048576, "parallelism": "none (1 GPU)"},
+        "roofline": leg["roofline"], "calls": leg["calls"], "total_ms": leg["total_ms"]}), flush=True)
 
 
 SWA_WINDOW = 1024   # YOCO's Self-Decoder window C
@@ -611,7 +713,10 @@ def bench_gret(args, torch, dk, synth, dev):
         flush=True)
 
 
-def bench_ragged(args, torch, dk, synth, dev):
+def leg_ragged(args, torch, dk, synth, dev):
+    """16 prompts of log-uniform lengths (Hq=32, Hkv=8): their causal prefill
+    (timed over `steps` calls), then 32 decode steps of one append and one
+    layer call, each decode call timed on its own."""
     w = synth.WORKLOADS["ragged"]
     t = time.perf_counter()
     pc = synth.make_prefill_case(list(w.seq_lens), w.q_heads, w.kv_heads, w.head_dim, 1, w.dtype, w.seed,
@@ -620,21 +725,23 @@ def bench_ragged(args, torch, dk, synth, dev):
                                 w.seed, w.value_std)
     cache = dk.SharedKV(pc.k_pool.to(dev), pc.v_pool.to(dev), pc.seq_start.to(dev), pc.seq_len.to(dev).clone(),
                         pc.seq_cap.to(dev))
-    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
+    log(f"ragged inputs ready in {time.perf_counter() - t:.1f} s")
     q = pc.q[0].to(dev)
+    del pc.q
     cu = pc.cu_seqlens.to(dev)
     maxq = max(w.seq_lens)
     out = torch.empty_like(q)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    steps = max(args.steps, 1)
     for _ in range(args.warmup):
         dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out)
     torch.cuda.synchronize()
     e[0].record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out)
     e[1].record()
     torch.cuda.synchronize()
-    pre_ms = e[0].elapsed_time(e[1]) / args.steps
+    pre_ms = e[0].elapsed_time(e[1]) / steps
     flops = prefill_flops(w.seq_lens, w.q_heads, w.head_dim)
     qd = dc.q.to(dev)
     kn, vn = dc.k_new.to(dev), dc.v_new.to(dev)
@@ -644,7 +751,7 @@ def bench_ragged(args, torch, dk, synth, dev):
     lens = list(w.seq_lens)
     # untimed decode calls first (decode leaves the cache as it is): the first
     # launch of a kernel pays for loading its code object
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 1)):
         dk.xattn_decode(cache, qd[0, 0], maxq + w.decode_steps, pc.scale, ws, out=outd, total_kv_len=sum(lens))
     torch.cuda.synchronize()
     nbytes = 0.0
@@ -669,20 +776,39 @@ def bench_ragged(args, torch, dk, synth, dev):
     tfl = flops / (pre_ms / 1e3) / 1e12
     gbs = nbytes / (cms / 1e3) / 1e9
     gbs_step = nbytes / (dms / 1e3) / 1e9
+    res = {"workload": f"ragged: 16 seqs L={list(w.seq_lens)} Hq=32 Hkv=8 d=128; prefill + 32 decode steps",
+           "prefill": {"value": tfl, "unit": "TFLOP/s", "avg_call_ms": pre_ms, "calls": steps,
+                       "algorithmic_flops_per_call": flops,
+                       "roofline": {"bound": "mfma", "achieved": tfl, "peak": BF16_DENSE_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": tfl / BF16_DENSE_PEAK_TFLOPS, "traffic": None,
+                                    "kernel": "prefill_bf16_kernel<128>"}},
+           "decode": {"value": gbs, "unit": "GB/s", "avg_call_ms": cms / w.decode_steps,
+                      "algorithmic_bytes_per_call": nbytes / w.decode_steps,
+                      "what": "per decode call (split + merge launches), bytes of the call over its time",
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                   "kernel": "decode_split_bf16_kernel<128, 1, 1> + decode_merge_kernel"},
+                      "call_median_ms": float(sorted(call_ms)[len(call_ms) // 2]), "call_min_ms": min(call_ms),
+                      "steps": {"GB/s": gbs_step, "frac": gbs_step / HBM_PEAK_GBS,
+                                "avg_step_ms": dms / w.decode_steps,
+                                "what": "append + decode call per step, bytes of the call over the step"}},
+           "ms_per_step": pre_ms + dms / w.decode_steps}
+    del cache, q, out, qd, kn, vn, ws
+    return res
+
+
+def bench_ragged(args, torch, dk, synth, dev):
+    leg = leg_ragged(args, torch, dk, synth, dev)
+    w = synth.WORKLOADS["ragged"]
+    pre = leg["prefill"]
     print(json.dumps({
-        "metric": METRIC, "value": tfl, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": pre_ms + dms / w.decode_steps, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": pre["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": leg["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1)/sqrt(128) bf16)",
-        "config": {"workload": f"ragged: 16 seqs L={list(w.seq_lens)} Hq=32 Hkv=8 d=128; prefill + 32 decode steps",
-                   "global_batch": 16, "seq_len": maxq, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": tfl, "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tfl / BF16_DENSE_PEAK_TFLOPS, "traffic": None, "avg_launch_ms": pre_ms},
-        "decode": {"value": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "avg_call_ms": cms / w.decode_steps,
-                   "what": "per decode call (split + merge launches), bytes of the call over its time",
-                   "call_median_ms": float(sorted(call_ms)[len(call_ms) // 2]), "call_min_ms": min(call_ms),
-                   "steps": {"GB/s": gbs_step, "frac": gbs_step / HBM_PEAK_GBS, "avg_step_ms": dms / w.decode_steps,
-                             "what": "append + decode call per step, bytes of the call over the step"}}}),
-        flush=True)
+        "config": {"workload": leg["workload"], "global_batch": 16, "seq_len": max(w.seq_lens),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {**pre["roofline"], "avg_launch_ms": pre["avg_call_ms"]},
+        "decode": leg["decode"]}), flush=True)
 
 
 if __name__ == "__main__":

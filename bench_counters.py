@@ -36,8 +36,8 @@ KERNELS = {
 }
 
 RUNS = {
-    "prefill": ["--skip", "decode", "--steps", "1", "--warmup", "0", "--no-cpu-baseline"],
-    "decode": ["--skip", "prefill", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
+    "prefill": ["--skip", "decode,decode_1m,ragged", "--steps", "1", "--warmup", "0", "--no-cpu-baseline"],
+    "decode": ["--skip", "prefill,decode_1m,ragged", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
     "copy": ["--copy-probe"],
 }
 COPY_BYTES = 1 << 30

@@ -1,8 +1,12 @@
-"""Build the HIP library in-tree: decoder_shared_kv_amd/lib/libyoco_xattn.so (gfx950).
+"""Build the HIP libraries in-tree (gfx950):
 
-Every source under csrc/ is compiled by hipcc for gfx950 only, with packed fp32
-instructions disabled, and linked into one shared library that exports the C
-ABI declared in include/yoco_xattn.h.
+* decoder_shared_kv_amd/lib/libyoco_xattn.so: the attention path, exporting the
+  C ABI declared in include/yoco_xattn.h;
+* decoder_shared_kv_amd/lib/libyoco_probe.so: the benchmark's streaming-read
+  probe (csrc/read_probe.hip), a measuring instrument kept out of the ABI.
+
+Every source is compiled by hipcc for gfx950 only, with packed fp32
+instructions disabled.
 """
 from __future__ import annotations
 
@@ -16,6 +20,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "lib", "obj")
 LIB = os.path.join(HERE, "lib", "libyoco_xattn.so")
+PROBE_LIB = os.path.join(HERE, "lib", "libyoco_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "kv_append.hip", "attn_f32.hip", "decode_merge.hip", "decode_bf16.hip", "prefill_bf16.hip",
@@ -41,18 +47,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    sources = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
+        objs = list(ex.map(_compile, sources))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
