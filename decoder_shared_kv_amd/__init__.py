@@ -23,6 +23,8 @@ from .xattn import (  # noqa: F401
     make_dims,
     workspace_size,
     xattn_decode,
+    xattn_decode_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     xattn_decode_window,
     xattn_prefill,
     xattn_prefill_window,

@@ -25,7 +25,7 @@ PROBE_SOURCES = ["read_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "kv_append.hip", "attn_f32.hip", "decode_merge.hip", "decode_bf16.hip", "prefill_bf16.hip",
-           "kv_project.hip", "gret.hip"]
+           "kv_project.hip", "gret.hip", "scratch.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

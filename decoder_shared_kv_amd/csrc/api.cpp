@@ -187,9 +187,11 @@ yoco_status prefill_impl(const yoco_dims* dims, const yoco_kv_cache* cache, cons
   return err == hipSuccess ? YOCO_OK : YOCO_ERR_HIP;
 }
 
+// noalloc: the partials go to the library's device-resident scratch (of
+// YOCO_NOALLOC_SCRATCH_BYTES on each device) instead of a caller workspace.
 yoco_status decode_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q, int32_t max_kv_len,
                         int64_t total_kv_len, int32_t window, void* out, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool noalloc = false) {
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
   st = check_cache(cache);
@@ -205,6 +207,11 @@ yoco_status decode_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const
   }
   const int32_t shares = decode_shares(dims, max_kv_len, total_kv_len);
   const size_t need = decode_workspace(dims, shares);
+  if (noalloc) {
+    if (need > (size_t)YOCO_NOALLOC_SCRATCH_BYTES) return YOCO_ERR_WORKSPACE;
+    if (yoco::noalloc_scratch(&workspace) != hipSuccess) return YOCO_ERR_HIP;
+    workspace_bytes = YOCO_NOALLOC_SCRATCH_BYTES;
+  }
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return YOCO_ERR_WORKSPACE;
   AttnParams p = base_params(dims, cache);
   p.q = q;
@@ -276,6 +283,12 @@ yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache,
                               int32_t max_kv_len, int64_t total_kv_len, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream) {
   return decode_impl(dims, cache, q, max_kv_len, total_kv_len, 0, out, lse, workspace, workspace_bytes, stream);
+}
+
+yoco_status yoco_xattn_decode_noalloc(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
+                                      int32_t max_kv_len, int64_t total_kv_len, void* out, float* lse,
+                                      void* stream) {
+  return decode_impl(dims, cache, q, max_kv_len, total_kv_len, 0, out, lse, nullptr, 0, stream, true);
 }
 
 yoco_status yoco_xattn_decode_window(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,

@@ -102,6 +102,9 @@ hipError_t launch_decode_merge(const AttnParams& p, int head_dim, int dtype, hip
 hipError_t launch_kv_project(const ProjectParams& p, hipStream_t stream);
 hipError_t launch_gret_prefill(const GretParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_gret_decode(const GretParams& p, int head_dim, hipStream_t stream);
+// Device address of this device's no-allocation scratch (YOCO_NOALLOC_SCRATCH_BYTES,
+// 256-byte aligned), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_kv_pack(const void* gain, const void* wk, const void* wv, void* out, int k_dim, int hd,
                           hipStream_t stream);
 

@@ -8,7 +8,7 @@ contiguity of every tensor) and raises YocoError(INVALID_ARG) on a mismatch.
 
 The functions mirror the C ABI (include/yoco_xattn.h) one to one:
 ``kv_append``, ``kv_append_ring``, ``xattn_prefill``, ``xattn_prefill_window``,
-``xattn_decode``, ``xattn_decode_window``, ``workspace_size``, ``decode_splits``,
+``xattn_decode``, ``xattn_decode_noalloc``, ``xattn_decode_window``, ``workspace_size``, ``decode_splits``,
 ``kv_project_pack``, ``kv_project_append``, ``gret_workspace_size``, ``gret_prefill``,
 ``gret_decode``.
 """
@@ -26,11 +26,12 @@ LIB_PATH = os.path.join(_HERE, "lib", "libyoco_xattn.so")
 
 YOCO_OK = 0
 YOCO_ERR_INVALID_ARG = 1
+NOALLOC_SCRATCH_BYTES = 8 << 20   # YOCO_NOALLOC_SCRATCH_BYTES of the C header
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip launch failed"}
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTS = ("yoco_kv_append", "yoco_kv_append_ring", "yoco_xattn_prefill", "yoco_xattn_prefill_window",
-           "yoco_xattn_decode", "yoco_xattn_decode_window", "yoco_xattn_workspace_size",
+           "yoco_xattn_decode", "yoco_xattn_decode_noalloc", "yoco_xattn_decode_window", "yoco_xattn_workspace_size",
            "yoco_xattn_decode_splits", "yoco_kv_project_pack", "yoco_kv_project_append", "yoco_gret_workspace_size",
            "yoco_gret_prefill", "yoco_gret_decode", "yoco_status_string")
 
@@ -81,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_xattn_prefill.argtypes = [dims_p, cache_p, P, P, i32, i64, P, P, P]
     lib.yoco_xattn_prefill_window.argtypes = [dims_p, cache_p, P, P, i32, i64, i32, P, P, P]
     lib.yoco_xattn_decode.argtypes = [dims_p, cache_p, P, i32, i64, P, P, P, ctypes.c_size_t, P]
+    lib.yoco_xattn_decode_noalloc.argtypes = [dims_p, cache_p, P, i32, i64, P, P, P]
     lib.yoco_xattn_decode_window.argtypes = [dims_p, cache_p, P, i32, i64, i32, P, P, P, ctypes.c_size_t, P]
     lib.yoco_kv_project_pack.argtypes = [dims_p, i32, P, P, P, P, P]
     lib.yoco_kv_project_append.argtypes = [dims_p, cache_p, P, P, i64, i32, P, ctypes.c_float,
@@ -324,6 +326,24 @@ def xattn_decode(cache: SharedKV, q: torch.Tensor, max_kv_len: int, scale: float
                                  _ptr(out),
                                  _ptr(lse), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                  _stream(stream)), "yoco_xattn_decode")
+    return out
+
+
+def xattn_decode_noalloc(cache: SharedKV, q: torch.Tensor, max_kv_len: int, scale: float,
+                         out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None,
+                         total_kv_len: int = 0):
+    """xattn_decode whose partials live in the library's device-resident scratch
+    (NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace: the call allocates
+    nothing, so the caller passes `out`. Calls that may overlap on one GPU race."""
+    lib = load_library()
+    if out is None:
+        raise YocoError(YOCO_ERR_INVALID_ARG, "out is missing (the no-allocation call allocates nothing)")
+    desc, out = _decode_args(cache, q, out, lse, need_workspace=False)
+    batch, hq, _ = q.shape
+    dims = _dims_for(cache, hq, scale, batch)
+    _check(lib.yoco_xattn_decode_noalloc(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), int(max_kv_len),
+                                         int(total_kv_len), _ptr(out), _ptr(lse), _stream(stream)),
+           "yoco_xattn_decode_noalloc")
     return out
 
 

@@ -29,7 +29,9 @@
  *    checks run before any launch: a call that returns an error launched
  *    nothing and touched no output.
  *  - The library allocates and frees nothing and keeps no global state: all
- *    buffers belong to the caller. Calls are re-entrant.
+ *    buffers belong to the caller. Calls are re-entrant. The one exception is
+ *    yoco_xattn_decode_noalloc, whose partials live in a device-resident
+ *    scratch array of the library (one per GPU).
  *  - Device-side sequence metadata is clamped, never trusted, for memory
  *    safety: a sequence's readable rows are seq_start[b] .. seq_start[b] +
  *    min(seq_len[b], seq_cap[b]) - 1, further limited to the pool. Metadata
@@ -145,6 +147,31 @@ yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache,
                               const void* q, int32_t max_kv_len, int64_t total_kv_len,
                               void* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the device-resident scratch yoco_xattn_decode_noalloc uses on each GPU. */
+#define YOCO_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * yoco_xattn_decode_noalloc -- yoco_xattn_decode without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same operation,
+ * arguments, kernels and results as yoco_xattn_decode; the split-K partials
+ * go to a scratch array of YOCO_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends (its device address is looked
+ * up on the first call on that device, which must be the current device of
+ * the calling thread). Calls whose plan needs more partial space than that
+ * (yoco_xattn_workspace_size(dims, max_kv_len) > YOCO_NOALLOC_SCRATCH_BYTES,
+ * e.g. hundreds of sequences) return YOCO_ERR_WORKSPACE and launch nothing.
+ * The call allocates and frees nothing (no hipMalloc, no library allocator).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that may overlap on
+ * one GPU (different streams, or different threads) race and must be
+ * serialised by the caller. YOCO_ERR_HIP if the device or the scratch address
+ * cannot be obtained.
+ */
+yoco_status yoco_xattn_decode_noalloc(const yoco_dims* dims, const yoco_kv_cache* cache,
+                                      const void* q, int32_t max_kv_len, int64_t total_kv_len,
+                                      void* out, float* lse, void* stream);
 
 /*
  * Sliding-window attention (the Self-Decoder's efficient attention)

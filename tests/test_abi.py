@@ -271,6 +271,27 @@ def test_missing_library_fails_loudly():
     assert "raised:" in r.stdout and "is not built" in r.stdout
 
 
+def test_noalloc_decode_argument_checks(lib):
+    """The no-allocation decode rejects bad arguments and plans whose partials
+    exceed its scratch on the host, before it looks for a device."""
+    dims, cache = _dims(batch=2), _cache()
+    N = lambda d, *a: lib.yoco_xattn_decode_noalloc(ctypes.byref(d), ctypes.byref(cache), *a)  # noqa: E731
+    assert N(dims, None, 5000, 0, FAKE, None, None) == 1          # q
+    assert N(dims, FAKE, 5000, 0, None, None, None) == 1          # out
+    assert N(dims, FAKE, -1, 0, FAKE, None, None) == 1            # max_kv_len
+    assert N(_dims(batch=0), FAKE, 5000, 0, FAKE, None, None) == 1
+    # a plan needing more than the scratch: thousands of sequences of 128 query heads
+    big = _dims(batch=4096, num_q_heads=128, num_kv_heads=8)
+    need = ctypes.c_size_t(0)
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(big), 100000, ctypes.byref(need)) == 0
+    assert need.value > X.NOALLOC_SCRATCH_BYTES
+    assert N(big, FAKE, 100000, 0, FAKE, None, None) == 3
+    # the header's constant and the binding's agree
+    text = open(os.path.join(ROOT, "include", "yoco_xattn.h")).read()
+    m = re.search(r"#define YOCO_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == X.NOALLOC_SCRATCH_BYTES
+
+
 def test_binding_rejects_bad_tensors():
     """The binding checks dtype, shape, device and contiguity before any ABI
     call (all cases here fail before the library is reached)."""
@@ -304,6 +325,8 @@ def test_binding_rejects_bad_tensors():
         dk.xattn_decode(good, q, 4, 0.1, torch.zeros(64, dtype=torch.uint8))
     with pytest.raises(dk.YocoError):      # decode workspace of the wrong dtype
         dk.xattn_decode(good, q[:1], 4, 0.1, torch.zeros(64, dtype=torch.float32))
+    with pytest.raises(dk.YocoError):      # the no-allocation decode needs out
+        dk.xattn_decode_noalloc(good, q[:1], 4, 0.1, None)
     with pytest.raises(dk.YocoError):      # appended rows of the wrong shape
         dk.kv_append(good, torch.zeros(1, 2, 32, dtype=torch.bfloat16), torch.zeros(1, 2, 32, dtype=torch.bfloat16))
     with pytest.raises(dk.YocoError):      # gRet gates in bf16
