@@ -204,6 +204,7 @@ def main():
         cu = pc.cu_seqlens.to(dev)
         out_p = torch.empty_like(qs[0])
         lse_p = torch.empty(wp.q_heads, n, device=dev, dtype=torch.float32)
+        pws = dk.alloc_prefill_workspace(dev)
     if "decode" not in skip:
         dc, dcache = make_decode(dk, synth, dev, wd, args.steps + args.warmup + 1)
         max_dec = int(dc.seq_len.max()) + args.steps + args.warmup + 1
@@ -224,7 +225,7 @@ def main():
             if record:
                 ev[0].record()
             for layer in range(wp.layers):
-                dk.xattn_prefill(pcache, qs[layer], cu, n, pc.scale, out=out_p, lse=lse_p)
+                dk.xattn_prefill(pcache, qs[layer], cu, n, pc.scale, out=out_p, lse=lse_p, workspace=pws)
             if record:
                 ev[1].record()
         if "decode" not in skip:
@@ -300,7 +301,8 @@ def main():
                            "algorithmic_per_launch": flops_layer}
         res["prefill_steps"] = {**spread(pre_steps), "what": f"{wp.layers} layer calls per step"}
         res["prefill_calls"] = call_stats(
-            lambda i: dk.xattn_prefill(pcache, qs[i % wp.layers], cu, n, pc.scale, out=out_p, lse=lse_p))
+            lambda i: dk.xattn_prefill(pcache, qs[i % wp.layers], cu, n, pc.scale, out=out_p, lse=lse_p,
+                                       workspace=pws))
     if "decode" not in skip:
         calls = args.steps * wd.layers
         call_s = dec_ms / 1e3 / calls
@@ -494,6 +496,7 @@ def bench_swa(args, torch, dk, synth, dev):
     cu = pc.cu_seqlens.to(dev)
     out_p = torch.empty_like(qs[0])
     lse_p = torch.empty(wp.q_heads, n, device=dev, dtype=torch.float32)
+    pws = dk.alloc_prefill_workspace(dev)
     g = torch.Generator(device=dev).manual_seed(5)
     B, L = wd.batch, wd.layers
     rings = []
@@ -513,7 +516,7 @@ def bench_swa(args, torch, dk, synth, dev):
 
     def prefill():
         for layer in range(wp.layers):
-            dk.xattn_prefill_window(pcache, qs[layer], cu, n, C, pc.scale, out=out_p, lse=lse_p)
+            dk.xattn_prefill_window(pcache, qs[layer], cu, n, C, pc.scale, out=out_p, lse=lse_p, workspace=pws)
 
     def decode_step():
         for layer in range(L):
@@ -733,12 +736,13 @@ def leg_ragged(args, torch, dk, synth, dev):
     out = torch.empty_like(q)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     steps = max(args.steps, 1)
+    pws = dk.alloc_prefill_workspace(dev)
     for _ in range(args.warmup):
-        dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out)
+        dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out, workspace=pws)
     torch.cuda.synchronize()
     e[0].record()
     for _ in range(steps):
-        dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out)
+        dk.xattn_prefill(cache, q, cu, maxq, pc.scale, out=out, workspace=pws)
     e[1].record()
     torch.cuda.synchronize()
     pre_ms = e[0].elapsed_time(e[1]) / steps

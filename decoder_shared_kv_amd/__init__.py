@@ -10,6 +10,7 @@ from .xattn import (  # noqa: F401
     LIB_PATH,
     SharedKV,
     YocoError,
+    alloc_prefill_workspace,
     alloc_workspace,
     decode_splits,
     gret_decode,

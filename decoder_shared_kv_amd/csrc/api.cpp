@@ -148,9 +148,20 @@ yoco_status append_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const
   return YOCO_OK;
 }
 
+// Workgroups of the persistent bf16 prefill grid: one per CU of the current
+// device (a workgroup's 128 KB of LDS leaves room for one).
+hipError_t persistent_workgroups(int* wgs) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  err = hipDeviceGetAttribute(wgs, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err == hipSuccess && *wgs < 1) *wgs = 1;
+  return err;
+}
+
 yoco_status prefill_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
                          const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q, int32_t window, void* out,
-                         float* lse, void* stream) {
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
   st = check_cache(cache);
@@ -159,6 +170,8 @@ yoco_status prefill_impl(const yoco_dims* dims, const yoco_kv_cache* cache, cons
   if (!aligned16(q) || !aligned16(out) || !aligned4(cu_seqlens_q)) return YOCO_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned4(lse)) return YOCO_ERR_INVALID_ARG;
   if (max_q_len < 0 || total_q < 0) return YOCO_ERR_INVALID_ARG;
+  const bool queue = workspace != nullptr && dims->dtype == YOCO_DTYPE_BF16;
+  if (queue && (!aligned16(workspace) || workspace_bytes < yoco::kPrefillQueueBytes)) return YOCO_ERR_WORKSPACE;
   if (total_q == 0) return YOCO_OK;
   AttnParams p = base_params(dims, cache);
   p.q = q;
@@ -175,7 +188,15 @@ yoco_status prefill_impl(const yoco_dims* dims, const yoco_kv_cache* cache, cons
     const int64_t blocks = (len + ppw - 1) / ppw;
     if (blocks * units > INT32_MAX / 2 || units > INT32_MAX) return YOCO_ERR_UNSUPPORTED;
     p.pos_blocks = (int32_t)blocks;
-    const int64_t grid = yoco::prefill_grid((int)units, (int)blocks);
+    const int64_t items = yoco::prefill_grid((int)units, (int)blocks);
+    p.n_items = (int32_t)items;
+    int64_t grid = items;
+    if (queue) {
+      int wgs = 0;
+      if (persistent_workgroups(&wgs) != hipSuccess) return YOCO_ERR_HIP;
+      p.queue = static_cast<int32_t*>(workspace);
+      if (grid > wgs) grid = wgs;
+    }
     err = yoco::launch_prefill_bf16(p, dims->head_dim, (int)grid, static_cast<hipStream_t>(stream));
   } else {
     const int64_t units = (int64_t)dims->batch * dims->num_q_heads;
@@ -248,15 +269,18 @@ yoco_status yoco_kv_append_ring(const yoco_dims* dims, const yoco_kv_cache* cach
 
 yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
                                const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q, void* out,
-                               float* lse, void* stream) {
-  return prefill_impl(dims, cache, q, cu_seqlens_q, max_q_len, total_q, 0, out, lse, stream);
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(dims, cache, q, cu_seqlens_q, max_q_len, total_q, 0, out, lse, workspace, workspace_bytes,
+                      stream);
 }
 
 yoco_status yoco_xattn_prefill_window(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
                                       const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q,
-                                      int32_t window, void* out, float* lse, void* stream) {
+                                      int32_t window, void* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   if (window < 1) return YOCO_ERR_INVALID_ARG;
-  return prefill_impl(dims, cache, q, cu_seqlens_q, max_q_len, total_q, window, out, lse, stream);
+  return prefill_impl(dims, cache, q, cu_seqlens_q, max_q_len, total_q, window, out, lse, workspace,
+                      workspace_bytes, stream);
 }
 
 yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len, int64_t total_kv_len,
@@ -271,11 +295,14 @@ yoco_status yoco_xattn_decode_splits(const yoco_dims* dims, int32_t max_kv_len, 
   return YOCO_OK;
 }
 
-yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes) {
+yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_len, int32_t is_decode, size_t* bytes) {
   yoco_status st = check_dims(dims);
   if (st != YOCO_OK) return st;
-  if (bytes == nullptr || max_kv_len < 0) return YOCO_ERR_INVALID_ARG;
-  *bytes = decode_workspace(dims, decode_shares(dims, max_kv_len, 0));
+  if (bytes == nullptr || max_len < 0) return YOCO_ERR_INVALID_ARG;
+  if (is_decode)
+    *bytes = decode_workspace(dims, decode_shares(dims, max_len, 0));
+  else
+    *bytes = dims->dtype == YOCO_DTYPE_BF16 ? yoco::kPrefillQueueBytes : 0;
   return YOCO_OK;
 }
 

@@ -27,6 +27,8 @@ struct AttnParams {
   int32_t window;             // sliding window in positions (0: none, plain causal)
   // prefill grid
   int32_t pos_blocks;         // position blocks covering max_q_len
+  int32_t n_items;            // (unit, position block) work items of the prefill schedule
+  int32_t* queue;             // prefill work queue counters (workspace), or null for the static grid
   // decode split plan: the row blocks of all sequences are cut into `splits`
   // equal shares per column (bf16: KV head x head chunk; f32: query head)
   int32_t splits;
@@ -155,6 +157,19 @@ __host__ __device__ inline void prefill_schedule(int bid, int units, int pos_blo
     *rank = bid % pos_blocks;
   }
 }
+
+// Prefill work queue (bf16 prefill with a workspace). The items are the
+// workgroups of the static schedule above, item i belonging to XCD i % 8; a
+// persistent grid of one workgroup per CU takes them from per-XCD queues
+// (queue x holds items x, x + 8, ... in schedule order) through atomic
+// counters, and a workgroup whose own queue is empty takes items from the
+// others, so faster XCDs absorb the tail. Counter layout (int32, one per
+// 128-byte line): queues 0..7, then the count of workgroups done; the last
+// workgroup to finish sets all of them back to zero, so the counters are zero
+// between calls (the caller zeroes them once, when the workspace is allocated).
+constexpr int kQueueStride = 32;                       // int32 per counter line
+constexpr int kQueueCounters = kXcds + 1;
+constexpr size_t kPrefillQueueBytes = 2048;            // >= kQueueCounters * kQueueStride * 4
 
 // fp32 prefill: one thread per query row, 64 rows per workgroup
 constexpr int kPrefillF32Rows = 64;

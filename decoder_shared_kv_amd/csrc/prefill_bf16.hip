@@ -359,6 +359,46 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
   }
 }
 
+// Work-queue fetch (thread 0 of a workgroup): the next item of this XCD's
+// queue, else of the first other queue that still has items; n_items when all
+// are empty. The counters of all queues are read in one round trip, then one
+// is incremented; a lost race (the queue emptied meanwhile) reads again.
+__device__ __forceinline__ int queue_fetch(int* q, int xcd, int n_items) {
+  for (;;) {
+    int cnt[kXcds];
+#pragma unroll
+    for (int x = 0; x < kXcds; ++x)
+      cnt[x] = __hip_atomic_load(q + x * kQueueStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int pick = -1, len = 0;
+#pragma unroll
+    for (int k = 0; k < kXcds; ++k) {
+      const int x = (xcd + k) & (kXcds - 1);
+      const int lx = n_items > x ? (n_items - x + kXcds - 1) / kXcds : 0;
+      if (pick < 0 && cnt[x] < lx) pick = x, len = lx;
+    }
+    if (pick < 0) return n_items;
+    const int j = __hip_atomic_fetch_add(q + pick * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (j < len) return pick + kXcds * j;
+  }
+}
+
+// With units a multiple of the XCD count, queue x lists its units one after
+// the other, P = pos_blocks items each. An empty item means that its unit's
+// sequence has fewer position blocks (nb) than P: the unit's other empty items
+// are skipped at once by raising the queue's counter past them (causal order:
+// the first P - nb items of a unit are empty; window order: the last P - nb).
+__device__ __forceinline__ void skip_empty_items(const AttnParams& p, int item, int units, int nb) {
+  if (units % kXcds != 0) return;
+  const int x = item % kXcds, j = item / kXcds;
+  const int P = p.pos_blocks;
+  const int first = (j / P) * P;
+  int target;
+  if (p.window > 0 || nb <= 0 || nb >= P) target = first + P;   // the unit's remaining items are empty
+  else target = first + (P - nb);                                 // its first non-empty item
+  if (target > j + 1)
+    __hip_atomic_fetch_max(p.queue + x * kQueueStride, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int D>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnParams p) {
   constexpr int kStage = Geom<D>::kStageBytes;
@@ -376,30 +416,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
   const int ppw = kPrefillWaves / hpw;
   const int hchunks = p.group / hpw;
   const int units = p.batch * p.hkv * hchunks;
-  int unit, rank;
-  prefill_schedule(blockIdx.x, units, p.pos_blocks, &unit, &rank);
-  if (rank >= p.pos_blocks) return;
-  const int hc = unit % hchunks;
-  const int kh = (unit / hchunks) % p.hkv;
-  const int b = unit / (hchunks * p.hkv);
-  // wave -> (head, position block): heads fastest
-  const int h = kh * p.group + hc * hpw + wave % hpw;
-  const int pbl = wave / hpw;
   const int pos_per_wg = kPrefillRowsPerWave * ppw;
   const float c = p.scale_log2;
-
-  int64_t start;
-  const int32_t n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
-  int64_t q0 = p.cu_seqlens[b];
-  int64_t q1 = p.cu_seqlens[b + 1];
-  if (q1 > p.total_q) q1 = p.total_q;
-  if (q0 < 0 || q0 > q1) return;
-  const int32_t n_q = (int32_t)(q1 - q0);
-  const int32_t offset = n_kv > n_q ? n_kv - n_q : 0;
-
   const int64_t row_stride = (int64_t)p.hkv * D;
-  const __bf16* kbase = static_cast<const __bf16*>(p.k) + start * row_stride + (int64_t)kh * D;
-  const __bf16* vbase = static_cast<const __bf16*>(p.v) + start * row_stride + (int64_t)kh * D;
   const __bf16* qbase = static_cast<const __bf16*>(p.q);
 
   Issue<D> is;
@@ -408,12 +427,60 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
   make_read_offs<D>(ro, lane);
   constexpr int L = 2 * Geom<D>::kLoads;   // loads per thread and tile
 
+  // Work items: with a queue, this (persistent) workgroup takes items until
+  // every queue is empty; the next item is fetched by thread 0 while the
+  // current one's first tiles are in flight and handed over through LDS
+  // (two slots, alternating, so a slot is rewritten only after a later barrier).
+  __shared__ int s_item[2];
+  const bool dyn = p.queue != nullptr;
+  const int xcd = blockIdx.x % kXcds;
+  int par = 0;
+  int item = blockIdx.x;
+  if (dyn) {
+    if (threadIdx.x == 0) s_item[0] = queue_fetch(p.queue, xcd, p.n_items);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item[0]);   // uniform: everything derived stays scalar
+    par = 1;
+  }
+  while (item < p.n_items) {
+  int unit, rank;
+  prefill_schedule(item, units, p.pos_blocks, &unit, &rank);
+  const int hc = unit % hchunks;
+  const int kh = (unit / hchunks) % p.hkv;
+  const int b = unit / (hchunks * p.hkv);
+  // wave -> (head, position block): heads fastest
+  const int h = kh * p.group + hc * hpw + wave % hpw;
+  const int pbl = wave / hpw;
+
+  int64_t start = 0;
+  int32_t n_kv = 0, n_q = 0;
+  if (rank < p.pos_blocks && b < p.batch) {
+    n_kv = readable_rows(p.seq_start, p.seq_len, p.seq_cap, p.pool_rows, b, &start);
+    int64_t q0_ = p.cu_seqlens[b];
+    int64_t q1_ = p.cu_seqlens[b + 1];
+    if (q1_ > p.total_q) q1_ = p.total_q;
+    if (q0_ >= 0 && q0_ <= q1_) n_q = (int32_t)(q1_ - q0_);
+  }
+  const int64_t q0 = n_q > 0 ? p.cu_seqlens[b] : 0;
+  const int32_t offset = n_kv > n_q ? n_kv - n_q : 0;
+
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + start * row_stride + (int64_t)kh * D;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + start * row_stride + (int64_t)kh * D;
+
   // causal: longest position blocks first (the last finish with the short ones).
   // Sliding window: blocks are (nearly) equally long, so workgroups started
   // together would also load and store together, each round; shortest first
   // (the first window's blocks are shorter) spreads their phases after round
   // one (+2-3% at C = 1024)
   const int pw0 = p.window > 0 ? rank : p.pos_blocks - 1 - rank;
+  // the next item of this XCD's queue is claimed now (thread 0) and its index
+  // read only at the end, so the atomic's round trip overlaps this item
+  int spec = 0;
+  if (dyn && threadIdx.x == 0) {
+    spec = __hip_atomic_fetch_add(p.queue + xcd * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (pw0 < 0 || pw0 * pos_per_wg >= n_q)   // an empty item (a position block past its sequence's end)
+      skip_empty_items(p, item, units, (n_q + pos_per_wg - 1) / pos_per_wg);
+  }
   for (int pw = pw0; pw >= 0 && pw * pos_per_wg < n_q; pw += p.pos_blocks) {
     const int wg_last_row = min(n_q, (pw + 1) * pos_per_wg) - 1;
     const int wg_last_key = min(wg_last_row + offset, n_kv - 1);
@@ -515,6 +582,24 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
             *reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8);
     }
     __syncthreads();  // the staging area is the next pass's first stage
+  }
+  if (!dyn) break;
+  if (threadIdx.x == 0) {
+    const int own = p.n_items > xcd ? (p.n_items - xcd + kXcds - 1) / kXcds : 0;
+    s_item[par] = spec < own ? xcd + kXcds * spec : queue_fetch(p.queue, xcd, p.n_items);
+  }
+  __syncthreads();
+  item = __builtin_amdgcn_readfirstlane(s_item[par]);
+  par ^= 1;
+  }
+  if (dyn && threadIdx.x == 0) {
+    // every workgroup has left its fetch loop once the done count reaches the
+    // grid: the last one zeroes the counters for the next call
+    int* q = p.queue;
+    const int done = __hip_atomic_fetch_add(q + kXcds * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (int)gridDim.x - 1)
+      for (int i = 0; i < kQueueCounters; ++i)
+        __hip_atomic_store(q + i * kQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

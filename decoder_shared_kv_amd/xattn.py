@@ -79,8 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.yoco_kv_append.argtypes = [dims_p, cache_p, P, P, P, P]
     lib.yoco_kv_append_ring.argtypes = [dims_p, cache_p, P, P, P, P]
-    lib.yoco_xattn_prefill.argtypes = [dims_p, cache_p, P, P, i32, i64, P, P, P]
-    lib.yoco_xattn_prefill_window.argtypes = [dims_p, cache_p, P, P, i32, i64, i32, P, P, P]
+    sz = ctypes.c_size_t
+    lib.yoco_xattn_prefill.argtypes = [dims_p, cache_p, P, P, i32, i64, P, P, P, sz, P]
+    lib.yoco_xattn_prefill_window.argtypes = [dims_p, cache_p, P, P, i32, i64, i32, P, P, P, sz, P]
     lib.yoco_xattn_decode.argtypes = [dims_p, cache_p, P, i32, i64, P, P, P, ctypes.c_size_t, P]
     lib.yoco_xattn_decode_noalloc.argtypes = [dims_p, cache_p, P, i32, i64, P, P, P]
     lib.yoco_xattn_decode_window.argtypes = [dims_p, cache_p, P, i32, i64, i32, P, P, P, ctypes.c_size_t, P]
@@ -91,7 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_gret_workspace_size.argtypes = [gdims_p, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.yoco_gret_prefill.argtypes = [gdims_p, P, P, P, P, P, i64, i32, P, P, P, P, ctypes.c_size_t, P]
     lib.yoco_gret_decode.argtypes = [gdims_p, P, P, P, P, P, P, P]
-    lib.yoco_xattn_workspace_size.argtypes = [dims_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.yoco_xattn_workspace_size.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.yoco_xattn_decode_splits.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                              ctypes.POINTER(ctypes.c_int32)]
     lib.yoco_status_string.argtypes = [ctypes.c_int]
@@ -228,8 +229,9 @@ def kv_append_ring(cache: SharedKV, k_new: torch.Tensor, v_new: torch.Tensor, fl
                                    _stream(stream)), "yoco_kv_append_ring")
 
 
-def _prefill_args(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, out, lse):
+def _prefill_args(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, out, lse, workspace):
     desc = cache.descriptor()
+    _need(workspace, "workspace", torch.uint8, device=cache.k.device, optional=True)
     _queries(cache, q)
     total_q, hq, _ = q.shape
     if cu_seqlens is None or cu_seqlens.dim() != 1 or int(cu_seqlens.shape[0]) != int(cache.seq_len.shape[0]) + 1:
@@ -241,40 +243,57 @@ def _prefill_args(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, ou
     return desc, out
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else int(t.numel() * t.element_size())
+
+
 def xattn_prefill(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, max_q_len: int, scale: float,
-                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
-    """Causal prefill over packed queries q [total_q, Hq, d]; returns out (and fills lse [Hq, total_q])."""
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Causal prefill over packed queries q [total_q, Hq, d]; returns out (and fills lse [Hq, total_q]).
+
+    workspace: the work queue (alloc_prefill_workspace: zeroed once, left zero by
+    every call), or None for the static grid."""
     lib = load_library()
-    desc, out = _prefill_args(cache, q, cu_seqlens, out, lse)
+    desc, out = _prefill_args(cache, q, cu_seqlens, out, lse, workspace)
     total_q, hq, _ = q.shape
     dims = _dims_for(cache, hq, scale, int(cu_seqlens.shape[0]) - 1)
     _check(lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), _ptr(cu_seqlens), int(max_q_len),
-                                  int(total_q), _ptr(out), _ptr(lse), _stream(stream)), "yoco_xattn_prefill")
+                                  int(total_q), _ptr(out), _ptr(lse), _ptr(workspace), _nbytes(workspace),
+                                  _stream(stream)), "yoco_xattn_prefill")
     return out
 
 
 def xattn_prefill_window(cache: SharedKV, q: torch.Tensor, cu_seqlens: torch.Tensor, max_q_len: int, window: int,
                          scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                         stream=None):
+                         stream=None, workspace: Optional[torch.Tensor] = None):
     """Sliding-window prefill: row at position p attends rows max(0, p - window + 1) .. p."""
     lib = load_library()
-    desc, out = _prefill_args(cache, q, cu_seqlens, out, lse)
+    desc, out = _prefill_args(cache, q, cu_seqlens, out, lse, workspace)
     total_q, hq, _ = q.shape
     dims = _dims_for(cache, hq, scale, int(cu_seqlens.shape[0]) - 1)
     _check(lib.yoco_xattn_prefill_window(ctypes.byref(dims), ctypes.byref(desc), _ptr(q), _ptr(cu_seqlens),
                                          int(max_q_len), int(total_q), int(window), _ptr(out), _ptr(lse),
-                                         _stream(stream)), "yoco_xattn_prefill_window")
+                                         _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "yoco_xattn_prefill_window")
     return out
 
 
 def workspace_size(batch: int, q_heads: int, kv_heads: int, head_dim: int, dtype: torch.dtype,
-                   max_kv_len: int) -> int:
+                   max_len: int, is_decode: bool = True) -> int:
+    """Workspace bytes of a decode call (is_decode) or of a prefill call (its work queue)."""
     lib = load_library()
     dims = make_dims(batch, q_heads, kv_heads, head_dim, dtype, 1.0)
     n = ctypes.c_size_t(0)
-    _check(lib.yoco_xattn_workspace_size(ctypes.byref(dims), int(max_kv_len), ctypes.byref(n)),
+    _check(lib.yoco_xattn_workspace_size(ctypes.byref(dims), int(max_len), int(bool(is_decode)), ctypes.byref(n)),
            "yoco_xattn_workspace_size")
     return int(n.value)
+
+
+def alloc_prefill_workspace(device, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """A zeroed prefill work-queue workspace (reused as is: every call leaves it zero)."""
+    n = workspace_size(1, 1, 1, 128, dtype, 1, is_decode=False)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def decode_splits(batch: int, q_heads: int, kv_heads: int, head_dim: int, dtype: torch.dtype, max_kv_len: int,

@@ -113,12 +113,25 @@ yoco_status yoco_kv_append(const yoco_dims* dims, const yoco_kv_cache* cache,
  *   total_q    [host] rows of q, out and columns of lse
  *   out        [device] [total_q, Hq, head_dim]
  *   lse        [device] fp32 [Hq, total_q] or NULL
- * No workspace is needed.
+ *   workspace  [device] the bf16 kernels' work queue: >=
+ *              yoco_xattn_workspace_size(dims, max_q_len, 0) bytes (2 KB),
+ *              16-byte aligned, ALL ZERO before its first use (allocate it
+ *              zeroed); every call that completes leaves it zero again (the
+ *              last workgroup resets the counters), so it is reused as is.
+ *              Calls that share it must be serialised, and it must not be
+ *              shared with a decode call (whose partials would overwrite it)
+ *              unless zeroed again. With a queue, one persistent workgroup per
+ *              CU takes (KV group, position block) items from per-XCD queues
+ *              and takes over other XCDs' items when its own run out, so no
+ *              XCD waits for a slower one at the end. NULL: the static grid
+ *              (one workgroup per item), same results. fp32 ignores it.
+ * YOCO_ERR_WORKSPACE: workspace misaligned or smaller than needed.
  */
 yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache,
                                const void* q, const int32_t* cu_seqlens_q,
                                int32_t max_q_len, int64_t total_q,
-                               void* out, float* lse, void* stream);
+                               void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * yoco_xattn_decode -- one query per sequence against the whole shared cache.
@@ -139,7 +152,7 @@ yoco_status yoco_xattn_prefill(const yoco_dims* dims, const yoco_kv_cache* cache
  *              the number of shares follows it (at most 512 or 1024 workgroups)
  *   out        [device] [B, Hq, head_dim]; a sequence with no rows gets O = 0
  *   lse        [device] fp32 [B, Hq] or NULL; -inf for a sequence with no rows
- *   workspace  [device] >= yoco_xattn_workspace_size(dims, max_kv_len) bytes,
+ *   workspace  [device] >= yoco_xattn_workspace_size(dims, max_kv_len, 1) bytes,
  *              16-byte aligned; contents need no initialisation and are
  *              overwritten. Calls that share a workspace must be serialised.
  */
@@ -160,7 +173,7 @@ yoco_status yoco_xattn_decode(const yoco_dims* dims, const yoco_kv_cache* cache,
  * on each GPU it runs on until the process ends (its device address is looked
  * up on the first call on that device, which must be the current device of
  * the calling thread). Calls whose plan needs more partial space than that
- * (yoco_xattn_workspace_size(dims, max_kv_len) > YOCO_NOALLOC_SCRATCH_BYTES,
+ * (yoco_xattn_workspace_size(dims, max_kv_len, 1) > YOCO_NOALLOC_SCRATCH_BYTES,
  * e.g. hundreds of sequences) return YOCO_ERR_WORKSPACE and launch nothing.
  * The call allocates and frees nothing (no hipMalloc, no library allocator).
  * Every call on one GPU shares that GPU's scratch, which keeps the last call's
@@ -190,12 +203,14 @@ yoco_status yoco_xattn_decode_noalloc(const yoco_dims* dims, const yoco_kv_cache
  * r at position p (as in yoco_xattn_prefill) attends rows max(0, p - window + 1)
  * .. p. window >= 1 (YOCO_ERR_INVALID_ARG otherwise); a window of at least the
  * sequence length gives yoco_xattn_prefill's result. Tiles wholly outside every
- * row's window are neither loaded nor computed.
+ * row's window are neither loaded nor computed. Workspace as for
+ * yoco_xattn_prefill.
  */
 yoco_status yoco_xattn_prefill_window(const yoco_dims* dims, const yoco_kv_cache* cache,
                                       const void* q, const int32_t* cu_seqlens_q,
                                       int32_t max_q_len, int64_t total_q, int32_t window,
-                                      void* out, float* lse, void* stream);
+                                      void* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * yoco_xattn_decode_window -- yoco_xattn_decode over a full (linear) cache with
@@ -336,10 +351,14 @@ yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const v
 yoco_status yoco_gret_decode(const yoco_gret_dims* dims, const void* q, const void* k, const void* v,
                              const float* gamma, float* state, void* out, void* stream);
 
-/* [host] Workspace bytes yoco_xattn_decode needs for this max_kv_len (any
- * total_kv_len, any smaller max_kv_len): per query head one fp32 partial
- * (head_dim + 2 values) per share and sequence, and two int32 per sequence. */
-yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_kv_len, size_t* bytes);
+/* [host] Workspace bytes of a call. is_decode != 0: yoco_xattn_decode (and
+ * yoco_xattn_decode_window) with this max_kv_len (any total_kv_len, any smaller
+ * max_kv_len): per query head one fp32 partial (head_dim + 2 values) per share
+ * and sequence, and two int32 per sequence. is_decode == 0: yoco_xattn_prefill
+ * (and _window) with any max_q_len: the work queue's counters, 2 KB for bf16,
+ * 0 for fp32. */
+yoco_status yoco_xattn_workspace_size(const yoco_dims* dims, int32_t max_len, int32_t is_decode,
+                                      size_t* bytes);
 
 /* [host] The split plan yoco_xattn_decode uses (for reports and tests):
  * *splits = shares per KV head (bf16) or per query head (fp32),

@@ -16,14 +16,30 @@ def device_cache(k_pool, v_pool, seq_start, seq_len, seq_cap) -> dk.SharedKV:
                        seq_len.to(DEV).clone(), seq_cap.to(DEV))
 
 
-def run_prefill(case: synth.PrefillCase, layer: int = 0, cache: dk.SharedKV = None, with_lse: bool = True):
+_QUEUE = {}
+
+
+def prefill_workspace() -> torch.Tensor:
+    """One zeroed work-queue workspace per process, reused by every prefill call
+    (each completed call leaves it zero); tests check that it stays zero."""
+    if "ws" not in _QUEUE:
+        _QUEUE["ws"] = dk.alloc_prefill_workspace(DEV)
+    return _QUEUE["ws"]
+
+
+def run_prefill(case: synth.PrefillCase, layer: int = 0, cache: dk.SharedKV = None, with_lse: bool = True,
+                queue: bool = True, max_q: int = None):
+    """Prefill through the library: with the work queue (the launch configuration
+    the benchmark times) unless queue=False (the static grid)."""
     if cache is None:
         cache = device_cache(case.k_pool, case.v_pool, case.seq_start, case.seq_len, case.seq_cap)
     q = case.q[layer].to(DEV)
     hq = q.shape[1]
     lse = torch.full((hq, case.total_q), float("nan"), device=DEV) if with_lse else None
-    max_q = int((case.cu_seqlens[1:] - case.cu_seqlens[:-1]).max()) if case.cu_seqlens.numel() > 1 else 0
-    out = dk.xattn_prefill(cache, q, case.cu_seqlens.to(DEV), max_q, case.scale, lse=lse)
+    if max_q is None:
+        max_q = int((case.cu_seqlens[1:] - case.cu_seqlens[:-1]).max()) if case.cu_seqlens.numel() > 1 else 0
+    ws = prefill_workspace() if queue else None
+    out = dk.xattn_prefill(cache, q, case.cu_seqlens.to(DEV), max_q, case.scale, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     return f64(out), (lse.cpu().numpy().astype(np.float64) if with_lse else None)
 

@@ -65,8 +65,10 @@ def _dims(**kw):
 def test_dims_rejected_everywhere(lib, bad, code):
     dims, cache = _dims(**bad), _cache()
     ws = ctypes.c_size_t(0)
-    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 10, ctypes.byref(ws)) == code
-    assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None) == code
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 10, 1, ctypes.byref(ws)) == code
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 10, 0, ctypes.byref(ws)) == code
+    assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None, 0,
+                                  None) == code
     assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, 0, FAKE, None, FAKE, 1 << 30,
                                  None) == code
     assert lib.yoco_kv_append(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, None, None) == code
@@ -76,7 +78,8 @@ def test_dims_rejected_everywhere(lib, bad, code):
                                  dict(seq_len=None), dict(seq_cap=None), dict(pool_rows=-1), dict(seq_start=FAKE + 4)])
 def test_cache_rejected(lib, bad):
     dims, cache = _dims(), _cache(**bad)
-    assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None) == 1
+    assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None, None, 0,
+                                  None) == 1
     assert lib.yoco_kv_append(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, None, None) == 1
     assert lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), FAKE, 10, 0, FAKE, None, FAKE, 1 << 30,
                                  None) == 1
@@ -84,14 +87,14 @@ def test_cache_rejected(lib, bad):
 
 def test_null_structs(lib):
     cache, dims = _cache(), _dims()
-    assert lib.yoco_xattn_prefill(None, ctypes.byref(cache), FAKE, FAKE, 1, 1, FAKE, None, None) == 1
-    assert lib.yoco_xattn_prefill(ctypes.byref(dims), None, FAKE, FAKE, 1, 1, FAKE, None, None) == 1
-    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5, None) == 1
+    assert lib.yoco_xattn_prefill(None, ctypes.byref(cache), FAKE, FAKE, 1, 1, FAKE, None, None, 0, None) == 1
+    assert lib.yoco_xattn_prefill(ctypes.byref(dims), None, FAKE, FAKE, 1, 1, FAKE, None, None, 0, None) == 1
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5, 1, None) == 1
 
 
 def test_prefill_argument_checks(lib):
     dims, cache = _dims(), _cache()
-    P = lambda *a: lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    P = lambda *a: lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), *a[:-1], None, 0, a[-1])  # noqa: E731
     assert P(None, FAKE, 10, 10, FAKE, None, None) == 1          # q
     assert P(FAKE, None, 10, 10, FAKE, None, None) == 1          # cu_seqlens
     assert P(FAKE, FAKE, 10, 10, None, None, None) == 1          # out
@@ -101,12 +104,23 @@ def test_prefill_argument_checks(lib):
     assert P(FAKE, FAKE, -1, 10, FAKE, None, None) == 1          # max_q_len
     assert P(FAKE, FAKE, 10, -5, FAKE, None, None) == 1          # total_q
     assert P(FAKE, FAKE, 10, 0, FAKE, None, None) == 0           # nothing to do, nothing launched
+    # the work-queue workspace: 2 KB for bf16 (0 for fp32), 16-byte aligned
+    need = ctypes.c_size_t(0)
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 1 << 20, 0, ctypes.byref(need)) == 0 and need.value == 2048
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(_dims(dtype=0)), 10, 0, ctypes.byref(need)) == 0
+    assert need.value == 0
+    Q = lambda *a: lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 10, FAKE, None,
+                                          *a, None)  # noqa: E731
+    assert Q(FAKE, 2047) == 3                                     # too small
+    assert Q(FAKE + 8, 2048) == 3                                 # misaligned
+    assert lib.yoco_xattn_prefill(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, 10, 0, FAKE, None, FAKE, 2048,
+                                  None) == 0                     # nothing to do, nothing launched
 
 
 def test_decode_workspace_checks(lib):
     dims, cache = _dims(batch=2), _cache()
     need = ctypes.c_size_t(0)
-    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5000, ctypes.byref(need)) == 0
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5000, 1, ctypes.byref(need)) == 0
     assert need.value > 0
     D = lambda *a: lib.yoco_xattn_decode(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
     assert D(FAKE, 5000, 0, FAKE, None, None, need.value, None) == 3
@@ -130,8 +144,9 @@ def test_append_argument_checks(lib):
 def test_window_argument_checks(lib):
     dims, cache = _dims(batch=2), _cache()
     need = ctypes.c_size_t(0)
-    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5000, ctypes.byref(need)) == 0
-    PW = lambda *a: lib.yoco_xattn_prefill_window(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(dims), 5000, 1, ctypes.byref(need)) == 0
+    PW = lambda *a: lib.yoco_xattn_prefill_window(ctypes.byref(dims), ctypes.byref(cache), *a[:-1], None, 0,
+                                                  a[-1])  # noqa: E731
     DW = lambda *a: lib.yoco_xattn_decode_window(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
     for w in (0, -1, -1024):
         assert PW(FAKE, FAKE, 10, 10, w, FAKE, None, None) == 1
@@ -142,7 +157,7 @@ def test_window_argument_checks(lib):
     assert DW(FAKE, 5000, 0, 64, FAKE, None, FAKE + 4, need.value, None) == 3
     assert DW(FAKE, 5000, 0, 64, FAKE, None, None, need.value, None) == 3
     assert lib.yoco_xattn_prefill_window(ctypes.byref(_dims(head_dim=96)), ctypes.byref(cache), FAKE, FAKE, 10,
-                                         10, 64, FAKE, None, None) == 2
+                                         10, 64, FAKE, None, None, 0, None) == 2
     A = lambda *a: lib.yoco_kv_append_ring(ctypes.byref(dims), ctypes.byref(cache), *a)  # noqa: E731
     assert A(None, FAKE, None, None) == 1
     assert A(FAKE, FAKE + 2, None, None) == 1
@@ -283,7 +298,7 @@ def test_noalloc_decode_argument_checks(lib):
     # a plan needing more than the scratch: thousands of sequences of 128 query heads
     big = _dims(batch=4096, num_q_heads=128, num_kv_heads=8)
     need = ctypes.c_size_t(0)
-    assert lib.yoco_xattn_workspace_size(ctypes.byref(big), 100000, ctypes.byref(need)) == 0
+    assert lib.yoco_xattn_workspace_size(ctypes.byref(big), 100000, 1, ctypes.byref(need)) == 0
     assert need.value > X.NOALLOC_SCRATCH_BYTES
     assert N(big, FAKE, 100000, 0, FAKE, None, None) == 3
     # the header's constant and the binding's agree

@@ -6,7 +6,7 @@ import torch
 import decoder_shared_kv_amd as dk
 import parity
 import synth
-from gpu_util import DEV, device_cache, f64, run_decode, run_prefill, say
+from gpu_util import prefill_workspace, DEV, device_cache, f64, run_decode, run_prefill, say
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +96,8 @@ def test_output_canaries_untouched():
     out = big[4:4 + total]
     lse_big = torch.full((8 * total + 64,), 5.0, dtype=torch.float32, device=DEV)
     lse = lse_big[32:32 + 8 * total].view(8, total)
-    dk.xattn_prefill(cache, c.q[0].to(DEV), c.cu_seqlens.to(DEV), 130, c.scale, out=out, lse=lse)
+    dk.xattn_prefill(cache, c.q[0].to(DEV), c.cu_seqlens.to(DEV), 130, c.scale, out=out, lse=lse,
+                     workspace=prefill_workspace())
     torch.cuda.synchronize()
     assert torch.all(big[:4] == 3.0) and torch.all(big[4 + total:] == 3.0)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()

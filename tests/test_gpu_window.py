@@ -14,18 +14,19 @@ import decoder_shared_kv_amd as dk
 import oracle
 import parity
 import synth
-from gpu_util import DEV, device_cache, f64, run_decode, run_prefill, say
+from gpu_util import DEV, device_cache, f64, prefill_workspace, run_decode, run_prefill, say
 
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_window(case, window, layer=0, max_q=None):
+def run_prefill_window(case, window, layer=0, max_q=None, queue=True):
     cache = device_cache(case.k_pool, case.v_pool, case.seq_start, case.seq_len, case.seq_cap)
     q = case.q[layer].to(DEV)
     lse = torch.full((q.shape[1], case.total_q), float("nan"), device=DEV)
     if max_q is None:
         max_q = int((case.cu_seqlens[1:] - case.cu_seqlens[:-1]).max())
-    out = dk.xattn_prefill_window(cache, q, case.cu_seqlens.to(DEV), max_q, window, case.scale, lse=lse)
+    out = dk.xattn_prefill_window(cache, q, case.cu_seqlens.to(DEV), max_q, window, case.scale, lse=lse,
+                                  workspace=prefill_workspace() if queue else None)
     torch.cuda.synchronize()
     return f64(out), lse.cpu().numpy().astype(np.float64)
 
