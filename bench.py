@@ -663,7 +663,7 @@ def bench_gret(args, torch, dk, synth, dev):
     v = torch.randn(N, H, d, device=dev, generator=g).to(torch.bfloat16)
     gam = 0.9 + 0.1 * torch.rand(N, H, device=dev, generator=g)
     cu = torch.tensor([0, N], dtype=torch.int32, device=dev)
-    ws = torch.empty(dk.gret_workspace_size(1, H, d, N), dtype=torch.uint8, device=dev)
+    ws = torch.empty(dk.gret_workspace_size(1, H, d, N), dtype=torch.uint8, device=dev)   # N rows in all
     st = torch.empty(1, H, d, d, device=dev)
     out = torch.empty_like(v)
     qd = (torch.randn(B, H, d, device=dev, generator=g) * std).to(torch.bfloat16)
@@ -675,12 +675,12 @@ def bench_gret(args, torch, dk, synth, dev):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     L = 16
     for _ in range(args.warmup):
-        dk.gret_prefill(q, k, v, gam, cu, N, ws, state_out=st, out=out)
+        dk.gret_prefill(q, k, v, gam, cu, ws, state_out=st, out=out)
         dk.gret_decode(qd, kd, vd, gd, state, out=outd)
     torch.cuda.synchronize()
     ev[0].record()
     for _ in range(args.steps * L):
-        dk.gret_prefill(q, k, v, gam, cu, N, ws, state_out=st, out=out)
+        dk.gret_prefill(q, k, v, gam, cu, ws, state_out=st, out=out)
     ev[1].record()
     ev[2].record()
     for _ in range(args.steps * L):

@@ -406,8 +406,15 @@ struct GretWorkspace {
   size_t state_off, in_off, decay_off, total;
 };
 
-GretWorkspace gret_workspace(const yoco_gret_dims* d, int64_t max_chunks) {
-  const size_t per = (size_t)d->batch * d->num_heads * max_chunks;
+// Chunk slots per head: every sequence's chunks, numbered one after the other,
+// fit ceil(total_rows / 256) + batch slots whatever the lengths (each sequence
+// adds at most one partial chunk).
+int64_t gret_slots(const yoco_gret_dims* d, int64_t total_rows) {
+  return (total_rows + kGretChunk - 1) / kGretChunk + d->batch;
+}
+
+GretWorkspace gret_workspace(const yoco_gret_dims* d, int64_t slots) {
+  const size_t per = (size_t)d->num_heads * slots;
   const size_t dd = (size_t)d->head_dim * d->head_dim;
   GretWorkspace w;
   w.state_off = 0;
@@ -421,16 +428,16 @@ GretWorkspace gret_workspace(const yoco_gret_dims* d, int64_t max_chunks) {
 
 extern "C" {
 
-yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int32_t max_len, size_t* bytes) {
+yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int64_t total_rows, size_t* bytes) {
   yoco_status st = check_gret(dims);
   if (st != YOCO_OK) return st;
-  if (bytes == nullptr || max_len < 0) return YOCO_ERR_INVALID_ARG;
-  *bytes = gret_workspace(dims, ((int64_t)max_len + kGretChunk - 1) / kGretChunk).total;
+  if (bytes == nullptr || total_rows < 0) return YOCO_ERR_INVALID_ARG;
+  *bytes = gret_workspace(dims, gret_slots(dims, total_rows)).total;
   return YOCO_OK;
 }
 
 yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const void* k, const void* v,
-                              const float* gamma, const int32_t* cu_seqlens, int64_t total_rows, int32_t max_len,
+                              const float* gamma, const int32_t* cu_seqlens, int64_t total_rows,
                               const float* state_in, float* state_out, void* out, void* workspace,
                               size_t workspace_bytes, void* stream) {
   yoco_status st = check_gret(dims);
@@ -442,13 +449,11 @@ yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const v
     return YOCO_ERR_INVALID_ARG;
   if ((state_in != nullptr && !aligned16(state_in)) || (state_out != nullptr && !aligned16(state_out)))
     return YOCO_ERR_INVALID_ARG;
-  if (total_rows < 0 || max_len < 0) return YOCO_ERR_INVALID_ARG;
-  const int64_t chunks = ((int64_t)max_len + kGretChunk - 1) / kGretChunk;
-  if (chunks > 65535) return YOCO_ERR_UNSUPPORTED;
-  if (total_rows == 0 || chunks == 0) {
-    if (state_out == nullptr) return YOCO_OK;      // nothing to compute; a state still has to be passed on
-  }
-  const GretWorkspace w = gret_workspace(dims, chunks > 0 ? chunks : 1);
+  if (total_rows < 0) return YOCO_ERR_INVALID_ARG;
+  const int64_t slots = gret_slots(dims, total_rows);
+  if (slots > INT32_MAX || dims->num_heads > 65535) return YOCO_ERR_UNSUPPORTED;
+  if (total_rows == 0 && state_out == nullptr) return YOCO_OK;   // nothing to compute or pass on
+  const GretWorkspace w = gret_workspace(dims, slots);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < w.total) return YOCO_ERR_WORKSPACE;
   yoco::GretParams p{};
   p.q = q;
@@ -466,7 +471,7 @@ yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const v
   p.total_rows = total_rows;
   p.batch = dims->batch;
   p.heads = dims->num_heads;
-  p.max_chunks = (int32_t)(chunks > 0 ? chunks : 1);
+  p.slots = (int32_t)slots;
   if (yoco::launch_gret_prefill(p, dims->head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
     return YOCO_ERR_HIP;
   return YOCO_OK;

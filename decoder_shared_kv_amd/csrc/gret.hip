@@ -4,7 +4,9 @@
 // o_n = Q_n S_n, and the chunkwise form; section 5.3.2: chunks of 256 rows).
 //
 // Prefill runs the chunkwise form in three launches, so that every (sequence,
-// head, chunk) works in parallel and only the cheap state recurrence is serial:
+// head, chunk) works in parallel and only the cheap state recurrence is serial
+// (the chunks of all sequences are numbered one after the other and located on
+// the device, so every row is computed whatever the lengths):
 //   1. gret_state_kernel: per chunk, U = sum_m w_m k_m^T v_m with w_m the decay
 //      from row m to the chunk's end, and the chunk's total decay G
 //      (MFMA: U^T = V^T diag(w) K, both operands by transposing LDS reads);
@@ -118,6 +120,49 @@ struct ChunkInfo {
   int n;          // rows of the chunk (0: no chunk)
 };
 
+// Rows of sequence b (clamped to the packed rows) and its chunks.
+__device__ __forceinline__ int64_t seq_rows(const GretParams& p, int b) {
+  int64_t r0 = p.cu_seqlens[b], r1 = p.cu_seqlens[b + 1];
+  if (r1 > p.total_rows) r1 = p.total_rows;
+  return (r0 >= 0 && r1 > r0) ? r1 - r0 : 0;
+}
+__device__ __forceinline__ int seq_chunks(const GretParams& p, int b) {
+  return (int)((seq_rows(p, b) + kGC - 1) / kGC);
+}
+
+// The chunks of all sequences are numbered one after the other (sequence 0's
+// first), so a grid over the workspace's slots covers every row whatever the
+// lengths. Global chunk g -> (sequence b, its chunk c), counted by the whole
+// wave (64 sequences per step: chunk counts, a DPP prefix sum, a ballot for the
+// first sequence whose prefix passes g). All 64 lanes must be active. False if
+// g is past the last chunk.
+__device__ __forceinline__ bool locate_chunk(const GretParams& p, int g, int* b_out, int* c_out) {
+  const int lane = threadIdx.x & 63;
+  int before = 0;   // chunks of the sequences before this group of 64
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const int bb = b0 + lane;
+    const int n = bb < p.batch ? seq_chunks(p, bb) : 0;
+    const int incl = wave_incl_scan_i32(n);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (g < before + total) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(before + incl > g);
+      const int l = __builtin_ctzll(m);
+      *b_out = b0 + l;
+      *c_out = g - before - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(n, l));
+      return true;
+    }
+    before += total;
+  }
+  return false;
+}
+
+// First global chunk of sequence b (scalar loop over the sequences before it).
+__device__ __forceinline__ int64_t chunk_start(const GretParams& p, int b) {
+  int64_t g = 0;
+  for (int i = 0; i < b; ++i) g += seq_chunks(p, i);
+  return g;
+}
+
 __device__ __forceinline__ ChunkInfo chunk_info(const GretParams& p, int b, int c) {
   int64_t r0 = p.cu_seqlens[b], r1 = p.cu_seqlens[b + 1];
   if (r1 > p.total_rows) r1 = p.total_rows;
@@ -139,16 +184,19 @@ __global__ __launch_bounds__(kGThreads, 2) void gret_state_kernel(GretParams p) 
   __shared__ __attribute__((aligned(16))) float wgt[kGC];
   __shared__ float wsum[4];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, h = blockIdx.y;
+  int b, c;
+  if (!locate_chunk(p, g, &b, &c)) return;
   const ChunkInfo ci = chunk_info(p, b, c);
   if (ci.n == 0) return;
+  const int64_t slot = (int64_t)h * p.slots + g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // decay from row m to the chunk's end: 2^(A_last - A_m), A = prefix of log2 gates
   const float a = log2_gate(p.gamma, ci.row0 + tid, h, p.heads, tid < ci.n);
   const float A = chunk_prefix(a, wsum);
   const float a_last = wsum[0] + wsum[1] + wsum[2] + wsum[3];   // gates past the end count 1
   if (tid < kGC) wgt[tid] = tid < ci.n ? exp2f(a_last - A) : 0.f;
-  if (tid == 0) p.chunk_decay[((int64_t)b * p.heads + h) * p.max_chunks + c] = exp2f(a_last);
+  if (tid == 0) p.chunk_decay[slot] = exp2f(a_last);
   wait_vm_lgkm0<0>();   // the gates are in: from here on only the tile copies are in flight
 
   // K and V of the chunk in quarters of 64 rows through two stages (64 KB of LDS,
@@ -215,7 +263,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gret_state_kernel(GretParams p) 
   }
   if (idle) return;
   // lane holds dk = 32 bj + lane % 32, dv rows 32 bi + 8(r/4) + 4hf + r%4
-  float* u = p.chunk_state + (((int64_t)b * p.heads + h) * p.max_chunks + c) * (D * D);
+  float* u = p.chunk_state + slot * (D * D);
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int bj = (blk0 + e) % NB;
@@ -236,11 +284,10 @@ __global__ __launch_bounds__(256) void gret_scan_kernel(GretParams p) {
   const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;   // element (dv, dk..dk+3) of S^T
   if (e0 >= D * D) return;
   const int dv = e0 / D, dk = e0 % D;
-  int64_t r0 = p.cu_seqlens[b], r1 = p.cu_seqlens[b + 1];
-  if (r1 > p.total_rows) r1 = p.total_rows;
-  const int64_t n = (r0 >= 0 && r1 > r0) ? r1 - r0 : 0;
-  int64_t nc = (n + kGC - 1) / kGC;
-  if (nc > p.max_chunks) nc = p.max_chunks;     // rows past the planned chunks are not computed
+  const int64_t g0 = chunk_start(p, b);
+  int64_t nc = seq_chunks(p, b);
+  // non-decreasing cu_seqlens keep every chunk within the slots; others are clamped to them
+  if (g0 + nc > p.slots) nc = g0 < p.slots ? p.slots - g0 : 0;
   const int64_t bh = (int64_t)b * p.heads + h;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   if (p.state_in != nullptr) {
@@ -250,9 +297,10 @@ __global__ __launch_bounds__(256) void gret_scan_kernel(GretParams p) {
   // the loads do not depend on the state: fetch a group of chunks ahead, then
   // run the (serial) recurrence over the group
   constexpr int kAhead = 8;
-  const float* __restrict__ us = p.chunk_state + bh * p.max_chunks * (D * D) + e0;
-  const float* __restrict__ gs = p.chunk_decay + bh * p.max_chunks;
-  uint16_t* __restrict__ sin = p.chunk_in + bh * p.max_chunks * (D * D) + e0;
+  const int64_t slot0 = (int64_t)h * p.slots + g0;
+  const float* __restrict__ us = p.chunk_state + slot0 * (D * D) + e0;
+  const float* __restrict__ gs = p.chunk_decay + slot0;
+  uint16_t* __restrict__ sin = p.chunk_in + slot0 * (D * D) + e0;
   for (int c0 = 0; c0 < nc; c0 += kAhead) {
     f32x4 u[kAhead];
     float g[kAhead];
@@ -312,7 +360,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   __shared__ float wsum[4];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
   YOCO_LDS float* A_lds = (YOCO_LDS float*)(smem + LY::kA);
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, h = blockIdx.y;
+  int b, c;
+  if (!locate_chunk(p, g, &b, &c)) return;
   const ChunkInfo ci = chunk_info(p, b, c);
   if (ci.n == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -322,7 +372,6 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   const int n_tiles = (ci.n + kGT - 1) / kGT;
   const __bf16* kg = static_cast<const __bf16*>(p.k);
   const __bf16* vg = static_cast<const __bf16*>(p.v);
-  const int64_t bh = (int64_t)b * H + h;
   const bool has_state = c > 0 || p.state_in != nullptr;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int t) {
@@ -340,7 +389,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   }
   if (has_state) {
     constexpr int cpr = D / 8;
-    const __bf16* sg = reinterpret_cast<const __bf16*>(p.chunk_in) + (bh * p.max_chunks + c) * (D * D);
+    const __bf16* sg = reinterpret_cast<const __bf16*>(p.chunk_in) + ((int64_t)h * p.slots + g) * (D * D);
     for (int i = 0; i < D * cpr / kGThreads; ++i) {
       const int q = i * kGThreads + tid;
       const int r = q / cpr, slot = q % cpr;
@@ -548,7 +597,7 @@ __global__ __launch_bounds__(256) void gret_decode_kernel(GretParams p) {
 }  // namespace
 
 hipError_t launch_gret_prefill(const GretParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid_c(p.max_chunks, p.heads, p.batch);
+  const dim3 grid_c(p.slots, p.heads);
   const dim3 grid_s((head_dim * head_dim / 4 + 255) / 256, p.heads, p.batch);
   if (head_dim == 64) {
     hipLaunchKernelGGL(gret_state_kernel<64>, grid_c, dim3(kGThreads), 0, stream, p);

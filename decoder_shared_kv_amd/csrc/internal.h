@@ -91,7 +91,8 @@ struct GretParams {
   int64_t total_rows;
   int32_t batch;
   int32_t heads;
-  int32_t max_chunks;         // chunks of the longest sequence (grid and workspace stride)
+  int32_t slots;              // chunk slots per head in the workspace: ceil(total_rows / 256) + batch,
+                              // at least the chunks of all sequences together for any lengths
 };
 
 // Host launchers (one per kernel family); each returns the hipGetLastError code.

@@ -89,8 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_kv_project_append.argtypes = [dims_p, cache_p, P, P, i64, i32, P, ctypes.c_float,
                                            ctypes.POINTER(Residual), P, P]
     gdims_p = ctypes.POINTER(GretDims)
-    lib.yoco_gret_workspace_size.argtypes = [gdims_p, i32, ctypes.POINTER(ctypes.c_size_t)]
-    lib.yoco_gret_prefill.argtypes = [gdims_p, P, P, P, P, P, i64, i32, P, P, P, P, ctypes.c_size_t, P]
+    lib.yoco_gret_workspace_size.argtypes = [gdims_p, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.yoco_gret_prefill.argtypes = [gdims_p, P, P, P, P, P, i64, P, P, P, P, ctypes.c_size_t, P]
     lib.yoco_gret_decode.argtypes = [gdims_p, P, P, P, P, P, P, P]
     lib.yoco_xattn_workspace_size.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.yoco_xattn_decode_splits.argtypes = [dims_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
@@ -440,10 +440,11 @@ def gret_dims(batch: int, heads: int, head_dim: int, dtype: torch.dtype = torch.
     return GretDims(batch, heads, head_dim, DTYPE_CODE[dtype])
 
 
-def gret_workspace_size(batch: int, heads: int, head_dim: int, max_len: int) -> int:
+def gret_workspace_size(batch: int, heads: int, head_dim: int, total_rows: int) -> int:
+    """Workspace bytes of gret_prefill over total_rows packed rows of up to `batch` sequences."""
     lib = load_library()
     n = ctypes.c_size_t(0)
-    _check(lib.yoco_gret_workspace_size(ctypes.byref(gret_dims(batch, heads, head_dim)), int(max_len),
+    _check(lib.yoco_gret_workspace_size(ctypes.byref(gret_dims(batch, heads, head_dim)), int(total_rows),
                                         ctypes.byref(n)), "yoco_gret_workspace_size")
     return int(n.value)
 
@@ -460,7 +461,7 @@ def _gret_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Te
 
 
 def gret_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, cu_seqlens: torch.Tensor,
-                 max_len: int, workspace: torch.Tensor, state_in: Optional[torch.Tensor] = None,
+                 workspace: torch.Tensor, state_in: Optional[torch.Tensor] = None,
                  state_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
     """Gated retention over packed sequences (q, k, v [T, H, d] bf16, gamma [T, H] fp32); returns out."""
     lib = load_library()
@@ -477,7 +478,7 @@ def gret_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch
     _need(out, "out", torch.bfloat16, q.shape, dev)
     dims = gret_dims(batch, heads, d, q.dtype)
     _check(lib.yoco_gret_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(cu_seqlens),
-                                 int(total), int(max_len), _ptr(state_in), _ptr(state_out), _ptr(out),
+                                 int(total), _ptr(state_in), _ptr(state_out), _ptr(out),
                                  _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                  _stream(stream)), "yoco_gret_prefill")
     return out

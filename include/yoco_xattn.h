@@ -322,25 +322,30 @@ typedef struct {
   int32_t dtype;       /* YOCO_DTYPE_BF16 (fp32 storage: YOCO_ERR_UNSUPPORTED) */
 } yoco_gret_dims;
 
-/* [host] Workspace bytes of yoco_gret_prefill for sequences of at most max_len rows. */
-yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int32_t max_len, size_t* bytes);
+/* [host] Workspace bytes of yoco_gret_prefill for total_rows packed rows (any
+ * number of sequences up to dims->batch, any lengths): per head and chunk slot
+ * (ceil(total_rows / 256) + batch slots) an fp32 and a bf16 head_dim^2 state and
+ * one fp32 decay. */
+yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int64_t total_rows, size_t* bytes);
 
 /*
  * yoco_gret_prefill -- the chunkwise form over packed sequences: sequence b owns
- * rows cu_seqlens[b] .. cu_seqlens[b+1]-1. Three launches: per-chunk state
- * contributions, the state recurrence across chunks, per-chunk outputs.
- *   max_len    [host] the longest sequence's rows; it sizes the grid and the
- *              workspace and MUST be >= every sequence's length (rows past
- *              max_len rounded up to a chunk are not computed)
+ * rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (clamped to total_rows). Three
+ * launches: per-chunk state contributions, the state recurrence across chunks,
+ * per-chunk outputs. The chunks of all sequences are numbered one after the
+ * other and found on the device, so every row of every sequence is computed
+ * whatever the lengths; cu_seqlens must be non-decreasing (otherwise chunks
+ * beyond the workspace's slots are left out, never written out of bounds).
+ *   total_rows [host] rows of q, k, v, gamma and out
  *   state_in   [device] [B, H, d, d] fp32 initial states, or NULL for zero
  *   state_out  [device] [B, H, d, d] fp32 states after each sequence's last row,
  *              or NULL; may be the same buffer as state_in
- *   workspace  [device] >= yoco_gret_workspace_size(dims, max_len), 16-byte
+ *   workspace  [device] >= yoco_gret_workspace_size(dims, total_rows), 16-byte
  *              aligned; needs no initialisation; serialise calls that share it
  */
 yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const void* k, const void* v,
                               const float* gamma, const int32_t* cu_seqlens, int64_t total_rows,
-                              int32_t max_len, const float* state_in, float* state_out, void* out,
+                              const float* state_in, float* state_out, void* out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*

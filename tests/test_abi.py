@@ -197,28 +197,33 @@ def test_gret_argument_checks(lib):
     need = ctypes.c_size_t(0)
     lib.yoco_gret_workspace_size(ctypes.byref(gd), 1000, ctypes.byref(need))
     G = lambda *a: lib.yoco_gret_prefill(ctypes.byref(gd), *a)  # noqa: E731
-    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 500, 1000, None, None, FAKE, FAKE, need.value, None]
-    for i in (0, 1, 2, 3, 4, 9):                        # q, k, v, gamma, cu_seqlens, out
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 1000, None, None, FAKE, FAKE, need.value, None]
+    for i in (0, 1, 2, 3, 4, 8):                        # q, k, v, gamma, cu_seqlens, out
         args = list(ok)
         args[i] = None
         assert G(*args) == 1, i
     args = list(ok); args[0] = FAKE + 8; assert G(*args) == 1          # misaligned q
-    args = list(ok); args[7] = FAKE + 4; assert G(*args) == 1          # misaligned state_in
+    args = list(ok); args[6] = FAKE + 4; assert G(*args) == 1          # misaligned state_in
     args = list(ok); args[5] = -1; assert G(*args) == 1                # total_rows
-    args = list(ok); args[10] = None; assert G(*args) == 3             # workspace
-    args = list(ok); args[11] = need.value - 1; assert G(*args) == 3
+    args = list(ok); args[9] = None; assert G(*args) == 3              # workspace
+    args = list(ok); args[10] = need.value - 1; assert G(*args) == 3
+    args = list(ok); args[5] = 2000; assert G(*args) == 3              # more rows than the workspace was sized for
     args = list(ok); args[5] = 0; assert G(*args) == 0                 # nothing to do, no state: no launch
     D = lambda *a: lib.yoco_gret_decode(ctypes.byref(gd), *a)  # noqa: E731
     assert D(FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
     assert D(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == 1
     assert lib.yoco_gret_decode(ctypes.byref(X.GretDims(2, 4, 128, 0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 None) == 2
-    # a larger max_len never needs less workspace
+    # more rows never need less workspace; the slots bound the chunks of any split of the rows
     sizes = []
     for m in (1, 255, 256, 257, 10000):
         lib.yoco_gret_workspace_size(ctypes.byref(gd), m, ctypes.byref(n))
         sizes.append(n.value)
     assert sizes == sorted(sizes)
+    rows, batch = 1000, 2
+    slots = (rows + 255) // 256 + batch
+    for split in [(0, 1000), (1, 999), (255, 745), (257, 743), (500, 500), (1000, 0)]:
+        assert sum((x + 255) // 256 for x in split) <= slots, split
 
 
 def test_split_plan():

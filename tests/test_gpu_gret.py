@@ -42,9 +42,9 @@ def _state_check(st, ref, what):
 
 def _run_prefill(q, k, v, gam, s0, cu, lens):
     heads, d = q.shape[1], q.shape[2]
-    ws = torch.empty(dk.gret_workspace_size(len(lens), heads, d, max(lens)), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(dk.gret_workspace_size(len(lens), heads, d, sum(lens)), dtype=torch.uint8, device=DEV)
     st = torch.full((len(lens), heads, d, d), float("nan"), device=DEV)
-    out = dk.gret_prefill(q.to(DEV), k.to(DEV), v.to(DEV), gam.to(DEV), cu.to(DEV), max(lens), ws,
+    out = dk.gret_prefill(q.to(DEV), k.to(DEV), v.to(DEV), gam.to(DEV), cu.to(DEV), ws,
                           state_in=None if s0 is None else s0.to(DEV), state_out=st)
     torch.cuda.synchronize()
     return f64(out), st.cpu().numpy().astype(np.float64)
@@ -55,6 +55,8 @@ def _run_prefill(q, k, v, gam, s0, cu, lens):
     ([256, 300, 17], 2, 128, True),     # a whole chunk, a chunk and a bit, a tiny one
     ([700], 3, 64, True),               # head_dim 64
     ([5000, 1234], 4, 128, True),
+    ([3, 600, 0, 257, 1, 90] * 11 + [1300], 2, 128, True),   # 67 sequences (a wave's chunk count and more),
+                                                              # empty and one-row sequences
 ])
 def test_gret_prefill(lens, heads, d, with_state):
     say(f"gret prefill lens={lens} H={heads} d={d} state={with_state}")
