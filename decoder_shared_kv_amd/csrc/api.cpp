@@ -148,17 +148,6 @@ yoco_status append_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const
   return YOCO_OK;
 }
 
-// Workgroups of the persistent bf16 prefill grid: one per CU of the current
-// device (a workgroup's 128 KB of LDS leaves room for one).
-hipError_t persistent_workgroups(int* wgs) {
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  err = hipDeviceGetAttribute(wgs, hipDeviceAttributeMultiprocessorCount, dev);
-  if (err == hipSuccess && *wgs < 1) *wgs = 1;
-  return err;
-}
-
 yoco_status prefill_impl(const yoco_dims* dims, const yoco_kv_cache* cache, const void* q,
                          const int32_t* cu_seqlens_q, int32_t max_q_len, int64_t total_q, int32_t window, void* out,
                          float* lse, void* workspace, size_t workspace_bytes, void* stream) {
@@ -190,14 +179,8 @@ yoco_status prefill_impl(const yoco_dims* dims, const yoco_kv_cache* cache, cons
     p.pos_blocks = (int32_t)blocks;
     const int64_t items = yoco::prefill_grid((int)units, (int)blocks);
     p.n_items = (int32_t)items;
-    int64_t grid = items;
-    if (queue) {
-      int wgs = 0;
-      if (persistent_workgroups(&wgs) != hipSuccess) return YOCO_ERR_HIP;
-      p.queue = static_cast<int32_t*>(workspace);
-      if (grid > wgs) grid = wgs;
-    }
-    err = yoco::launch_prefill_bf16(p, dims->head_dim, (int)grid, static_cast<hipStream_t>(stream));
+    if (queue) p.queue = static_cast<int32_t*>(workspace);   // the launcher sizes the persistent grid
+    err = yoco::launch_prefill_bf16(p, dims->head_dim, (int)items, static_cast<hipStream_t>(stream));
   } else {
     const int64_t units = (int64_t)dims->batch * dims->num_q_heads;
     const int64_t blocks = (len + yoco::kPrefillF32Rows - 1) / yoco::kPrefillF32Rows;

@@ -605,12 +605,33 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid, hipStream_t stream) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(kPrefillThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(kPrefillThreads), 0, stream, p);
+namespace {
+
+// With a work queue the grid is persistent: as many workgroups as the device
+// holds at once (CUs times the kernel's occupancy), each taking items until
+// the queues are empty; without one, one workgroup per item.
+template <int D>
+hipError_t launch_prefill(const AttnParams& p, int items, hipStream_t stream) {
+  int grid = items;
+  if (p.queue != nullptr) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess)
+      err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(prefill_bf16_kernel<D>),
+                                                         kPrefillThreads, 0);
+    if (err != hipSuccess) return err;
+    const int64_t wgs = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    if (grid > wgs) grid = (int)wgs;
+  }
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3(grid), dim3(kPrefillThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int items, hipStream_t stream) {
+  return head_dim == 64 ? launch_prefill<64>(p, items, stream) : launch_prefill<128>(p, items, stream);
 }
 
 }  // namespace yoco
