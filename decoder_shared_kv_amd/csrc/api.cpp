@@ -401,7 +401,7 @@ GretWorkspace gret_workspace(const yoco_gret_dims* d, int64_t slots) {
   const size_t dd = (size_t)d->head_dim * d->head_dim;
   GretWorkspace w;
   w.state_off = 0;
-  w.in_off = (per * dd * 4 + 255) & ~(size_t)255;
+  w.in_off = (per * dd * 2 + 255) & ~(size_t)255;
   w.decay_off = (w.in_off + per * dd * 2 + 255) & ~(size_t)255;
   w.total = w.decay_off + per * 4;
   return w;
@@ -448,7 +448,7 @@ yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const v
   p.state_in = state_in;
   p.state_out = state_out;
   char* ws = static_cast<char*>(workspace);
-  p.chunk_state = reinterpret_cast<float*>(ws + w.state_off);
+  p.chunk_state = reinterpret_cast<uint16_t*>(ws + w.state_off);
   p.chunk_in = reinterpret_cast<uint16_t*>(ws + w.in_off);
   p.chunk_decay = reinterpret_cast<float*>(ws + w.decay_off);
   p.total_rows = total_rows;

@@ -262,15 +262,17 @@ __global__ __launch_bounds__(kGThreads, 2) void gret_state_kernel(GretParams p) 
     }
   }
   if (idle) return;
-  // lane holds dk = 32 bj + lane % 32, dv rows 32 bi + 8(r/4) + 4hf + r%4
-  float* u = p.chunk_state + slot * (D * D);
+  // lane holds dk = 32 bj + lane % 32, dv rows 32 bi + 8(r/4) + 4hf + r%4; stored
+  // as bf16 (the scan adds it to an fp32 state): half the bytes of fp32 for the
+  // store here and the scan's read, for one more rounding of the contribution
+  __bf16* u = reinterpret_cast<__bf16*>(p.chunk_state) + slot * (D * D);
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int bj = (blk0 + e) % NB;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int dv = 32 * bi + 8 * (r >> 2) + 4 * hf + (r & 3);
-      u[dv * D + 32 * bj + (lane & 31)] = acc[e][r];
+      u[dv * D + 32 * bj + (lane & 31)] = (__bf16)acc[e][r];
     }
   }
 }
@@ -298,24 +300,25 @@ __global__ __launch_bounds__(256) void gret_scan_kernel(GretParams p) {
   // run the (serial) recurrence over the group
   constexpr int kAhead = 8;
   const int64_t slot0 = (int64_t)h * p.slots + g0;
-  const float* __restrict__ us = p.chunk_state + slot0 * (D * D) + e0;
+  const uint16_t* __restrict__ us = p.chunk_state + slot0 * (D * D) + e0;
   const float* __restrict__ gs = p.chunk_decay + slot0;
   uint16_t* __restrict__ sin = p.chunk_in + slot0 * (D * D) + e0;
   for (int c0 = 0; c0 < nc; c0 += kAhead) {
-    f32x4 u[kAhead];
+    u32x2 u[kAhead];   // four bf16 contributions
     float g[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
       const int c = c0 + i < nc ? c0 + i : nc - 1;
-      u[i] = *reinterpret_cast<const f32x4*>(us + (int64_t)c * (D * D));
+      u[i] = *reinterpret_cast<const u32x2*>(us + (int64_t)c * (D * D));
       g[i] = gs[c];
     }
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
       if (c0 + i >= nc) break;
       *reinterpret_cast<u32x2*>(sin + (int64_t)(c0 + i) * (D * D)) = u32x2{pack2(s[0], s[1]), pack2(s[2], s[3])};
+      const float uf[4] = {bf16_lo(u[i][0]), bf16_hi(u[i][0]), bf16_lo(u[i][1]), bf16_hi(u[i][1])};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = fmaf(g[i], s[j], u[i][j]);
+      for (int j = 0; j < 4; ++j) s[j] = fmaf(g[i], s[j], uf[j]);
     }
   }
   if (p.state_out != nullptr) {

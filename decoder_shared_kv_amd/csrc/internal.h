@@ -85,7 +85,7 @@ struct GretParams {
   const int32_t* cu_seqlens;  // [B + 1] (prefill)
   const float* state_in;      // [B, H, D(dk), D(dv)] fp32 or null (prefill)
   float* state_out;           // [B, H, D, D]: prefill's final states; decode's states, updated in place
-  float* chunk_state;         // workspace: per chunk U^T [D(dv)][D(dk)] fp32
+  uint16_t* chunk_state;      // workspace: per chunk U^T [D(dv)][D(dk)], bf16 bits
   uint16_t* chunk_in;         // workspace: per chunk incoming state S^T, bf16 bits
   float* chunk_decay;         // workspace: per chunk total decay
   int64_t total_rows;

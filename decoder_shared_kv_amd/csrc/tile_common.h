@@ -21,6 +21,10 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// the low / high bf16 of a packed pair, as float (exact: a bf16 is the top half of an fp32)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // Cross-lane exchanges without LDS (gfx950 v_permlane{16,32}_swap). Called
 // with the same register twice, the swap leaves lanes l and l ^ 32 (resp.
 // l ^ 16) holding each other's value in one of the two results, so combining

@@ -324,8 +324,8 @@ typedef struct {
 
 /* [host] Workspace bytes of yoco_gret_prefill for total_rows packed rows (any
  * number of sequences up to dims->batch, any lengths): per head and chunk slot
- * (ceil(total_rows / 256) + batch slots) an fp32 and a bf16 head_dim^2 state and
- * one fp32 decay. */
+ * (ceil(total_rows / 256) + batch slots) two bf16 head_dim^2 states (the
+ * chunk's contribution and its incoming state) and one fp32 decay. */
 yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int64_t total_rows, size_t* bytes);
 
 /*
