@@ -68,6 +68,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def gret_traffic_fields(call_s):
+    """Measured HBM bytes of one chunkwise gRet prefill call: the three kernels'
+    counter traffic summed, as a rate over the call time, or null when any is
+    absent or was taken on a different version of the kernels."""
+    from bench_counters import traffic_for
+    parts = [traffic_for(k) for k in ("gret_state_kernel<128>", "gret_scan_kernel<128>", "gret_out_kernel<128>")]
+    if any(b is None for b in parts):
+        return {"traffic": None}
+    b = sum(parts)
+    return {"traffic": b / call_s / 1e9, "traffic_unit": "GB/s", "traffic_bytes_per_launch": b}
+
+
 def traffic_fields(kernel, launch_s):
     """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated
     against a plain copy; see bench_counters.py) as a rate over the measured launch
@@ -706,7 +718,7 @@ def bench_gret(args, torch, dk, synth, dev):
                                "decode B=8 H=16 d=128, 16 layer steps", "global_batch": 1, "seq_len": N,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs / HBM_PEAK_GBS, **gret_traffic_fields(call_s),
                      "kernel": "gret_state_kernel + gret_scan_kernel + gret_out_kernel (one call, timed together)",
                      "avg_launch_ms": call_s * 1e3, "algorithmic_per_launch": alg_bytes,
                      "mfma_tflops": tfl, "mfma_flops_per_launch": flops},
