@@ -473,11 +473,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
   // (the first window's blocks are shorter) spreads their phases after round
   // one (+2-3% at C = 1024)
   const int pw0 = p.window > 0 ? rank : p.pos_blocks - 1 - rank;
-  // the next item of this XCD's queue is claimed now (thread 0) and its index
-  // read only at the end, so the atomic's round trip overlaps this item
-  int spec = 0;
+  // The next item of this XCD's queue is claimed while this one runs (thread 0,
+  // once this item's first tiles are in) and its index read only at the end,
+  // so the atomic's round trip overlaps this item. Not near the end of the
+  // queue (within 4 items per workgroup of this XCD, as the counter read when
+  // the item starts shows): an item claimed ahead can no longer go to an idle
+  // workgroup, and held behind a long one it would end the launch late; there
+  // the next item is taken when this one is done.
+  const int own = p.n_items > xcd ? (p.n_items - xcd + kXcds - 1) / kXcds : 0;   // this XCD's queue length
+  int spec = -1, seen = 0;
   if (dyn && threadIdx.x == 0) {
-    spec = __hip_atomic_fetch_add(p.queue + xcd * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seen = __hip_atomic_load(p.queue + xcd * kQueueStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (pw0 < 0 || pw0 * pos_per_wg >= n_q)   // an empty item (a position block past its sequence's end)
       skip_empty_items(p, item, units, (n_q + pos_per_wg - 1) / pos_per_wg);
   }
@@ -521,6 +527,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     // Q^ (and the first tiles) in: from here on the only loads in flight are
     // tile copies, which the loop awaits by count
     wait_vm_lgkm0<0>();
+    if (dyn && threadIdx.x == 0 && pw == pw0 && seen < own - 4 * (int)(gridDim.x / kXcds))
+      spec = __hip_atomic_fetch_add(p.queue + xcd * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
@@ -584,10 +592,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     __syncthreads();  // the staging area is the next pass's first stage
   }
   if (!dyn) break;
-  if (threadIdx.x == 0) {
-    const int own = p.n_items > xcd ? (p.n_items - xcd + kXcds - 1) / kXcds : 0;
-    s_item[par] = spec < own ? xcd + kXcds * spec : queue_fetch(p.queue, xcd, p.n_items);
-  }
+  if (threadIdx.x == 0)
+    s_item[par] = spec >= 0 && spec < own ? xcd + kXcds * spec : queue_fetch(p.queue, xcd, p.n_items);
   __syncthreads();
   item = __builtin_amdgcn_readfirstlane(s_item[par]);
   par ^= 1;
