@@ -41,6 +41,22 @@ __device__ __forceinline__ void lds_barrier() {
   barrier_only();
 }
 
+// Inclusive prefix sum over a wave's lanes on DPP lane moves, no LDS: the same
+// pattern as wave_incl_scan_i32, on fp32 values.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_add(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, BOUND));
+}
+__device__ __forceinline__ float wave_incl_scan_f32(float x) {
+  x += dpp_add<0x111, 0xf, true>(x);    // row_shr:1 (lanes shifted in read 0)
+  x += dpp_add<0x112, 0xf, true>(x);    // row_shr:2
+  x += dpp_add<0x114, 0xf, true>(x);    // row_shr:4
+  x += dpp_add<0x118, 0xf, true>(x);    // row_shr:8
+  x += dpp_add<0x142, 0xa, false>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_add<0x143, 0xc, false>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // inclusive prefix sum of 256 values held by threads 0..255 (one each); every
 // thread of the workgroup must call it. Returns the sum up to and including
 // this thread's value (threads >= 256 get garbage). kWaitAll: the barrier also
@@ -49,11 +65,7 @@ __device__ __forceinline__ void lds_barrier() {
 template <bool kWaitAll = true>
 __device__ __forceinline__ float chunk_prefix(float x, float* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  x = wave_incl_scan_f32(x);
   if (lane == 63 && wave < 4) wsum[wave] = x;
   if constexpr (kWaitAll) __syncthreads();
   else lds_barrier();
