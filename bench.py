@@ -73,7 +73,7 @@ def gret_traffic_fields(call_s):
     counter traffic summed, as a rate over the call time, or null when any is
     absent or was taken on a different version of the kernels."""
     from bench_counters import traffic_for
-    parts = [traffic_for(k) for k in ("gret_state_kernel<128>", "gret_scan_kernel<128>", "gret_out_kernel<128>")]
+    parts = [traffic_for(k) for k in ("gret_segstate_kernel<128>", "gret_segscan_kernel<128>", "gret_out_kernel<128>")]
     if any(b is None for b in parts):
         return {"traffic": None}
     b = sum(parts)
@@ -719,7 +719,7 @@ def bench_gret(args, torch, dk, synth, dev):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, **gret_traffic_fields(call_s),
-                     "kernel": "gret_state_kernel + gret_scan_kernel + gret_out_kernel (one call, timed together)",
+                     "kernel": "gret_segstate_kernel + gret_segscan_kernel + gret_out_kernel (one call, timed together)",
                      "avg_launch_ms": call_s * 1e3, "algorithmic_per_launch": alg_bytes,
                      "mfma_tflops": tfl, "mfma_flops_per_launch": flops},
         "decode": {"us_per_step": dec_us, "state_bytes_per_step": state_bytes,

@@ -42,13 +42,13 @@ KERNELS = {
     "prefill_bf16_kernel<128>": ["prefill_bf16.hip", "internal.h", "lds_copy.h", "tile_common.h"],
     "decode_split_bf16_kernel<128, 1, 0>": ["decode_bf16.hip", "internal.h", "tile_common.h"],
     "decode_merge_kernel<128, 16, 1, __hip_bfloat16>": ["decode_merge.hip", "internal.h", "tile_common.h"],
-    "gret_state_kernel<128>": ["gret.hip", "internal.h", "lds_copy.h", "tile_common.h"],
-    "gret_scan_kernel<128>": ["gret.hip", "internal.h", "lds_copy.h", "tile_common.h"],
+    "gret_segstate_kernel<128>": ["gret.hip", "internal.h", "lds_copy.h", "tile_common.h"],
+    "gret_segscan_kernel<128>": ["gret.hip", "internal.h", "lds_copy.h", "tile_common.h"],
     "gret_out_kernel<128>": ["gret.hip", "internal.h", "lds_copy.h", "tile_common.h"],
 }
 # the run whose counters describe each kernel
-KERNEL_RUN = {"prefill_bf16_kernel<128>": "prefill", "gret_state_kernel<128>": "gret",
-              "gret_scan_kernel<128>": "gret", "gret_out_kernel<128>": "gret"}
+KERNEL_RUN = {"prefill_bf16_kernel<128>": "prefill", "gret_segstate_kernel<128>": "gret",
+              "gret_segscan_kernel<128>": "gret", "gret_out_kernel<128>": "gret"}
 
 RUNS = {
     "prefill": ["--skip", "decode,decode_1m,ragged", "--steps", "1", "--warmup", "0", "--no-cpu-baseline"],

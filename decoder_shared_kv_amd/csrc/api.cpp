@@ -386,25 +386,55 @@ yoco_status check_gret(const yoco_gret_dims* d) {
 }
 
 struct GretWorkspace {
-  size_t state_off, in_off, decay_off, total;
+  size_t u_off, s_off, decay_off, total;
 };
 
-// Chunk slots per head: every sequence's chunks, numbered one after the other,
-// fit ceil(total_rows / 256) + batch slots whatever the lengths (each sequence
-// adds at most one partial chunk).
-int64_t gret_slots(const yoco_gret_dims* d, int64_t total_rows) {
-  return (total_rows + kGretChunk - 1) / kGretChunk + d->batch;
+// Chunks per segment: the largest power of two (at most 64) that still leaves
+// one segment per compute unit (256 on MI355X) over all heads, counting the
+// rows' chunks; 1 for short inputs.
+constexpr int64_t kGretTargetSegs = 256;
+int gret_seg_chunks(const yoco_gret_dims* d, int64_t total_rows) {
+  const int64_t ch = (total_rows + kGretChunk - 1) / kGretChunk * d->num_heads;
+  int seg = 1;
+  while (seg < 64 && ch >= kGretTargetSegs * 2 * seg) seg *= 2;
+  return seg;
+}
+
+// Segment slots per head: every sequence's segments, numbered one after the
+// other, fit ceil(chunks / seg) + batch slots whatever the lengths, chunks =
+// ceil(total_rows / 256) + batch (each sequence adds at most one partial chunk
+// and one partial segment).
+int64_t gret_slots(const yoco_gret_dims* d, int64_t total_rows, int seg) {
+  const int64_t chunks = (total_rows + kGretChunk - 1) / kGretChunk + d->batch;
+  return (chunks + seg - 1) / seg + d->batch;
 }
 
 GretWorkspace gret_workspace(const yoco_gret_dims* d, int64_t slots) {
   const size_t per = (size_t)d->num_heads * slots;
   const size_t dd = (size_t)d->head_dim * d->head_dim;
   GretWorkspace w;
-  w.state_off = 0;
-  w.in_off = (per * dd * 2 + 255) & ~(size_t)255;
-  w.decay_off = (w.in_off + per * dd * 2 + 255) & ~(size_t)255;
+  w.u_off = 0;
+  w.s_off = (per * dd * 4 + 255) & ~(size_t)255;
+  w.decay_off = (w.s_off + per * dd * 4 + 255) & ~(size_t)255;
   w.total = w.decay_off + per * 4;
   return w;
+}
+
+// The most slots any call with at most total_rows rows uses (the segment
+// length grows with the rows, so fewer rows can need more slots): the reported
+// workspace size never shrinks as total_rows grows.
+int64_t gret_max_slots(const yoco_gret_dims* d, int64_t total_rows) {
+  const int seg = gret_seg_chunks(d, total_rows);
+  int64_t most = gret_slots(d, total_rows, seg);
+  for (int s = 1; s < seg; s *= 2) {
+    // the most rows that still take segments of s chunks
+    const int64_t ch_max = kGretTargetSegs * 2 * s - 1;               // chunk count over all heads
+    const int64_t rows = ch_max / d->num_heads * kGretChunk;
+    const int64_t r = rows < total_rows ? rows : total_rows;
+    const int64_t n = gret_slots(d, r, gret_seg_chunks(d, r));
+    if (n > most) most = n;
+  }
+  return most;
 }
 
 }  // namespace
@@ -415,7 +445,7 @@ yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int64_t total_r
   yoco_status st = check_gret(dims);
   if (st != YOCO_OK) return st;
   if (bytes == nullptr || total_rows < 0) return YOCO_ERR_INVALID_ARG;
-  *bytes = gret_workspace(dims, gret_slots(dims, total_rows)).total;
+  *bytes = gret_workspace(dims, gret_max_slots(dims, total_rows)).total;
   return YOCO_OK;
 }
 
@@ -433,8 +463,9 @@ yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const v
   if ((state_in != nullptr && !aligned16(state_in)) || (state_out != nullptr && !aligned16(state_out)))
     return YOCO_ERR_INVALID_ARG;
   if (total_rows < 0) return YOCO_ERR_INVALID_ARG;
-  const int64_t slots = gret_slots(dims, total_rows);
-  if (slots > INT32_MAX || dims->num_heads > 65535) return YOCO_ERR_UNSUPPORTED;
+  const int seg = gret_seg_chunks(dims, total_rows);
+  const int64_t slots = gret_slots(dims, total_rows, seg);
+  if (slots * dims->num_heads > INT32_MAX || dims->num_heads > 65535) return YOCO_ERR_UNSUPPORTED;
   if (total_rows == 0 && state_out == nullptr) return YOCO_OK;   // nothing to compute or pass on
   const GretWorkspace w = gret_workspace(dims, slots);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < w.total) return YOCO_ERR_WORKSPACE;
@@ -448,13 +479,14 @@ yoco_status yoco_gret_prefill(const yoco_gret_dims* dims, const void* q, const v
   p.state_in = state_in;
   p.state_out = state_out;
   char* ws = static_cast<char*>(workspace);
-  p.chunk_state = reinterpret_cast<uint16_t*>(ws + w.state_off);
-  p.chunk_in = reinterpret_cast<uint16_t*>(ws + w.in_off);
-  p.chunk_decay = reinterpret_cast<float*>(ws + w.decay_off);
+  p.seg_u = reinterpret_cast<float*>(ws + w.u_off);
+  p.seg_s = reinterpret_cast<float*>(ws + w.s_off);
+  p.seg_decay = reinterpret_cast<float*>(ws + w.decay_off);
   p.total_rows = total_rows;
   p.batch = dims->batch;
   p.heads = dims->num_heads;
   p.slots = (int32_t)slots;
+  p.seg_chunks = seg;
   if (yoco::launch_gret_prefill(p, dims->head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
     return YOCO_ERR_HIP;
   return YOCO_OK;

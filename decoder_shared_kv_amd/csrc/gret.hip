@@ -3,24 +3,28 @@
 // decay D[n][m] = γ_{m+1} ... γ_n, the recurrent form S_n = γ_n S_{n-1} + K_n^T V_n,
 // o_n = Q_n S_n, and the chunkwise form; section 5.3.2: chunks of 256 rows).
 //
-// Prefill runs the chunkwise form in three launches, so that every (sequence,
-// head, chunk) works in parallel and only the cheap state recurrence is serial
-// (the chunks of all sequences are numbered one after the other and located on
-// the device, so every row is computed whatever the lengths):
-//   1. gret_state_kernel: per chunk, U = sum_m w_m k_m^T v_m with w_m the decay
-//      from row m to the chunk's end, and the chunk's total decay G
-//      (MFMA: U^T = V^T diag(w) K, both operands by transposing LDS reads);
-//   2. gret_scan_kernel: S_{c+1} = G_c S_c + U_c over the chunks (fp32), writing
-//      each chunk's incoming state S_c (bf16, for the MFMA of step 3) and the
-//      final state;
-//   3. gret_out_kernel: o_j = e_j q_j S_c + sum_{m <= j} (e_j / e_m) (q_j . k_m) v_m
-//      with e_j the decay from the chunk's start to row j: the first term is one
-//      MFMA product with the staged S_c, the second the intra-chunk parallel
-//      form, tiled like attention (S^T = K Q^T, decay and causal mask on the
-//      accumulator registers, O^T += V^T P^T) but without a softmax.
+// Prefill runs the chunkwise form in three launches. A sequence's chunks are
+// grouped into segments of seg_chunks consecutive chunks (the segments of all
+// sequences numbered one after the other and located on the device, so every
+// row is computed whatever the lengths); every (segment, head) works in
+// parallel and only the recurrence across segments is serial:
+//   1. gret_segstate_kernel: per segment, its contribution to the state, U, and
+//      its total decay, by the chunk recurrence U <- G_c U + sum_m w_m k_m^T v_m
+//      (w_m the decay from row m to the chunk's end; MFMA: U = (w ⊙ K)^T V, both
+//      operands by transposing LDS reads, U in fp32 accumulators);
+//   2. gret_segscan_kernel: S_{s+1} = G_s S_s + U_s over the segments (fp32),
+//      writing each segment's incoming state and the final state;
+//   3. gret_out_kernel: per segment, chunk after chunk, carrying the state
+//      in fp32 accumulators: o_j = e_j q_j S_c + sum_{m <= j} (e_j / e_m)
+//      (q_j . k_m) v_m with e_j the decay from the chunk's start to row j (the
+//      first term one MFMA product with S_c staged in LDS as bf16, the second
+//      the intra-chunk parallel form, tiled like attention: S^T = K Q^T, decay
+//      and causal mask on the accumulator registers, O^T += V^T P^T, without a
+//      softmax), then S_{c+1} = G_c S_c + (w ⊙ K)^T V from the same LDS tiles.
 // Decays are handled as base-2 logarithms, accumulated along the chunk; a gate
 // below 2^-126 counts as 2^-126 (its products vanish below fp32's range).
 // Decode is the recurrent form's step on the fp32 state (gret_decode_kernel).
+
 #include "internal.h"
 #include "lds_copy.h"
 #include "tile_common.h"
@@ -93,46 +97,115 @@ template <int D>
 __device__ __forceinline__ uint32_t row_slot(int r, int c) {
   return (uint32_t)(r * (D * 2) + 16 * (c ^ (r & (D / 8 - 1))));
 }
+// ... and of a K tile of the output pass, read both ways (row-wise for the
+// scores, transposed for the state update): chunk c at c ^ kd_swizzle(r), a map
+// linear in the bits of r mod 16 under which 16 consecutive rows at one chunk
+// and the 8 rows x 64 bytes of a transposing read both fall on distinct banks
+// (D = 128, for 32 and for 64 banks, checked by enumeration on the host; for
+// D = 64 no such map exists and this one keeps the transposing reads whole)
+template <int D>
+__device__ __forceinline__ int kd_swizzle(int r) {
+  if constexpr (D == 128) {
+    return ((r >> 2) & 3) ^ (12 * (r & 1)) ^ (6 * ((r >> 1) & 1));
+  } else {
+    return (4 * (r & 1)) ^ (2 * ((r >> 1) & 1)) ^ ((r >> 2) & 1);
+  }
+}
+template <int D>
+__device__ __forceinline__ uint32_t kd_slot(int r, int c) {
+  return (uint32_t)(r * (D * 2) + 16 * (c ^ kd_swizzle<D>(r)));
+}
+
+enum TileLayout { kRowLayout, kTrLayout, kKdLayout };
+
+// x, hidden from the optimiser: per-lane offsets derived from it are computed
+// where they are used instead of being kept live (or spilled) across a loop
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <int D, int LAYOUT>
+__device__ __forceinline__ int tile_swizzle(int r) {
+  if constexpr (LAYOUT == kRowLayout) return r & (D / 8 - 1);
+  else if constexpr (LAYOUT == kTrLayout) return v_swizzle<D>(r);
+  else return kd_swizzle<D>(r);
+}
 
 // Transposing read: 8 bf16 of one column (dim 32t + lane col) at rows
-// base + 4h + {0..3} and base + 8 + 4h + {0..3} of a tr_slot tile.
-template <int D>
+// base + 4h + {0..3} and base + 8 + 4h + {0..3} of a tr_slot (or kd_slot) tile.
+template <int D, int LAYOUT = kTrLayout>
 __device__ __forceinline__ bf16x8 read_tr(const YOCO_LDS char* tile, int base_row, int t, int lane) {
   const int i = lane & 15, g = lane >> 4, h = lane >> 5;
   const int q = i >> 2, w = i & 3;
   const int r = base_row + 4 * h + q;
   const int chunk = 4 * t + 2 * (g & 1) + (w >> 1);
-  const YOCO_LDS char* p = tile + tr_slot<D>(r, chunk) + 8 * (w & 1);
+  // rows r and r + 8 (the kd swizzle depends on bit 3 of the row, the
+  // transposing one only on r mod 4)
+  const YOCO_LDS char* p = tile + r * (D * 2) + 16 * (chunk ^ tile_swizzle<D, LAYOUT>(r)) + 8 * (w & 1);
+  const YOCO_LDS char* p8 = tile + (r + 8) * (D * 2) + 16 * (chunk ^ tile_swizzle<D, LAYOUT>(r + 8)) + 8 * (w & 1);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p + 8 * (D * 2)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p8));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Copy tile rows [first, first + rows) of a [rows, H, D] bf16 tensor (row
 // stride H*D) whose row 0 is global row `row0` (rows >= n_rows, n_rows >= 1,
 // repeat row n_rows - 1) into LDS at `lds` (tile row `first` at offset 0), in
-// the tr_slot (TR) or row_slot layout, by the load unit. rows * D / 8 must be a
-// multiple of the thread count.
-template <int D, bool TR>
+// the given layout, by the load unit (tid: this thread's index in the
+// workgroup). rows * D / 8 must be a multiple of the thread count, `first` a
+// multiple of 16.
+template <int D, int LAYOUT>
 __device__ __forceinline__ void load_tile(const __bf16* src, int64_t row0, int n_rows, int first, int rows, int H,
-                                          int h, uint32_t lds) {
+                                          int h, uint32_t lds, int tid) {
   constexpr int cpr = D / 8;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = 0; i < rows * cpr / kGThreads; ++i) {
-    const int p = i * kGThreads + (int)threadIdx.x;
+    const int p = i * kGThreads + tid;
     const int r = first + p / cpr, slot = p % cpr;
-    const int c = TR ? (slot ^ v_swizzle<D>(r)) : (slot ^ (r & (cpr - 1)));
+    const int c = slot ^ tile_swizzle<D, LAYOUT>(r);
     const int rr = r < n_rows ? r : n_rows - 1;
     dma16(src + ((row0 + rr) * H + h) * D + 8 * c, lds + (i * kGThreads + wave * 64) * 16);
   }
 }
+
+// The A operand of a state-update product, U += (w ⊙ K)^T V over 16 keys:
+// K columns 32bi + lane col at keys base + 8z + 4h + {0..3} (elements 4z..4z+3),
+// each times its key's weight (w: the chunk's weights in LDS, key0 the tile's
+// first key within the chunk).
+__device__ __forceinline__ bf16x8 weight_keys(const bf16x8 kb, const f32x4 w0, const f32x4 w1) {
+  uint32_t wv[4];
+#pragma unroll
+  for (int z = 0; z < 2; ++z) {
+    const f32x4 ww = z == 0 ? w0 : w1;
+    wv[2 * z] = pack2((float)kb[4 * z + 0] * ww[0], (float)kb[4 * z + 1] * ww[1]);
+    wv[2 * z + 1] = pack2((float)kb[4 * z + 2] * ww[2], (float)kb[4 * z + 3] * ww[3]);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+}
+template <int D, int LAYOUT>
+__device__ __forceinline__ bf16x8 weighted_k(const YOCO_LDS char* kt, const YOCO_LDS float* w, int key0,
+                                             int base_row, int bi, int lane) {
+  const int hf = lane >> 5;
+  const bf16x8 kb = read_tr<D, LAYOUT>(kt, base_row, bi, lane);
+  const f32x4 w0 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 4 * hf);
+  const f32x4 w1 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 8 + 4 * hf);
+  return weight_keys(kb, w0, w1);
+}
+
+// Keeps the scheduler from moving instructions across this point, so that LDS
+// operand reads stay issued ahead of the MFMAs that use them.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+constexpr int kGReadsAhead = 4;   // LDS operand reads kept in flight ahead of the MFMAs (output pass)
 
 struct ChunkInfo {
   int64_t row0;   // first global row of the chunk
   int n;          // rows of the chunk (0: no chunk)
 };
 
-// Rows of sequence b (clamped to the packed rows) and its chunks.
+// Rows of sequence b (clamped to the packed rows), its chunks and its segments
+// (runs of p.seg_chunks consecutive chunks, the unit of work of both passes
+// that read K and V).
 __device__ __forceinline__ int64_t seq_rows(const GretParams& p, int b) {
   int64_t r0 = p.cu_seqlens[b], r1 = p.cu_seqlens[b + 1];
   if (r1 > p.total_rows) r1 = p.total_rows;
@@ -141,26 +214,29 @@ __device__ __forceinline__ int64_t seq_rows(const GretParams& p, int b) {
 __device__ __forceinline__ int seq_chunks(const GretParams& p, int b) {
   return (int)((seq_rows(p, b) + kGC - 1) / kGC);
 }
+__device__ __forceinline__ int seq_segs(const GretParams& p, int b) {
+  return (seq_chunks(p, b) + p.seg_chunks - 1) / p.seg_chunks;
+}
 
-// The chunks of all sequences are numbered one after the other (sequence 0's
+// The segments of all sequences are numbered one after the other (sequence 0's
 // first), so a grid over the workspace's slots covers every row whatever the
-// lengths. Global chunk g -> (sequence b, its chunk c), counted by the whole
-// wave (64 sequences per step: chunk counts, a DPP prefix sum, a ballot for the
-// first sequence whose prefix passes g). All 64 lanes must be active. False if
-// g is past the last chunk.
-__device__ __forceinline__ bool locate_chunk(const GretParams& p, int g, int* b_out, int* c_out) {
+// lengths. Global segment g -> (sequence b, its segment s), counted by the
+// whole wave (64 sequences per step: segment counts, a DPP prefix sum, a ballot
+// for the first sequence whose prefix passes g). All 64 lanes must be active.
+// False if g is past the last segment.
+__device__ __forceinline__ bool locate_segment(const GretParams& p, int g, int* b_out, int* s_out) {
   const int lane = threadIdx.x & 63;
-  int before = 0;   // chunks of the sequences before this group of 64
+  int before = 0;   // segments of the sequences before this group of 64
   for (int b0 = 0; b0 < p.batch; b0 += 64) {
     const int bb = b0 + lane;
-    const int n = bb < p.batch ? seq_chunks(p, bb) : 0;
+    const int n = bb < p.batch ? seq_segs(p, bb) : 0;
     const int incl = wave_incl_scan_i32(n);
     const int total = __builtin_amdgcn_readlane(incl, 63);
     if (g < before + total) {
       const uint64_t m = __builtin_amdgcn_ballot_w64(before + incl > g);
       const int l = __builtin_ctzll(m);
       *b_out = b0 + l;
-      *c_out = g - before - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(n, l));
+      *s_out = g - before - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(n, l));
       return true;
     }
     before += total;
@@ -168,10 +244,10 @@ __device__ __forceinline__ bool locate_chunk(const GretParams& p, int g, int* b_
   return false;
 }
 
-// First global chunk of sequence b (scalar loop over the sequences before it).
-__device__ __forceinline__ int64_t chunk_start(const GretParams& p, int b) {
+// First global segment of sequence b (scalar loop over the sequences before it).
+__device__ __forceinline__ int64_t seg_start(const GretParams& p, int b) {
   int64_t g = 0;
-  for (int i = 0; i < b; ++i) g += seq_chunks(p, i);
+  for (int i = 0; i < b; ++i) g += seq_segs(p, i);
   return g;
 }
 
@@ -185,170 +261,221 @@ __device__ __forceinline__ ChunkInfo chunk_info(const GretParams& p, int b, int 
   return ci;
 }
 
-// ---------------------------------------------------------------------------
-// 1. per-chunk state contribution U^T[dv][dk] and total decay
-// ---------------------------------------------------------------------------
+// This wave's blocks of a head_dim x head_dim state held as MFMA accumulators:
+// blocks (bi, bj) of 32 x 32, rows dk = 32 bi + 8(r/4) + 4hf + r%4 in register r,
+// column dv = 32 bj + lane % 32. D = 128: 16 blocks, two per wave (same bi);
+// D = 64: 4 blocks, waves 0..3 (waves 4..7 hold none).
 template <int D>
-__global__ __launch_bounds__(kGThreads, 2) void gret_state_kernel(GretParams p) {
-  constexpr int kQ = kGC / 4;                        // rows per quarter
-  constexpr int kQBytes = kQ * D * 2;                // one matrix's quarter
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * kQBytes];   // 2 stages x (K, V)
-  __shared__ __attribute__((aligned(16))) float wgt[kGC];
+struct StateBlocks {
+  static constexpr int NB = D / 32;
+  static constexpr int PER = (NB * NB) / 8 > 0 ? (NB * NB) / 8 : 1;
+  bool idle;
+  int blk0, bi;
+  __device__ explicit StateBlocks(int wave) {
+    idle = wave * PER >= NB * NB;
+    blk0 = idle ? 0 : wave * PER;
+    bi = blk0 / NB;
+  }
+  __device__ int bj(int e) const { return (blk0 + e) % NB; }
+};
+
+// Wait until at most n of this wave's copies are in flight (n from a short list
+// of wave-uniform values: the waits need an immediate).
+template <int LQ>
+__device__ __forceinline__ void wait_copies(int n) {
+  if (n == 0) wait_vm_lgkm0<0>();
+  else if (n == LQ) wait_vm_lgkm0<LQ>();
+  else if (n == LQ + 1) wait_vm_lgkm0<LQ + 1>();
+  else if (n == 2 * LQ) wait_vm_lgkm0<2 * LQ>();
+  else wait_vm_lgkm0<2 * LQ + 1>();
+}
+
+// ---------------------------------------------------------------------------
+// 1. per segment: its state contribution and total decay
+// ---------------------------------------------------------------------------
+// U = sum over the segment's rows m of (decay from m to the segment's end)
+// k_m^T v_m, built chunk by chunk as U <- G_c U + sum_{m in c} w_m k_m^T v_m, with
+// w_m the decay from row m to the chunk's end and G_c the chunk's total decay
+// (the recurrence itself, in fp32 accumulators). K and V stream through
+// kSStages LDS stages in quarters of 64 rows, kSStages - 1 quarters ahead and
+// across chunk boundaries; each chunk's gates come in by the load unit with its
+// first quarter (every thread one dword, so that all waves count the same
+// copies), into one of two buffers by chunk parity.
+constexpr int kSStages = 4;
+
+template <int D>
+struct SegLds {
+  static constexpr int kQ = kGC / 4;                        // rows per quarter
+  static constexpr int kQBytes = kQ * D * 2;                // one matrix's quarter
+  static constexpr int kStage = 2 * kQBytes;                // K then V
+  static constexpr int kGates = kSStages * kStage;          // 2 x kGThreads dwords
+  static constexpr int kWgt = kGates + 2 * kGThreads * 4;   // 2 x kGC weights
+  static constexpr int kBytes = kWgt + 2 * kGC * 4;
+};
+
+template <int D>
+__global__ __launch_bounds__(kGThreads, 1) void gret_segstate_kernel(GretParams p) {
+  typedef SegLds<D> LY;
+  constexpr int kQ = LY::kQ;
+  constexpr int LQ = 2 * (kQ * D / 8 / kGThreads);   // tile copies per thread and quarter
+  constexpr int kAhead = kSStages - 1;
+  __shared__ __attribute__((aligned(16))) char smem_raw[LY::kBytes];
   __shared__ float wsum[4];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
-  const int g = blockIdx.x, h = blockIdx.y;
-  int b, c;
-  if (!locate_chunk(p, g, &b, &c)) return;
-  const ChunkInfo ci = chunk_info(p, b, c);
-  if (ci.n == 0) return;
+  const int h = blockIdx.x % p.heads, g = blockIdx.x / p.heads;
+  int b, s;
+  if (!locate_segment(p, g, &b, &s)) return;
+  const int c0 = s * p.seg_chunks;
+  const int left = seq_chunks(p, b) - c0;
+  const int nc = left < p.seg_chunks ? left : p.seg_chunks;
+  const ChunkInfo first = chunk_info(p, b, c0);
+  const int n_last = chunk_info(p, b, c0 + nc - 1).n;
+  const int nq = 4 * (nc - 1) + (n_last + kQ - 1) / kQ;    // quarters holding rows
   const int64_t slot = (int64_t)h * p.slots + g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // decay from row m to the chunk's end: 2^(A_last - A_m), A = prefix of log2 gates
-  const float a = log2_gate(p.gamma, ci.row0 + tid, h, p.heads, tid < ci.n);
-  const float A = chunk_prefix(a, wsum);
-  const float a_last = wsum[0] + wsum[1] + wsum[2] + wsum[3];   // gates past the end count 1
-  if (tid < kGC) wgt[tid] = tid < ci.n ? exp2f(a_last - A) : 0.f;
-  if (tid == 0) p.chunk_decay[slot] = exp2f(a_last);
-  wait_vm_lgkm0<0>();   // the gates are in: from here on only the tile copies are in flight
-
-  // K and V of the chunk in quarters of 64 rows through two stages (64 KB of LDS,
-  // so two workgroups share a CU and one's copies overlap the other's MFMAs)
+  const int hf = lane >> 5;
+  const int H = p.heads;
   const uint32_t base = (uint32_t)(uintptr_t)smem;
-  constexpr int LQ = 2 * (kQ * D / 8 / kGThreads);   // copies per thread and quarter
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
   const __bf16* kg = static_cast<const __bf16*>(p.k);
   const __bf16* vg = static_cast<const __bf16*>(p.v);
   auto issue = [&](int f) {
-    const uint32_t st = base + (f & 1) * 2 * kQBytes;
-    load_tile<D, true>(kg, ci.row0, ci.n, kQ * f, kQ, p.heads, h, st);
-    load_tile<D, true>(vg, ci.row0, ci.n, kQ * f, kQ, p.heads, h, st + kQBytes);
+    const int cf = f >> 2;
+    const int64_t row0 = first.row0 + (int64_t)cf * kGC;
+    const int n = cf == nc - 1 ? n_last : kGC;
+    if ((f & 3) == 0) {
+      const int r = (tid & (kGC - 1)) < n ? (tid & (kGC - 1)) : n - 1;
+      dma4(p.gamma + (row0 + r) * H + h, base + LY::kGates + (cf & 1) * (kGThreads * 4) + wv * 256);
+    }
+    const uint32_t st = base + (f % kSStages) * LY::kStage;
+    load_tile<D, kTrLayout>(kg, row0, n, kQ * (f & 3), kQ, H, h, st, tid);
+    load_tile<D, kTrLayout>(vg, row0, n, kQ * (f & 3), kQ, H, h, st + LY::kQBytes, tid);
   };
-  const int n_q = (ci.n + kQ - 1) / kQ;              // quarters holding rows
-  issue(0);
-  if (n_q > 1) issue(1);
+  for (int f = 0; f < kAhead && f < nq; ++f) issue(f);
 
-  // output blocks (dv block i, dk block j) of 32 x 32; D = 128: 16 blocks, two per
-  // wave (same i); D = 64: 4 blocks, waves 0..3
-  constexpr int NB = D / 32;
-  constexpr int PER = (NB * NB) / 8 > 0 ? (NB * NB) / 8 : 1;
-  const bool idle = wave * PER >= NB * NB;     // D = 64: waves 4..7 only join the barriers
-  const int blk0 = idle ? 0 : wave * PER;
-  const int bi = blk0 / NB;
+  const StateBlocks<D> sb(wave);
+  constexpr int PER = StateBlocks<D>::PER;
   f32x16 acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = f32x16{};
-  const int hf = lane >> 5;
-  for (int f = 0; f < n_q; ++f) {
-    // quarter f is in when at most the next one's copies are in flight
-    if (f + 1 < n_q) wait_vm_lgkm0<LQ>(); else wait_vm_lgkm0<0>();
+  float a_seg = 0.f;   // the segment's log2 decay
+  for (int f = 0; f < nq; ++f) {
+    // quarter f is in when at most the copies of the quarters issued after it
+    // (up to kAhead - 1, one of them perhaps a chunk's first) are in flight
+    const int later = nq - 1 - f < kAhead - 1 ? nq - 1 - f : kAhead - 1;
+    int pending = later * LQ;
+    for (int j = 1; j <= later; ++j) pending += ((f + j) & 3) == 0 ? 1 : 0;
+    wait_copies<LQ>(pending);
     barrier_only();
-    const YOCO_LDS char* kt = smem + (f & 1) * 2 * kQBytes;
-    const YOCO_LDS char* vt = kt + kQBytes;
-    if (!idle) {
+    const int cf = f >> 2;
+    YOCO_LDS float* wgt = (YOCO_LDS float*)(smem + LY::kWgt + (cf & 1) * (kGC * 4));
+    if ((f & 3) == 0) {
+      // the chunk's decay prefix, its weights and total decay
+      const int n = cf == nc - 1 ? n_last : kGC;
+      const YOCO_LDS float* gt = (const YOCO_LDS float*)(smem + LY::kGates + (cf & 1) * (kGThreads * 4));
+      float a = 0.f;
+      if (tid < kGC && tid < n) {
+        const float l = __log2f(gt[tid]);
+        a = l > kLogGateFloor ? l : kLogGateFloor;
+      }
+      const float A = chunk_prefix<false>(a, wsum);
+      const float a_last = wsum[0] + wsum[1] + wsum[2] + wsum[3];   // rows past the end count gate 1
+      if (tid < kGC) wgt[tid] = tid < n ? exp2f(a_last - A) : 0.f;
+      const float G = exp2f(a_last);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] *= G;
+      a_seg += a_last;
+      lds_barrier();   // the weights are in for every wave
+    }
+    if (!sb.idle) {
+      const YOCO_LDS char* kt = smem + (f % kSStages) * LY::kStage;
+      const YOCO_LDS char* vt = kt + LY::kQBytes;
 #pragma unroll
       for (int s4 = 0; s4 < kQ / 16; ++s4) {
-        // keys 16 s + {0..3, 8..11} + 4h of the chunk, s = 4f + s4 (two 4-key runs per lane)
-        const int base_q = 16 * s4;               // row within the quarter
-        const int key = kQ * f + base_q;          // row within the chunk
-        const bf16x8 av = read_tr<D>(vt, base_q, bi, lane);            // V^T rows dv, 8 keys
-        const f32x4 w0 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (key + 4 * hf));
-        const f32x4 w1 = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)wgt + 4 * (key + 8 + 4 * hf));
+        const bf16x8 ka = weighted_k<D, kTrLayout>(kt, wgt, kQ * (f & 3), 16 * s4, sb.bi, lane);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-          const int bj = (blk0 + e) % NB;
-          const bf16x8 kb = read_tr<D>(kt, base_q, bj, lane);          // K columns dk, same 8 keys
-          uint32_t wv[4];
-#pragma unroll
-          for (int z = 0; z < 2; ++z) {
-            const f32x4 ww = z == 0 ? w0 : w1;
-            wv[2 * z] = pack2((float)kb[4 * z + 0] * ww[0], (float)kb[4 * z + 1] * ww[1]);
-            wv[2 * z + 1] = pack2((float)kb[4 * z + 2] * ww[2], (float)kb[4 * z + 3] * ww[3]);
-          }
-          const bf16x8 kw = __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, kw, acc[e], 0, 0, 0);
+          const bf16x8 vb = read_tr<D>(vt, 16 * s4, sb.bj(e), lane);   // V columns dv, same 8 keys
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, vb, acc[e], 0, 0, 0);
         }
       }
     }
-    if (f + 2 < n_q) {
-      barrier_only();   // every wave is done with stage f & 1
-      issue(f + 2);
-    }
+    // its stage held quarter f - 1, which every wave finished before the barrier above
+    if (f + kAhead < nq) issue(f + kAhead);
   }
-  if (idle) return;
-  // lane holds dk = 32 bj + lane % 32, dv rows 32 bi + 8(r/4) + 4hf + r%4; stored
-  // as bf16 (the scan adds it to an fp32 state): half the bytes of fp32 for the
-  // store here and the scan's read, for one more rounding of the contribution
-  __bf16* u = reinterpret_cast<__bf16*>(p.chunk_state) + slot * (D * D);
+  if (tid == 0) p.seg_decay[slot] = exp2f(a_seg);
+  if (sb.idle) return;
+  float* u = p.seg_u + slot * (D * D);
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int bj = (blk0 + e) % NB;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int dv = 32 * bi + 8 * (r >> 2) + 4 * hf + (r & 3);
-      u[dv * D + 32 * bj + (lane & 31)] = (__bf16)acc[e][r];
+      const int dk = 32 * sb.bi + 8 * (r >> 2) + 4 * hf + (r & 3);
+      u[dk * D + 32 * sb.bj(e) + (lane & 31)] = acc[e][r];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2. the state recurrence across chunks
+// 2. the state recurrence across segments
 // ---------------------------------------------------------------------------
+// S_{s+1} = G_s S_s + U_s (fp32), writing each segment's incoming state and the
+// final state; each thread holds 4 consecutive elements of S [dk][dv].
 template <int D>
-__global__ __launch_bounds__(256) void gret_scan_kernel(GretParams p) {
+__global__ __launch_bounds__(256) void gret_segscan_kernel(GretParams p) {
   const int h = blockIdx.y, b = blockIdx.z;
-  const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;   // element (dv, dk..dk+3) of S^T
+  const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (e0 >= D * D) return;
-  const int dv = e0 / D, dk = e0 % D;
-  const int64_t g0 = chunk_start(p, b);
-  int64_t nc = seq_chunks(p, b);
-  // non-decreasing cu_seqlens keep every chunk within the slots; others are clamped to them
-  if (g0 + nc > p.slots) nc = g0 < p.slots ? p.slots - g0 : 0;
+  const int64_t g0 = seg_start(p, b);
+  int64_t ns = seq_segs(p, b);
+  // non-decreasing cu_seqlens keep every segment within the slots; others are clamped to them
+  if (g0 + ns > p.slots) ns = g0 < p.slots ? p.slots - g0 : 0;
   const int64_t bh = (int64_t)b * p.heads + h;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  if (p.state_in != nullptr) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = p.state_in[(bh * D + dk + i) * D + dv];
-  }
-  // the loads do not depend on the state: fetch a group of chunks ahead, then
-  // run the (serial) recurrence over the group
+  f32x4 st = {0.f, 0.f, 0.f, 0.f};
+  if (p.state_in != nullptr) st = *reinterpret_cast<const f32x4*>(p.state_in + bh * (D * D) + e0);
+  // the loads do not depend on the state: fetch a group of segments ahead,
+  // then run the (serial) recurrence over the group
   constexpr int kAhead = 8;
   const int64_t slot0 = (int64_t)h * p.slots + g0;
-  const uint16_t* __restrict__ us = p.chunk_state + slot0 * (D * D) + e0;
-  const float* __restrict__ gs = p.chunk_decay + slot0;
-  uint16_t* __restrict__ sin = p.chunk_in + slot0 * (D * D) + e0;
-  for (int c0 = 0; c0 < nc; c0 += kAhead) {
-    u32x2 u[kAhead];   // four bf16 contributions
-    float g[kAhead];
+  const float* __restrict__ us = p.seg_u + slot0 * (D * D) + e0;
+  const float* __restrict__ gs = p.seg_decay + slot0;
+  float* __restrict__ sin = p.seg_s + slot0 * (D * D) + e0;
+  for (int64_t s0 = 0; s0 < ns; s0 += kAhead) {
+    f32x4 u[kAhead];
+    float gd[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
-      const int c = c0 + i < nc ? c0 + i : nc - 1;
-      u[i] = *reinterpret_cast<const u32x2*>(us + (int64_t)c * (D * D));
-      g[i] = gs[c];
+      const int64_t s = s0 + i < ns ? s0 + i : ns - 1;
+      u[i] = *reinterpret_cast<const f32x4*>(us + s * (D * D));
+      gd[i] = gs[s];
     }
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
-      if (c0 + i >= nc) break;
-      *reinterpret_cast<u32x2*>(sin + (int64_t)(c0 + i) * (D * D)) = u32x2{pack2(s[0], s[1]), pack2(s[2], s[3])};
-      const float uf[4] = {bf16_lo(u[i][0]), bf16_hi(u[i][0]), bf16_lo(u[i][1]), bf16_hi(u[i][1])};
+      if (s0 + i >= ns) break;
+      *reinterpret_cast<f32x4*>(sin + (s0 + i) * (D * D)) = st;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = fmaf(g[i], s[j], uf[j]);
+      for (int j = 0; j < 4; ++j) st[j] = fmaf(gd[i], st[j], u[i][j]);
     }
   }
-  if (p.state_out != nullptr) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p.state_out[(bh * D + dk + i) * D + dv] = s[i];
-  }
+  if (p.state_out != nullptr) *reinterpret_cast<f32x4*>(p.state_out + bh * (D * D) + e0) = st;
 }
 
 // ---------------------------------------------------------------------------
-// 3. outputs of one chunk
+// 3. outputs: one segment per workgroup, its chunks one after the other
 // ---------------------------------------------------------------------------
-// LDS of the output kernel (head_dim D): every K/V tile of the chunk has its
-// own stage, Q^ and the incoming state come in by the load unit too and their
-// space is handed to tiles 1, 2 (Q^) and 3 (state) once read:
+// The workgroup starts from the segment's incoming state (fp32, in its MFMA
+// accumulators) and carries it across its chunks: each chunk's state goes into
+// LDS as bf16 for the inter-chunk product, and the chunk's own contribution is
+// added tile by tile from the K and V tiles already staged for the outputs.
+// LDS (head_dim D): every K/V tile of the chunk has its own stage, Q^ comes in
+// by the load unit and its space is handed to tiles 1 and 2 once read, the
+// state's to tile 3 once the inter-chunk product is done:
 //   [0, T)          tile 0
 //   [T, 3T)         Q^ rows of the chunk, then tiles 1 and 2
-//   [3T, 4T)        S_c^T, then tile 3
+//   [3T, 4T)        S_c^T (bf16), then tile 3
 //   [4T, 4T + 1 KB) the gates, then their prefix A
+//   [.., + 1 KB)    the state-update weights
+// K tiles are in the kd layout (read both ways), V tiles in the transposing one.
 template <int D>
 struct OutLds {
   static constexpr int kTile = kGT * D * 2;        // one K or V tile
@@ -356,7 +483,8 @@ struct OutLds {
   static constexpr int kQ = kStage;                 // Q^ area (2 stages)
   static constexpr int kS = 3 * kStage;             // state area (stage 3)
   static constexpr int kA = 4 * kStage;             // gates / prefix
-  static constexpr int kBytes = kA + kGC * 4;
+  static constexpr int kW = kA + kGC * 4;           // weights
+  static constexpr int kBytes = kW + kGC * 4;
   static_assert(kGC * D * 2 == 2 * kStage, "the chunk's Q^ rows fill two stages");
   static_assert(D * D * 2 <= kStage, "the state fits a stage");
 };
@@ -375,179 +503,267 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   __shared__ float wsum[4];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
   YOCO_LDS float* A_lds = (YOCO_LDS float*)(smem + LY::kA);
-  const int g = blockIdx.x, h = blockIdx.y;
-  int b, c;
-  if (!locate_chunk(p, g, &b, &c)) return;
-  const ChunkInfo ci = chunk_info(p, b, c);
-  if (ci.n == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qj = lane & 31, hf = lane >> 5;
+  YOCO_LDS float* W_lds = (YOCO_LDS float*)(smem + LY::kW);
+  const int h = blockIdx.x % p.heads, g = blockIdx.x / p.heads;
+  int b, s;
+  if (!locate_segment(p, g, &b, &s)) return;
+  const int c0 = s * p.seg_chunks;
+  const int left = seq_chunks(p, b) - c0;
+  const int nc = left < p.seg_chunks ? left : p.seg_chunks;
+  const int64_t slot = (int64_t)h * p.slots + g;
+  const bool has_state0 = s > 0 || p.state_in != nullptr;
+  const int tid0 = threadIdx.x, wave = tid0 >> 6;
   const int H = p.heads;
   const uint32_t base_lds = (uint32_t)(uintptr_t)smem;
-  const int n_tiles = (ci.n + kGT - 1) / kGT;
   const __bf16* kg = static_cast<const __bf16*>(p.k);
   const __bf16* vg = static_cast<const __bf16*>(p.v);
-  const bool has_state = c > 0 || p.state_in != nullptr;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int t) {
-    const uint32_t st = base_lds + out_stage_off(t, kStage);
-    const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
-    load_tile<D, false>(kg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st);
-    load_tile<D, true>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile);
-  };
+  constexpr int L = 2 * (kGT * D / 8 / kGThreads);   // copies per thread and tile
 
-  // copies, in this order: the gates (one dword per row), the incoming state
-  // (bf16 [dv][dk] in the workspace), Q^ (row_slot layout), tile 0
-  if (tid < kGC) {
-    const int r = tid < ci.n ? tid : ci.n - 1;
-    dma4(p.gamma + (ci.row0 + r) * H + h, base_lds + LY::kA + wv * 256);
-  }
-  if (has_state) {
-    constexpr int cpr = D / 8;
-    const __bf16* sg = reinterpret_cast<const __bf16*>(p.chunk_in) + ((int64_t)h * p.slots + g) * (D * D);
-    for (int i = 0; i < D * cpr / kGThreads; ++i) {
-      const int q = i * kGThreads + tid;
-      const int r = q / cpr, slot = q % cpr;
-      dma16(sg + r * D + 8 * (slot ^ (r & (cpr - 1))), base_lds + LY::kS + (i * kGThreads + wv * 64) * 16);
+  // the running state S (fp32): the segment's incoming state, then after each chunk
+  const StateBlocks<D> sb(wave);
+  constexpr int PER = StateBlocks<D>::PER;
+  f32x16 sacc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) sacc[e] = f32x16{};
+  if (has_state0 && !sb.idle) {
+    const int lane = tid0 & 63, hf = lane >> 5;
+    const float* src = p.seg_s + slot * (D * D);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dk = 32 * sb.bi + 8 * (r >> 2) + 4 * hf + (r & 3);
+        sacc[e][r] = src[dk * D + 32 * sb.bj(e) + (lane & 31)];
+      }
     }
   }
-  load_tile<D, false>(static_cast<const __bf16*>(p.q), ci.row0, ci.n, 0, kGC, H, h, base_lds + LY::kQ);
-  issue(0);
-  constexpr int L = 2 * (kGT * D / 8 / kGThreads);   // copies per thread and tile
-  wait_vm_lgkm0<L>();   // all but tile 0
-  barrier_only();
 
-  // decay prefix A_j (base 2) of the chunk's rows, in place of the gates
-  float a = 0.f;
-  if (tid < kGC && tid < ci.n) {
-    const float l = __log2f(A_lds[tid]);
-    a = l > kLogGateFloor ? l : kLogGateFloor;
-  }
-  const float A = chunk_prefix<false>(a, wsum);
-  if (tid < kGC) A_lds[tid] = A;
-
-  // Q^T as the B operand: query row qj of this wave, dims 16kk + 8hf .. +7
-  const int j_row = 32 * wave + qj;                         // row within the chunk
-  const int j_load = j_row < ci.n ? j_row : ci.n - 1;
-  bf16x8 qf[D / 16];
-  {
-    const YOCO_LDS char* qs = smem + LY::kQ;
+  for (int cc = 0; cc < nc; ++cc) {
+    // the per-lane LDS offsets of the chunk's prologue and epilogue are
+    // recomputed per chunk (kept live across the loop they would not fit)
+    const int tid = opaque(tid0), lane = tid & 63;
+    const int qj = lane & 31, hf = lane >> 5;
+    const ChunkInfo ci = chunk_info(p, b, c0 + cc);
+    const bool has_state = has_state0 || cc > 0;
+    const int n_tiles = (ci.n + kGT - 1) / kGT;
+    auto issue = [&](int t) {
+      const uint32_t st = base_lds + out_stage_off(t, kStage);
+      const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
+      load_tile<D, kKdLayout>(kg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st, tid);
+      load_tile<D, kTrLayout>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile, tid);
+    };
+    // S_c^T into the state area as bf16 (row dv, 16-byte chunk dk / 8; each lane
+    // 4 consecutive dk of one dv); the area is free: the previous chunk's tile 3
+    // was done with before its outputs were staged
+    if (has_state && !sb.idle) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = *reinterpret_cast<const YOCO_LDS bf16x8*>(qs + row_slot<D>(j_load, 2 * kk + hf));
-  }
-  lds_barrier();   // Q^ read by every wave (its area takes tiles 1 and 2); A in LDS
-  if (n_tiles > 1) issue(1);
-  if (n_tiles > 2) issue(2);
-
-  const bool wave_active = 32 * wave < ci.n;
-  const float Aj = A_lds[j_load];
-  f32x16 acc[D / 32];
+      for (int e = 0; e < PER; ++e) {
+        const int dv = 32 * sb.bj(e) + (lane & 31);
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-  if (has_state && wave_active) {
-    // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j
-    const YOCO_LDS char* sl = smem + LY::kS;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const u32x2 w2 = {pack2(sacc[e][4 * g4 + 0], sacc[e][4 * g4 + 1]),
+                            pack2(sacc[e][4 * g4 + 2], sacc[e][4 * g4 + 3])};
+          *reinterpret_cast<YOCO_LDS u32x2*>(smem + LY::kS + row_slot<D>(dv, 4 * sb.bi + g4) + 8 * hf) = w2;
+        }
+      }
+    }
+    __syncthreads();   // every wave has read its staged outputs of the previous chunk
+
+    // copies, in this order: the gates (one dword per row), Q^ (row_slot layout), tile 0
+    if (tid < kGC) {
+      const int r = tid < ci.n ? tid : ci.n - 1;
+      dma4(p.gamma + (ci.row0 + r) * H + h, base_lds + LY::kA + wv * 256);
+    }
+    load_tile<D, kRowLayout>(static_cast<const __bf16*>(p.q), ci.row0, ci.n, 0, kGC, H, h, base_lds + LY::kQ, tid);
+    issue(0);
+    wait_vm_lgkm0<L>();   // all but tile 0 (and the state's LDS writes)
+    barrier_only();
+
+    // decay prefix A_j (base 2) of the chunk's rows, in place of the gates; the
+    // state-update weights 2^(A_last - A_m) and the chunk's total decay
+    float a = 0.f;
+    if (tid < kGC && tid < ci.n) {
+      const float l = __log2f(A_lds[tid]);
+      a = l > kLogGateFloor ? l : kLogGateFloor;
+    }
+    const float A = chunk_prefix<false>(a, wsum);
+    const float a_last = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (tid < kGC) {
+      A_lds[tid] = A;
+      W_lds[tid] = tid < ci.n ? exp2f(a_last - A) : 0.f;
+    }
+
+    // Q^T as the B operand: query row qj of this wave, dims 16kk + 8hf .. +7
+    const int j_row = 32 * wave + qj;                         // row within the chunk
+    const int j_load = j_row < ci.n ? j_row : ci.n - 1;
+    bf16x8 qf[D / 16];
+    {
+      const YOCO_LDS char* qs = smem + LY::kQ;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        qf[kk] = *reinterpret_cast<const YOCO_LDS bf16x8*>(qs + row_slot<D>(j_load, 2 * kk + hf));
+    }
+    lds_barrier();   // Q^ read by every wave (its area takes tiles 1 and 2); A and the weights in LDS
+    if (n_tiles > 1) issue(1);
+    if (n_tiles > 2) issue(2);
+
+    const bool wave_active = 32 * wave < ci.n;
+    const float Aj = A_lds[j_load];
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    if (has_state && wave_active) {
+      // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j
+      const YOCO_LDS char* sl = smem + LY::kS;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 sa = *reinterpret_cast<const YOCO_LDS bf16x8*>(sl + row_slot<D>(32 * t + qj, 2 * kk + hf));
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qf[kk], acc[t], 0, 0, 0);
+        }
+      }
+      const float e = exp2f(Aj);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) acc[t] *= e;
+    }
+    if (n_tiles > 3) {
+      lds_barrier();   // the state is read by every wave: its area takes tile 3
+      issue(3);
+    }
+    // S_{c+1} = G_c S_c + (the chunk's contribution, added tile by tile below)
+    const float G = exp2f(a_last);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) sacc[e] *= G;
+
+    // intra-chunk term and state update, tile by tile; tile t is in when at
+    // most the copies of the tiles requested after it (n_tiles - 1 - t of them)
+    // are in flight
+    static_assert(kGC / kGT == 4, "the waits below assume four tiles per chunk");
+    for (int t = 0; t < n_tiles; ++t) {
+      const int after = n_tiles - 1 - t;
+      if (after >= 3) wait_vm_lgkm0<3 * L>();
+      else if (after == 2) wait_vm_lgkm0<2 * L>();
+      else if (after == 1) wait_vm_lgkm0<L>();
+      else wait_vm_lgkm0<0>();
+      barrier_only();
+      const int key0 = t * kGT;
+      const YOCO_LDS char* ks = smem + out_stage_off(t, kStage);
+      const YOCO_LDS char* vs = ks + kTile;
+      if (wave_active && key0 <= j_row) {
+        // S^T[m][j] = K Q^T: two 32-key chains, steps (kk, kb) with kb fastest;
+        // the K reads run kGReadsAhead steps ahead of their MFMAs
+        constexpr int NQ = D / 8;
+        constexpr int RA = kGReadsAhead;
+        auto read_k = [&](int i) {
+          return *reinterpret_cast<const YOCO_LDS bf16x8*>(ks + kd_slot<D>(32 * (i & 1) + qj, 2 * (i >> 1) + hf));
+        };
+        f32x16 sc[2] = {f32x16{}, f32x16{}};
+        bf16x8 ka[NQ];
+#pragma unroll
+        for (int i = 0; i < RA; ++i) ka[i] = read_k(i);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          if (i + RA < NQ) ka[i + RA] = read_k(i + RA);
+          sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1], sc[i & 1], 0, 0, 0);
+          sched_fence();
+        }
+        // O^T += V^T P^T in steps (kb, cc2, tt) with tt fastest; the first V reads
+        // go out before the decay, whose VALU work hides their latency
+        constexpr int NT = D / 32;
+        constexpr int NV = 4 * NT;
+        auto read_v = [&](int j) { return read_tr<D>(vs, 32 * (j / (2 * NT)) + 16 * ((j / NT) & 1), j % NT, lane); };
+        bf16x8 va[NV];
+#pragma unroll
+        for (int j = 0; j < RA; ++j) va[j] = read_v(j);
+        sched_fence();
+        // P^T = S^T * 2^(A_j - A_m) for m <= j, else 0; register r of chain kb is
+        // key key0 + 32kb + 8(r/4) + 4hf + r%4
+        uint32_t w[2][2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int m0 = key0 + 32 * kb + 8 * g4 + 4 * hf;
+            const f32x4 am = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)A_lds + 4 * m0);
+            float pv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float d = __builtin_amdgcn_exp2f(Aj - am[e]);   // below 2^-126: 0 or denormal, as the product vanishes
+              pv[e] = (m0 + e <= j_row) ? sc[kb][4 * g4 + e] * d : 0.f;
+            }
+            w[kb][g4 >> 1][2 * (g4 & 1)] = pack2(pv[0], pv[1]);
+            w[kb][g4 >> 1][2 * (g4 & 1) + 1] = pack2(pv[2], pv[3]);
+          }
+        }
+        sched_fence();
+        // B operand of step (kb, cc2) = registers 8cc2 .. 8cc2 + 7 of chain kb
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int kb = j / (2 * NT), cc2 = (j / NT) & 1, tt = j % NT;
+          if (j + RA < NV) va[j + RA] = read_v(j + RA);
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[kb][cc2][0], w[kb][cc2][1], w[kb][cc2][2],
+                                                                  w[kb][cc2][3]));
+          acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[tt], 0, 0, 0);
+          sched_fence();
+        }
+      }
+      // the state update from this tile: S += (w ⊙ K)^T V over its 64 keys (rows
+      // past the chunk's end have weight 0), in steps of 16 keys whose LDS reads
+      // are issued one step ahead of their MFMAs
+      if (!sb.idle) {
+        struct StepOps {
+          bf16x8 k;
+          f32x4 w0, w1;
+          bf16x8 v[PER];
+        };
+        auto read_step = [&](int s4, StepOps& o) {
+          o.k = read_tr<D, kKdLayout>(ks, 16 * s4, sb.bi, lane);
+          o.w0 = *reinterpret_cast<const YOCO_LDS f32x4*>(W_lds + key0 + 16 * s4 + 4 * hf);
+          o.w1 = *reinterpret_cast<const YOCO_LDS f32x4*>(W_lds + key0 + 16 * s4 + 8 + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < PER; ++e) o.v[e] = read_tr<D>(vs, 16 * s4, sb.bj(e), lane);
+        };
+        StepOps op[2];
+        read_step(0, op[0]);
+#pragma unroll
+        for (int s4 = 0; s4 < kGT / 16; ++s4) {
+          if (s4 + 1 < kGT / 16) read_step(s4 + 1, op[(s4 + 1) & 1]);
+          sched_fence();
+          const StepOps& o = op[s4 & 1];
+          const bf16x8 kw = weight_keys(o.k, o.w0, o.w1);
+#pragma unroll
+          for (int e = 0; e < PER; ++e) sacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kw, o.v[e], sacc[e], 0, 0, 0);
+          sched_fence();
+        }
+      }
+    }
+    wait_vm_lgkm0<0>();
+    __syncthreads();   // the tiles are done with: stage the outputs in LDS
+
+    YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)smem + wave * (32 * kOStride);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 sa = *reinterpret_cast<const YOCO_LDS bf16x8*>(sl + row_slot<D>(32 * t + qj, 2 * kk + hf));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qf[kk], acc[t], 0, 0, 0);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const u32x2 w2 = {pack2(acc[t][4 * g4 + 0], acc[t][4 * g4 + 1]), pack2(acc[t][4 * g4 + 2], acc[t][4 * g4 + 3])};
+        *reinterpret_cast<YOCO_LDS u32x2*>(ot + qj * kOStride + 32 * t + 8 * g4 + 4 * hf) = w2;
       }
     }
-    const float e = exp2f(Aj);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __bf16* obase = static_cast<__bf16*>(p.out);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] *= e;
-  }
-  if (n_tiles > 3) {
-    lds_barrier();   // the state is read by every wave: its area takes tile 3
-    issue(3);
-  }
-
-  // intra-chunk term, tile by tile; tile t is in when at most the copies of
-  // the tiles requested after it (n_tiles - 1 - t of them) are in flight
-  static_assert(kGC / kGT == 4, "the waits below assume four tiles per chunk");
-  for (int t = 0; t < n_tiles; ++t) {
-    const int after = n_tiles - 1 - t;
-    if (after >= 3) wait_vm_lgkm0<3 * L>();
-    else if (after == 2) wait_vm_lgkm0<2 * L>();
-    else if (after == 1) wait_vm_lgkm0<L>();
-    else wait_vm_lgkm0<0>();
-    barrier_only();
-    const int key0 = t * kGT;
-    if (wave_active && key0 <= j_row) {
-      const YOCO_LDS char* ks = smem + out_stage_off(t, kStage);
-      const YOCO_LDS char* vs = ks + kTile;
-      // S^T[m][j] = K Q^T: two 32-key chains
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *reinterpret_cast<const YOCO_LDS bf16x8*>(ks + row_slot<D>(32 * kb + qj, 2 * kk + hf));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[kb], 0, 0, 0);
-        }
-      }
-      // P^T = S^T * 2^(A_j - A_m) for m <= j, else 0; register r of chain kb is
-      // key key0 + 32kb + 8(r/4) + 4hf + r%4
-      uint32_t w[2][2][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int m0 = key0 + 32 * kb + 8 * g4 + 4 * hf;
-          const f32x4 am = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)A_lds + 4 * m0);
-          float pv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float d = __builtin_amdgcn_exp2f(Aj - am[e]);   // below 2^-126: 0 or denormal, as the product vanishes
-            pv[e] = (m0 + e <= j_row) ? s[kb][4 * g4 + e] * d : 0.f;
-          }
-          w[kb][g4 >> 1][2 * (g4 & 1)] = pack2(pv[0], pv[1]);
-          w[kb][g4 >> 1][2 * (g4 & 1) + 1] = pack2(pv[2], pv[3]);
-        }
-      }
-      // O^T += V^T P^T: B operand of step (kb, cc) = registers 8cc .. 8cc + 7 of chain kb
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[kb][cc][0], w[kb][cc][1], w[kb][cc][2],
-                                                                  w[kb][cc][3]));
-#pragma unroll
-          for (int tt = 0; tt < D / 32; ++tt) {
-            const bf16x8 va = read_tr<D>(vs, 32 * kb + 16 * cc, tt, lane);
-            acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[tt], 0, 0, 0);
-          }
-        }
-      }
+    for (int i = 0; i < 32 * (D / 8) / 64; ++i) {
+      const int ci8 = lane + 64 * i;
+      const int row = ci8 / (D / 8), c8 = ci8 % (D / 8);
+      const int jr = 32 * wave + row;
+      if (jr < ci.n)
+        *reinterpret_cast<u32x4*>(obase + ((ci.row0 + jr) * H + h) * D + 8 * c8) =
+            *reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8);
     }
-  }
-  wait_vm_lgkm0<0>();
-  __syncthreads();   // the tiles are done with: stage the outputs in LDS
-
-  YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)smem + wave * (32 * kOStride);
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const u32x2 wv = {pack2(acc[t][4 * g4 + 0], acc[t][4 * g4 + 1]), pack2(acc[t][4 * g4 + 2], acc[t][4 * g4 + 3])};
-      *reinterpret_cast<YOCO_LDS u32x2*>(ot + qj * kOStride + 32 * t + 8 * g4 + 4 * hf) = wv;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  __bf16* obase = static_cast<__bf16*>(p.out);
-#pragma unroll
-  for (int i = 0; i < 32 * (D / 8) / 64; ++i) {
-    const int ci8 = lane + 64 * i;
-    const int row = ci8 / (D / 8), c8 = ci8 % (D / 8);
-    const int jr = 32 * wave + row;
-    if (jr < ci.n)
-      *reinterpret_cast<u32x4*>(obase + ((ci.row0 + jr) * H + h) * D + 8 * c8) =
-          *reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8);
   }
 }
 
@@ -612,15 +828,19 @@ __global__ __launch_bounds__(256) void gret_decode_kernel(GretParams p) {
 }  // namespace
 
 hipError_t launch_gret_prefill(const GretParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid_c(p.slots, p.heads);
+  // one workgroup per (segment slot, head), heads fastest: the slots past the
+  // last segment come last in dispatch order, so that they never take a place
+  // that a real segment waits for (within an XCD, workgroups are dealt to the
+  // shader engines in turn)
+  const dim3 grid_c((unsigned)p.slots * (unsigned)p.heads);
   const dim3 grid_s((head_dim * head_dim / 4 + 255) / 256, p.heads, p.batch);
   if (head_dim == 64) {
-    hipLaunchKernelGGL(gret_state_kernel<64>, grid_c, dim3(kGThreads), 0, stream, p);
-    hipLaunchKernelGGL(gret_scan_kernel<64>, grid_s, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gret_segstate_kernel<64>, grid_c, dim3(kGThreads), 0, stream, p);
+    hipLaunchKernelGGL(gret_segscan_kernel<64>, grid_s, dim3(256), 0, stream, p);
     hipLaunchKernelGGL(gret_out_kernel<64>, grid_c, dim3(kGThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(gret_state_kernel<128>, grid_c, dim3(kGThreads), 0, stream, p);
-    hipLaunchKernelGGL(gret_scan_kernel<128>, grid_s, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gret_segstate_kernel<128>, grid_c, dim3(kGThreads), 0, stream, p);
+    hipLaunchKernelGGL(gret_segscan_kernel<128>, grid_s, dim3(256), 0, stream, p);
     hipLaunchKernelGGL(gret_out_kernel<128>, grid_c, dim3(kGThreads), 0, stream, p);
   }
   return hipGetLastError();

@@ -85,14 +85,15 @@ struct GretParams {
   const int32_t* cu_seqlens;  // [B + 1] (prefill)
   const float* state_in;      // [B, H, D(dk), D(dv)] fp32 or null (prefill)
   float* state_out;           // [B, H, D, D]: prefill's final states; decode's states, updated in place
-  uint16_t* chunk_state;      // workspace: per chunk U^T [D(dv)][D(dk)], bf16 bits
-  uint16_t* chunk_in;         // workspace: per chunk incoming state S^T, bf16 bits
-  float* chunk_decay;         // workspace: per chunk total decay
+  float* seg_u;               // workspace: per segment slot, its state contribution U [D(dk)][D(dv)]
+  float* seg_s;               // workspace: per segment slot, its incoming state S [D(dk)][D(dv)]
+  float* seg_decay;           // workspace: per segment slot, its total decay
   int64_t total_rows;
   int32_t batch;
   int32_t heads;
-  int32_t slots;              // chunk slots per head in the workspace: ceil(total_rows / 256) + batch,
-                              // at least the chunks of all sequences together for any lengths
+  int32_t slots;              // segment slots per head in the workspace, at least the segments of
+                              // all sequences together for any lengths
+  int32_t seg_chunks;         // chunks (of 256 rows) per segment, >= 1
 };
 
 // Host launchers (one per kernel family); each returns the hipGetLastError code.

@@ -323,19 +323,24 @@ typedef struct {
 } yoco_gret_dims;
 
 /* [host] Workspace bytes of yoco_gret_prefill for total_rows packed rows (any
- * number of sequences up to dims->batch, any lengths): per head and chunk slot
- * (ceil(total_rows / 256) + batch slots) two bf16 head_dim^2 states (the
- * chunk's contribution and its incoming state) and one fp32 decay. */
+ * number of sequences up to dims->batch, any lengths): per head and segment
+ * slot two fp32 head_dim^2 states (the segment's contribution and its incoming
+ * state) and one fp32 decay. A segment is a run of consecutive 256-row chunks
+ * of one sequence (1 to 64 chunks, more as the rows grow); the size covers
+ * every call with at most total_rows rows, so it never shrinks as total_rows
+ * grows. */
 yoco_status yoco_gret_workspace_size(const yoco_gret_dims* dims, int64_t total_rows, size_t* bytes);
 
 /*
  * yoco_gret_prefill -- the chunkwise form over packed sequences: sequence b owns
  * rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (clamped to total_rows). Three
- * launches: per-chunk state contributions, the state recurrence across chunks,
- * per-chunk outputs. The chunks of all sequences are numbered one after the
- * other and found on the device, so every row of every sequence is computed
- * whatever the lengths; cu_seqlens must be non-decreasing (otherwise chunks
- * beyond the workspace's slots are left out, never written out of bounds).
+ * launches: per-segment state contributions, the state recurrence across
+ * segments, and the outputs, each segment's chunks in turn with the state
+ * carried from chunk to chunk. The segments of all sequences are numbered one
+ * after the other and found on the device, so every row of every sequence is
+ * computed whatever the lengths; cu_seqlens must be non-decreasing (otherwise
+ * segments beyond the workspace's slots are left out, never written out of
+ * bounds).
  *   total_rows [host] rows of q, k, v, gamma and out
  *   state_in   [device] [B, H, d, d] fp32 initial states, or NULL for zero
  *   state_out  [device] [B, H, d, d] fp32 states after each sequence's last row,

@@ -55,6 +55,31 @@ def check(out, ref, dtype, discriminating=False, what=""):
     return e
 
 
+def check_signed_sum(out, ref, dtype, what=""):
+    """The row-relative check for outputs that are signed sums with no
+    normalisation (gated retention: o_j = sum_m D[j,m] (q_j . k_m) v_m). Each
+    term carries the bf16 rounding of its weight, but a row whose terms cancel
+    has a max|ref| well below the terms' scale, so its row-relative error grows
+    with the cancellation, and over 10^5 rows a few rows cancel strongly. The
+    bulk keeps the softmax bound (99.9% of rows within ROW_REL) and no row may
+    exceed 4 x ROW_REL; a missing or wrong term (a dropped state, a wrong chunk)
+    gives errors of order 1 in most rows."""
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if out.shape != ref.shape:
+        raise AssertionError(f"shape {out.shape} != {ref.shape}")
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    d = out.shape[-1]
+    e2 = np.abs(out - ref).reshape(-1, d).max(axis=1)
+    r2 = np.abs(ref).reshape(-1, d).max(axis=1)
+    rel = e2 / np.maximum(r2, 1e-30)
+    bulk = float(np.quantile(rel, 0.999))
+    worst = float(rel.max())
+    assert bulk <= ROW_REL[dtype], f"{what}: 99.9th percentile row-relative {bulk:.3e} > {ROW_REL[dtype]}"
+    assert worst <= 4 * ROW_REL[dtype], f"{what}: row-relative {worst:.3e} > {4 * ROW_REL[dtype]}"
+    return {"row_rel": worst, "row_rel_p999": bulk}
+
+
 def check_lse(lse, ref, dtype, what=""):
     lse = np.asarray(lse, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

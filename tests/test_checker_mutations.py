@@ -120,3 +120,29 @@ def test_max_abs_alone_is_weak_on_small_logits():
     parity.check(_bf16(pm), ref, "bf16", discriminating=False)
     with pytest.raises(AssertionError):
         parity.check(_bf16(pm), ref, "bf16", discriminating=True)
+
+
+def test_signed_sum_check_for_gated_retention():
+    """The gRet check (bulk row-relative bound plus a looser cap for rows that
+    cancel) accepts bf16 weights and outputs and rejects a carried state that is
+    dropped or passed on without a chunk boundary's decay."""
+    import oracle.gret as og
+    rng = np.random.default_rng(5)
+    n, d = 1200, 64
+    q = _bf16(rng.standard_normal((n, d)) * d ** -0.25)
+    k = _bf16(rng.standard_normal((n, d)) * d ** -0.25)
+    v = _bf16(rng.standard_normal((n, d)))
+    gam = 0.8 + 0.2 * rng.random(n)
+    ref, _ = og.gret_recurrent_ref(q, k, v, gam)
+    sim = _bf16(_bf16((q @ k.T) * og.gret_decay_matrix(gam)) @ v)   # bf16 weights and output
+    e = parity.check_signed_sum(sim[:, None], ref[:, None], "bf16", what="sim")
+    assert e["row_rel"] < 1e-2
+    dropped = np.concatenate([og.gret_recurrent_ref(q[c:c + 256], k[c:c + 256], v[c:c + 256], gam[c:c + 256])[0]
+                              for c in range(0, n, 256)])
+    with pytest.raises(AssertionError):
+        parity.check_signed_sum(_bf16(dropped)[:, None], ref[:, None], "bf16")
+    g2 = gam.copy()
+    g2[256::256] = 1.0                       # the state enters each chunk undecayed by its first gate
+    undecayed, _ = og.gret_recurrent_ref(q, k, v, g2)
+    with pytest.raises(AssertionError):
+        parity.check_signed_sum(_bf16(undecayed)[:, None], ref[:, None], "bf16")

@@ -69,6 +69,37 @@ def test_gret_prefill(lens, heads, d, with_state):
     say(f"  out row-rel {e['row_rel']:.2e}, state rel {rel:.2e}")
 
 
+# Inputs long enough (chunks x heads >= 512) that the library groups 2 or 8
+# chunks per segment: segments that end mid-sequence, partial segments at
+# sequence ends, one-chunk sequences, initial states carried into later
+# segments. Heads are checked in a subset at the larger size to keep the fp64
+# oracle within seconds.
+@pytest.mark.parametrize("lens,heads,d,check_heads", [
+    ([5000, 1234, 7000, 300], 16, 128, None),          # 2 chunks per segment
+    ([20000, 3000], 8, 64, None),                     # head_dim 64, 2 chunks per segment
+    ([9000, 300, 17000, 6468], 16, 128, [0, 7, 15]),  # 8 chunks per segment
+])
+def test_gret_prefill_segments(lens, heads, d, check_heads):
+    say(f"gret prefill over multi-chunk segments lens={lens} H={heads} d={d}")
+    q, k, v, gam, s0, cu = _inputs(lens, heads, d, seed=len(lens) + heads + d, with_state=True)
+    out, st = _run_prefill(q, k, v, gam, s0, cu, lens)
+    sel = list(range(heads)) if check_heads is None else check_heads
+    # the fp64 recurrence, row by row (the parallel form's decay matrix is
+    # quadratic in Python loops at these lengths)
+    ref = np.zeros((q.shape[0], len(sel), d))
+    ref_st = np.zeros((len(lens), len(sel), d, d))
+    qf, kf, vf = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
+    for b in range(len(lens)):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        for i, h in enumerate(sel):
+            ref[r0:r1, i], ref_st[b, i] = oracle.gret_recurrent_ref(qf[r0:r1, h], kf[r0:r1, h], vf[r0:r1, h],
+                                                                    gam[r0:r1, h].double().numpy(),
+                                                                    s0[b, h].double().numpy())
+    e = parity.check_signed_sum(out[:, sel], ref, "bf16", what="gret prefill, segments")
+    rel = _state_check(st[:, sel], ref_st, "gret prefill, segments")
+    say(f"  out row-rel {e['row_rel']:.2e} (99.9th percentile {e['row_rel_p999']:.2e}), state rel {rel:.2e}")
+
+
 def test_gret_decode_steps():
     say("gret decode: 5 recurrent steps from a prefill's state")
     lens, heads, d = [300, 77, 1], 4, 128
