@@ -169,10 +169,9 @@ __device__ __forceinline__ void load_tile(const __bf16* src, int64_t row0, int n
   }
 }
 
-// The A operand of a state-update product, U += (w ⊙ K)^T V over 16 keys:
-// K columns 32bi + lane col at keys base + 8z + 4h + {0..3} (elements 4z..4z+3),
-// each times its key's weight (w: the chunk's weights in LDS, key0 the tile's
-// first key within the chunk).
+// The A operand of a state-update product, U += (w ⊙ K)^T V over 16 keys: the
+// K columns read transposed (elements 4z..4z+3 at keys base + 8z + 4h + {0..3}),
+// each times its key's weight (w0: keys base + 4h + {0..3}, w1: base + 8 + ...).
 __device__ __forceinline__ bf16x8 weight_keys(const bf16x8 kb, const f32x4 w0, const f32x4 w1) {
   uint32_t wv[4];
 #pragma unroll
@@ -183,16 +182,6 @@ __device__ __forceinline__ bf16x8 weight_keys(const bf16x8 kb, const f32x4 w0, c
   }
   return __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
 }
-template <int D, int LAYOUT>
-__device__ __forceinline__ bf16x8 weighted_k(const YOCO_LDS char* kt, const YOCO_LDS float* w, int key0,
-                                             int base_row, int bi, int lane) {
-  const int hf = lane >> 5;
-  const bf16x8 kb = read_tr<D, LAYOUT>(kt, base_row, bi, lane);
-  const f32x4 w0 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 4 * hf);
-  const f32x4 w1 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 8 + 4 * hf);
-  return weight_keys(kb, w0, w1);
-}
-
 // Keeps the scheduler from moving instructions across this point, so that LDS
 // operand reads stay issued ahead of the MFMAs that use them.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -251,14 +240,25 @@ __device__ __forceinline__ int64_t seg_start(const GretParams& p, int b) {
   return g;
 }
 
-__device__ __forceinline__ ChunkInfo chunk_info(const GretParams& p, int b, int c) {
-  int64_t r0 = p.cu_seqlens[b], r1 = p.cu_seqlens[b + 1];
-  if (r1 > p.total_rows) r1 = p.total_rows;
-  ChunkInfo ci{r0 + (int64_t)c * kGC, 0};
-  if (r0 < 0 || r1 <= r0) return ci;
-  const int64_t left = r1 - ci.row0;
+// Rows [r0, r1) of a sequence (clamped to the packed rows; r1 <= r0: none).
+struct SeqRows {
+  int64_t r0, r1;
+};
+__device__ __forceinline__ SeqRows seq_range(const GretParams& p, int b) {
+  SeqRows sr{p.cu_seqlens[b], p.cu_seqlens[b + 1]};
+  if (sr.r1 > p.total_rows) sr.r1 = p.total_rows;
+  return sr;
+}
+// Chunk c of a sequence, from its row range (no memory access)
+__device__ __forceinline__ ChunkInfo chunk_of(const SeqRows& sr, int c) {
+  ChunkInfo ci{sr.r0 + (int64_t)c * kGC, 0};
+  if (sr.r0 < 0 || sr.r1 <= sr.r0) return ci;
+  const int64_t left = sr.r1 - ci.row0;
   ci.n = left <= 0 ? 0 : (left < kGC ? (int)left : kGC);
   return ci;
+}
+__device__ __forceinline__ ChunkInfo chunk_info(const GretParams& p, int b, int c) {
+  return chunk_of(seq_range(p, b), c);
 }
 
 // This wave's blocks of a head_dim x head_dim state held as MFMA accumulators:
@@ -277,6 +277,31 @@ struct StateBlocks {
     bi = blk0 / NB;
   }
   __device__ int bj(int e) const { return (blk0 + e) % NB; }
+};
+
+// One 16-key step of a state update S += (w ⊙ K)^T V for this wave's blocks:
+// its LDS operands (K columns of block row bi, transposed; the keys' weights;
+// V columns of each block column, transposed), read ahead of the MFMAs.
+template <int PER>
+struct StepOps {
+  bf16x8 k;
+  f32x4 w0, w1;
+  bf16x8 v[PER];
+  template <int D, int KLAYOUT>
+  __device__ __forceinline__ void read(const YOCO_LDS char* kt, const YOCO_LDS char* vt, const YOCO_LDS float* w,
+                                       int key0, int base_row, const StateBlocks<D>& sb, int lane) {
+    const int hf = lane >> 5;
+    k = read_tr<D, KLAYOUT>(kt, base_row, sb.bi, lane);
+    w0 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 4 * hf);
+    w1 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 8 + 4 * hf);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] = read_tr<D>(vt, base_row, sb.bj(e), lane);
+  }
+  __device__ __forceinline__ void mfma(f32x16 (&acc)[PER]) const {
+    const bf16x8 kw = weight_keys(k, w0, w1);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kw, v[e], acc[e], 0, 0, 0);
+  }
 };
 
 // Wait until at most n of this wave's copies are in flight (n from a short list
@@ -367,6 +392,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_segstate_kernel(GretParams 
     for (int j = 1; j <= later; ++j) pending += ((f + j) & 3) == 0 ? 1 : 0;
     wait_copies<LQ>(pending);
     barrier_only();
+    // the next quarter goes out at once: its stage held quarter f - 1, which
+    // every wave finished before the barrier above
+    if (f + kAhead < nq) issue(f + kAhead);
     const int cf = f >> 2;
     YOCO_LDS float* wgt = (YOCO_LDS float*)(smem + LY::kWgt + (cf & 1) * (kGC * 4));
     if ((f & 3) == 0) {
@@ -388,20 +416,21 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_segstate_kernel(GretParams 
       lds_barrier();   // the weights are in for every wave
     }
     if (!sb.idle) {
+      // U += (w ⊙ K)^T V over the quarter in steps of 16 keys, each step's LDS
+      // reads issued one step ahead of its MFMAs
       const YOCO_LDS char* kt = smem + (f % kSStages) * LY::kStage;
       const YOCO_LDS char* vt = kt + LY::kQBytes;
+      const int key0 = kQ * (f & 3);
+      StepOps<PER> op[2];
+      op[0].template read<D, kTrLayout>(kt, vt, wgt, key0, 0, sb, lane);
 #pragma unroll
       for (int s4 = 0; s4 < kQ / 16; ++s4) {
-        const bf16x8 ka = weighted_k<D, kTrLayout>(kt, wgt, kQ * (f & 3), 16 * s4, sb.bi, lane);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          const bf16x8 vb = read_tr<D>(vt, 16 * s4, sb.bj(e), lane);   // V columns dv, same 8 keys
-          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, vb, acc[e], 0, 0, 0);
-        }
+        if (s4 + 1 < kQ / 16) op[(s4 + 1) & 1].template read<D, kTrLayout>(kt, vt, wgt, key0, 16 * (s4 + 1), sb, lane);
+        sched_fence();
+        op[s4 & 1].mfma(acc);
+        sched_fence();
       }
     }
-    // its stage held quarter f - 1, which every wave finished before the barrier above
-    if (f + kAhead < nq) issue(f + kAhead);
   }
   if (tid == 0) p.seg_decay[slot] = exp2f(a_seg);
   if (sb.idle) return;
@@ -467,29 +496,36 @@ __global__ __launch_bounds__(256) void gret_segscan_kernel(GretParams p) {
 // accumulators) and carries it across its chunks: each chunk's state goes into
 // LDS as bf16 for the inter-chunk product, and the chunk's own contribution is
 // added tile by tile from the K and V tiles already staged for the outputs.
-// LDS (head_dim D): every K/V tile of the chunk has its own stage, Q^ comes in
-// by the load unit and its space is handed to tiles 1 and 2 once read, the
-// state's to tile 3 once the inter-chunk product is done:
-//   [0, T)          tile 0
-//   [T, 3T)         Q^ rows of the chunk, then tiles 1 and 2
-//   [3T, 4T)        S_c^T (bf16), then tile 3
-//   [4T, 4T + 1 KB) the gates, then their prefix A
-//   [.., + 1 KB)    the state-update weights
+// LDS (head_dim D, T = one stage, a K and a V tile of 64 rows):
+//   [0, 2T)         Q^ rows of the chunk, then tiles 1 and 2; during the
+//                   chunk's last tile, the next chunk's Q^ rows
+//   [2T, 3T)        tile 0
+//   [3T, 4T)        S_c^T (bf16, written from the running state), then tile 3
+//   [2T, 2T + O)    the outputs, staged for whole-row stores (tiles 0 and 3
+//                   done with; past 4T for head_dim 128)
+//   then the gates / their prefix A (two buffers, chunk parity: the next
+//   chunk's gates come in while this chunk's prefix is in use) and the
+//   state-update weights.
 // K tiles are in the kd layout (read both ways), V tiles in the transposing one.
 template <int D>
 struct OutLds {
   static constexpr int kTile = kGT * D * 2;        // one K or V tile
   static constexpr int kStage = 2 * kTile;          // K then V
-  static constexpr int kQ = kStage;                 // Q^ area (2 stages)
+  static constexpr int kQ = 0;                      // Q^ area (2 stages)
   static constexpr int kS = 3 * kStage;             // state area (stage 3)
-  static constexpr int kA = 4 * kStage;             // gates / prefix
-  static constexpr int kW = kA + kGC * 4;           // weights
+  static constexpr int kO = 2 * kStage;             // output staging
+  static constexpr int kOStride = D + 8;            // staged output row (elements)
+  static constexpr int kOBytes = 8 * 32 * kOStride * 2;
+  static constexpr int kEnd = kO + kOBytes > 4 * kStage ? kO + kOBytes : 4 * kStage;
+  static constexpr int kA = (kEnd + 15) / 16 * 16;  // gates / prefix, 2 x kGC floats
+  static constexpr int kW = kA + 2 * kGC * 4;       // weights
   static constexpr int kBytes = kW + kGC * 4;
   static_assert(kGC * D * 2 == 2 * kStage, "the chunk's Q^ rows fill two stages");
   static_assert(D * D * 2 <= kStage, "the state fits a stage");
 };
+// tile t's stage: 0 after Q^, 1 and 2 in the Q^ area, 3 in the state area
 __device__ __forceinline__ uint32_t out_stage_off(int t, int stage) {
-  return (uint32_t)(t == 0 ? 0 : t * stage);   // tiles 1, 2 in the Q^ area, 3 in the state area
+  return (uint32_t)(t == 0 ? 2 * stage : t == 3 ? 3 * stage : (t - 1) * stage);
 }
 
 template <int D>
@@ -497,12 +533,10 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   typedef OutLds<D> LY;
   constexpr int kTile = LY::kTile;
   constexpr int kStage = LY::kStage;
-  constexpr int kOStride = D + 8;
-  static_assert(8 * 32 * kOStride * 2 <= LY::kS, "output staging fits tiles 0..2");
+  constexpr int kOStride = LY::kOStride;
   __shared__ __attribute__((aligned(16))) char smem_raw[LY::kBytes];
   __shared__ float wsum[4];
   YOCO_LDS char* smem = (YOCO_LDS char*)smem_raw;
-  YOCO_LDS float* A_lds = (YOCO_LDS float*)(smem + LY::kA);
   YOCO_LDS float* W_lds = (YOCO_LDS float*)(smem + LY::kW);
   const int h = blockIdx.x % p.heads, g = blockIdx.x / p.heads;
   int b, s;
@@ -510,6 +544,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   const int c0 = s * p.seg_chunks;
   const int left = seq_chunks(p, b) - c0;
   const int nc = left < p.seg_chunks ? left : p.seg_chunks;
+  const SeqRows sr = seq_range(p, b);   // loaded once: a load in the chunk loop would wait for the copies in flight
   const int64_t slot = (int64_t)h * p.slots + g;
   const bool has_state0 = s > 0 || p.state_in != nullptr;
   const int tid0 = threadIdx.x, wave = tid0 >> 6;
@@ -544,9 +579,18 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
     // recomputed per chunk (kept live across the loop they would not fit)
     const int tid = opaque(tid0), lane = tid & 63;
     const int qj = lane & 31, hf = lane >> 5;
-    const ChunkInfo ci = chunk_info(p, b, c0 + cc);
+    const ChunkInfo ci = chunk_of(sr, c0 + cc);
     const bool has_state = has_state0 || cc > 0;
     const int n_tiles = (ci.n + kGT - 1) / kGT;
+    YOCO_LDS float* A_lds = (YOCO_LDS float*)(smem + LY::kA + (cc & 1) * (kGC * 4));
+    // the gates and Q^ rows of chunk c (one dword per row; Q^ in the row_slot layout)
+    auto issue_q = [&](const ChunkInfo& c, int parity) {
+      if (tid < kGC) {
+        const int r = tid < c.n ? tid : c.n - 1;
+        dma4(p.gamma + (c.row0 + r) * H + h, base_lds + LY::kA + parity * (kGC * 4) + wv * 256);
+      }
+      load_tile<D, kRowLayout>(static_cast<const __bf16*>(p.q), c.row0, c.n, 0, kGC, H, h, base_lds + LY::kQ, tid);
+    };
     auto issue = [&](int t) {
       const uint32_t st = base_lds + out_stage_off(t, kStage);
       const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
@@ -554,8 +598,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       load_tile<D, kTrLayout>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile, tid);
     };
     // S_c^T into the state area as bf16 (row dv, 16-byte chunk dk / 8; each lane
-    // 4 consecutive dk of one dv); the area is free: the previous chunk's tile 3
-    // was done with before its outputs were staged
+    // 4 consecutive dk of one dv), once the previous chunk's staged outputs are
+    // read (they cover this area for head_dim 128)
+    lds_barrier();   // every wave has read its staged outputs of the previous chunk
     if (has_state && !sb.idle) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
@@ -568,14 +613,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
         }
       }
     }
-    __syncthreads();   // every wave has read its staged outputs of the previous chunk
-
-    // copies, in this order: the gates (one dword per row), Q^ (row_slot layout), tile 0
-    if (tid < kGC) {
-      const int r = tid < ci.n ? tid : ci.n - 1;
-      dma4(p.gamma + (ci.row0 + r) * H + h, base_lds + LY::kA + wv * 256);
-    }
-    load_tile<D, kRowLayout>(static_cast<const __bf16*>(p.q), ci.row0, ci.n, 0, kGC, H, h, base_lds + LY::kQ, tid);
+    // copies: the gates and Q^ (unless requested during the previous chunk), tile 0
+    if (cc == 0) issue_q(ci, 0);
     issue(0);
     wait_vm_lgkm0<L>();   // all but tile 0 (and the state's LDS writes)
     barrier_only();
@@ -607,6 +646,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
     lds_barrier();   // Q^ read by every wave (its area takes tiles 1 and 2); A and the weights in LDS
     if (n_tiles > 1) issue(1);
     if (n_tiles > 2) issue(2);
+    const bool prefetch = cc + 1 < nc;   // then this chunk is whole: four tiles
 
     const bool wave_active = 32 * wave < ci.n;
     const float Aj = A_lds[j_load];
@@ -614,15 +654,24 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
     if (has_state && wave_active) {
-      // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j
+      // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j;
+      // steps (kk, t) with the output block t fastest (consecutive MFMAs update
+      // different accumulators), the state reads kGReadsAhead steps ahead
+      constexpr int NT = D / 32;
+      constexpr int NS = NT * (D / 16);
+      constexpr int RA = kGReadsAhead;
       const YOCO_LDS char* sl = smem + LY::kS;
+      auto read_s = [&](int i) {
+        return *reinterpret_cast<const YOCO_LDS bf16x8*>(sl + row_slot<D>(32 * (i % NT) + qj, 2 * (i / NT) + hf));
+      };
+      bf16x8 sa[NS];
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
+      for (int i = 0; i < RA; ++i) sa[i] = read_s(i);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 sa = *reinterpret_cast<const YOCO_LDS bf16x8*>(sl + row_slot<D>(32 * t + qj, 2 * kk + hf));
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, qf[kk], acc[t], 0, 0, 0);
-        }
+      for (int i = 0; i < NS; ++i) {
+        if (i + RA < NS) sa[i + RA] = read_s(i + RA);
+        acc[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[i], qf[i / NT], acc[i % NT], 0, 0, 0);
+        sched_fence();
       }
       const float e = exp2f(Aj);
 #pragma unroll
@@ -648,6 +697,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       else if (after == 1) wait_vm_lgkm0<L>();
       else wait_vm_lgkm0<0>();
       barrier_only();
+      // tiles 1 and 2 are done with: the next chunk's gates and Q^ go out now
+      if (t == 3 && prefetch) issue_q(chunk_of(sr, c0 + cc + 1), (cc + 1) & 1);
       const int key0 = t * kGT;
       const YOCO_LDS char* ks = smem + out_stage_off(t, kStage);
       const YOCO_LDS char* vs = ks + kTile;
@@ -713,36 +764,20 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       // past the chunk's end have weight 0), in steps of 16 keys whose LDS reads
       // are issued one step ahead of their MFMAs
       if (!sb.idle) {
-        struct StepOps {
-          bf16x8 k;
-          f32x4 w0, w1;
-          bf16x8 v[PER];
-        };
-        auto read_step = [&](int s4, StepOps& o) {
-          o.k = read_tr<D, kKdLayout>(ks, 16 * s4, sb.bi, lane);
-          o.w0 = *reinterpret_cast<const YOCO_LDS f32x4*>(W_lds + key0 + 16 * s4 + 4 * hf);
-          o.w1 = *reinterpret_cast<const YOCO_LDS f32x4*>(W_lds + key0 + 16 * s4 + 8 + 4 * hf);
-#pragma unroll
-          for (int e = 0; e < PER; ++e) o.v[e] = read_tr<D>(vs, 16 * s4, sb.bj(e), lane);
-        };
-        StepOps op[2];
-        read_step(0, op[0]);
+        StepOps<PER> op[2];
+        op[0].template read<D, kKdLayout>(ks, vs, W_lds, key0, 0, sb, lane);
 #pragma unroll
         for (int s4 = 0; s4 < kGT / 16; ++s4) {
-          if (s4 + 1 < kGT / 16) read_step(s4 + 1, op[(s4 + 1) & 1]);
+          if (s4 + 1 < kGT / 16) op[(s4 + 1) & 1].template read<D, kKdLayout>(ks, vs, W_lds, key0, 16 * (s4 + 1), sb, lane);
           sched_fence();
-          const StepOps& o = op[s4 & 1];
-          const bf16x8 kw = weight_keys(o.k, o.w0, o.w1);
-#pragma unroll
-          for (int e = 0; e < PER; ++e) sacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kw, o.v[e], sacc[e], 0, 0, 0);
+          op[s4 & 1].mfma(sacc);
           sched_fence();
         }
       }
     }
-    wait_vm_lgkm0<0>();
-    __syncthreads();   // the tiles are done with: stage the outputs in LDS
+    lds_barrier();   // tiles 0 and 3 are done with: stage the outputs there (the next chunk's copies stay in flight)
 
-    YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)smem + wave * (32 * kOStride);
+    YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)(smem + LY::kO) + wave * (32 * kOStride);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
