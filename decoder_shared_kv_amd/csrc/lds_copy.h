@@ -45,6 +45,12 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t d
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(off), "s"(base)
                : "memory", "m0");
 }
+// ... the same with the nontemporal hint, for data read once and not again soon
+// (streamed through the caches without displacing what is reused)
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(dst), "v"(src)
+               : "memory", "m0");
+}
 // 4 bytes per lane (lane l's dword lands at dst + 4 l), per-lane 64-bit source address
 __device__ __forceinline__ void dma4(const void* src, uint32_t dst) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dword %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
