@@ -800,8 +800,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       const int row = ci8 / (D / 8), c8 = ci8 % (D / 8);
       const int jr = 32 * wave + row;
       if (jr < ci.n)
-        *reinterpret_cast<u32x4*>(obase + ((ci.row0 + jr) * H + h) * D + 8 * c8) =
-            *reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8);
+        __builtin_nontemporal_store(*reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8),
+                                    reinterpret_cast<u32x4*>(obase + ((ci.row0 + jr) * H + h) * D + 8 * c8));
     }
   }
 }
