@@ -352,3 +352,23 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(dk.YocoError):      # gRet gates in bf16
         dk.gret_decode(q[:1], q[:1], q[:1], torch.zeros(1, 4, dtype=torch.bfloat16),
                        torch.zeros(1, 4, 64, 64))
+
+
+def test_gret_workspace_never_shrinks(lib):
+    """The gRet prefill groups chunks into longer segments as the rows grow, so a
+    call with fewer rows can need more segment slots; the reported size covers
+    every smaller row count, so a workspace sized once for the longest input
+    serves every shorter one."""
+    n = ctypes.c_size_t(0)
+    for heads, batch, dim in ((1, 1, 128), (16, 1, 128), (16, 5, 64), (64, 3, 128)):
+        gd = X.GretDims(batch, heads, dim, 1)
+        rows = set(range(0, 20000, 97))
+        for seg in (1, 2, 4, 8, 16, 32, 64):          # around the row counts where segments double
+            edge = 512 * seg * 256 // heads
+            rows.update(r for r in range(edge - 600, edge + 600, 37) if r >= 0)
+        rows.update(range(0, 3_000_000, 65_537))
+        last = 0
+        for r in sorted(rows):
+            assert lib.yoco_gret_workspace_size(ctypes.byref(gd), r, ctypes.byref(n)) == 0
+            assert n.value >= last, (heads, batch, r, n.value, last)
+            last = n.value

@@ -78,6 +78,7 @@ def test_gret_prefill(lens, heads, d, with_state):
     ([5000, 1234, 7000, 300], 16, 128, None),          # 2 chunks per segment
     ([20000, 3000], 8, 64, None),                     # head_dim 64, 2 chunks per segment
     ([9000, 300, 17000, 6468], 16, 128, [0, 7, 15]),  # 8 chunks per segment
+    ([0, 9000, 1, 4500, 0, 300], 16, 128, [0, 5, 15]),  # 2 chunks per segment, empty and one-row sequences
 ])
 def test_gret_prefill_segments(lens, heads, d, check_heads):
     say(f"gret prefill over multi-chunk segments lens={lens} H={heads} d={d}")
