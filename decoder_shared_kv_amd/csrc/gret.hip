@@ -186,6 +186,7 @@ __device__ __forceinline__ bf16x8 weight_keys(const bf16x8 kb, const f32x4 w0, c
   }
   return __builtin_bit_cast(bf16x8, make_uint4(wv[0], wv[1], wv[2], wv[3]));
 }
+
 // Keeps the scheduler from moving instructions across this point, so that LDS
 // operand reads stay issued ahead of the MFMAs that use them.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
