@@ -186,3 +186,18 @@ def test_gret_32k_two_heads_against_recurrence():
                                                 gam[:, h].double().numpy())
         parity.check(out[:, h][:, None], ref[:, None], "bf16", discriminating=True, what=f"32K head {h}")
         _state_check(st[:1, h:h + 1], ref_st[None, None], f"32K head {h}")
+
+
+def test_gret_128k_long_segments_against_recurrence():
+    """131072 rows x 16 heads: 16 chunks per segment and more segments than
+    CUs (two rounds of workgroups); heads 0 and 15 against the fp64 recurrence."""
+    say("gret prefill 128K rows, 16 heads; heads 0 and 15 against the fp64 recurrence")
+    lens, heads, d = [131072], 16, 128
+    q, k, v, gam, s0, cu = _inputs(lens, heads, d, seed=34, with_state=True)
+    out, st = _run_prefill(q, k, v, gam, s0, cu, lens)
+    for h in (0, 15):
+        ref, ref_st = oracle.gret_recurrent_ref(synth.to_f64(q[:, h]), synth.to_f64(k[:, h]), synth.to_f64(v[:, h]),
+                                                gam[:, h].double().numpy(), s0[0, h].double().numpy())
+        e = parity.check_signed_sum(out[:, h][:, None], ref[:, None], "bf16", what=f"128K head {h}")
+        rel = _state_check(st[:1, h:h + 1], ref_st[None, None], f"128K head {h}")
+        say(f"  head {h}: out row-rel {e['row_rel']:.2e} (99.9th percentile {e['row_rel_p999']:.2e}), state rel {rel:.2e}")
