@@ -15,10 +15,12 @@ source hashes still match.
 `python bench_counters.py summarize <dir>` rebuilds the files from the CSVs of
 an earlier collection without running anything.
 
-`python bench_counters.py collect-sq <dir>` collects shader-sequencer counters
-of the prefill kernel (MFMA utilisation, VALU busy, instruction mix, wait
-shares, clock) in two passes and writes profiles/prefill_sq_counters.{txt,json};
-`summarize-sq <dir>` rebuilds them.
+`python bench_counters.py collect-sq <dir> [prefill|gret]` collects
+shader-sequencer counters (MFMA utilisation, VALU busy, instruction mix, wait
+shares, clock) of the prefill kernel, or of the gRet prefill's output and
+state-contribution kernels, in two passes and writes
+profiles/{prefill,gret}_sq_counters.{txt,json}; `summarize-sq <dir> [target]`
+rebuilds them.
 
 `python bench_counters.py stats <run_kernel_stats.csv> <out.txt> <title> <command>`
 writes the text summary of a rocprofv3 --kernel-trace --stats run.
@@ -143,8 +145,8 @@ def summarize(src_dir):
     print("\n".join(lines))
 
 
-# Shader-sequencer counters of the prefill kernel, in passes small enough for
-# one rocprofv3 collection each (6 SQ counters and GRBM_GUI_ACTIVE per pass).
+# Shader-sequencer counters of a benchmark run's kernels, in passes small enough
+# for one rocprofv3 collection each (6 SQ counters and GRBM_GUI_ACTIVE per pass).
 # MfmaUtil, VALUBusy and LDSBankConflict are rocprofv3's derived metrics
 # (reduce(SQ_VALU_MFMA_BUSY_CYCLES, sum) / (reduce(GRBM_GUI_ACTIVE, max) *
 # SIMD_NUM) * 100, and alike).
@@ -154,25 +156,37 @@ SQ_PASSES = {
     "b": ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_LDS",
           "GRBM_GUI_ACTIVE"],
 }
-SQ_KERNEL = "prefill_bf16_kernel<128>"
+# target -> the run, its kernels, the file stem under profiles/ and the workload in words
+SQ_TARGETS = {
+    "prefill": {"run": "prefill", "kernels": ["prefill_bf16_kernel<128>"], "stem": "prefill_sq_counters",
+                "what": "32K causal prefill, Hq=16, Hkv=4, d=128"},
+    "gret": {"run": "gret", "kernels": ["gret_out_kernel<128>", "gret_segstate_kernel<128>"],
+             "stem": "gret_sq_counters", "what": "gRet chunkwise prefill, 32K rows x 16 heads, d=128"},
+}
 
 
-def collect_sq(out):
+def _sq_dir(src_dir, target, name):
+    # the prefill's passes keep their original directory names
+    return os.path.join(src_dir, f"sq_{name}" if target == "prefill" else f"sq_{target}_{name}")
+
+
+def collect_sq(out, target="prefill"):
     out = os.path.abspath(out)
     os.makedirs(out, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp")
+    run = SQ_TARGETS[target]["run"]
     for name, counters in SQ_PASSES.items():
-        d = os.path.join(out, f"sq_{name}")
+        d = _sq_dir(out, target, name)
         cmd = ["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "run", "--",
-               sys.executable, os.path.join(ROOT, "bench.py"), *RUNS["prefill"]]
-        print(f"[counters] prefill SQ pass {name}: {' '.join(counters)}", flush=True)
+               sys.executable, os.path.join(ROOT, "bench.py"), *RUNS[run]]
+        print(f"[counters] {target} SQ pass {name}: {' '.join(counters)}", flush=True)
         t = time.time()
         r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=240)
         if r.returncode != 0 or not os.path.exists(os.path.join(d, "run_counter_collection.csv")):
             print(r.stdout[-2000:], r.stderr[-2000:], file=sys.stderr)
             raise SystemExit(f"rocprofv3 failed for SQ pass {name}")
         print(f"[counters]   done in {time.time() - t:.0f} s", flush=True)
-    summarize_sq(out)
+    summarize_sq(out, target)
 
 
 def _kernel_rows(path, prefix):
@@ -188,11 +202,11 @@ def _kernel_rows(path, prefix):
     return vals, list(spans.values())
 
 
-def summarize_sq(src_dir):
+def _sq_kernel(src_dir, target, kernel):
     per = {}
     durations = []
     for name in SQ_PASSES:
-        vals, spans = _kernel_rows(os.path.join(src_dir, f"sq_{name}"), SQ_KERNEL)
+        vals, spans = _kernel_rows(_sq_dir(src_dir, target, name), kernel)
         for k, v in vals.items():
             per.setdefault(k, []).extend(v)
         durations += [e - s for s, e in spans if e > s]
@@ -211,25 +225,38 @@ def summarize_sq(src_dir):
         derived["share of wave time waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES)"] = mean.get("SQ_WAIT_ANY", 0) / mean["SQ_WAVE_CYCLES"]
         derived["share of wave time waiting for an instruction (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)"] = \
             mean.get("SQ_WAIT_INST_ANY", 0) / mean["SQ_WAVE_CYCLES"]
-    result = {"kernel": SQ_KERNEL, "source_sha256": source_hash(KERNELS[SQ_KERNEL]),
-              "workload": "bench.py " + " ".join(RUNS["prefill"]), "passes": SQ_PASSES,
-              "mean_per_launch": mean, "launches": launches, "duration_ns": dur_ns, "derived": derived}
+    return {"kernel": kernel, "source_sha256": source_hash(KERNELS[kernel]), "mean_per_launch": mean,
+            "launches": launches, "duration_ns": dur_ns, "derived": derived}
+
+
+def summarize_sq(src_dir, target="prefill"):
+    tg = SQ_TARGETS[target]
+    results = [_sq_kernel(src_dir, target, k) for k in tg["kernels"]]
+    workload = "bench.py " + " ".join(RUNS[tg["run"]])
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, "prefill_sq_counters.json"), "w") as f:
-        json.dump(result, f, indent=1)
-    lines = [f"Shader-sequencer counters of {SQ_KERNEL} (32K causal prefill, Hq=16, Hkv=4, d=128), per launch",
-             "command: python bench_counters.py collect-sq <dir>   (per pass: rocprofv3 --pmc <counters> "
-             "--output-format csv -d <dir> -o run -- python bench.py " + " ".join(RUNS["prefill"]) + ")",
-             "passes: " + "; ".join(f"{k}: {' '.join(v)}" for k, v in SQ_PASSES.items()),
-             f"source sha256 {result['source_sha256'][:16]}, mean kernel duration under the counters: "
-             + (f"{dur_ns / 1e3:.1f} us" if dur_ns else "n/a"), ""]
-    for k in sorted(mean):
-        lines.append(f"{k:32s} {mean[k]:16.6g}   ({launches[k]} dispatches)")
-    lines.append("")
-    for k, v in derived.items():
-        lines.append(f"{k}: {v:.4g}")
-    with open(os.path.join(PROFILES, "prefill_sq_counters.txt"), "w") as f:
-        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(PROFILES, tg["stem"] + ".json"), "w") as f:
+        if len(results) == 1:
+            json.dump({**results[0], "workload": workload, "passes": SQ_PASSES}, f, indent=1)
+        else:
+            json.dump({"workload": workload, "passes": SQ_PASSES, "kernels": results}, f, indent=1)
+    cmd = "python bench_counters.py collect-sq <dir>" + ("" if target == "prefill" else f" {target}")
+    lines = []
+    for res in results:
+        mean, launches, dur_ns = res["mean_per_launch"], res["launches"], res["duration_ns"]
+        lines += [f"Shader-sequencer counters of {res['kernel']} ({tg['what']}), per launch",
+                  f"command: {cmd}   (per pass: rocprofv3 --pmc <counters> --output-format csv -d <dir> -o run "
+                  f"-- python {workload})",
+                  "passes: " + "; ".join(f"{k}: {' '.join(v)}" for k, v in SQ_PASSES.items()),
+                  f"source sha256 {res['source_sha256'][:16]}, mean kernel duration under the counters: "
+                  + (f"{dur_ns / 1e3:.1f} us" if dur_ns else "n/a"), ""]
+        for k in sorted(mean):
+            lines.append(f"{k:32s} {mean[k]:16.6g}   ({launches[k]} dispatches)")
+        lines.append("")
+        for k, v in res["derived"].items():
+            lines.append(f"{k}: {v:.4g}")
+        lines.append("")
+    with open(os.path.join(PROFILES, tg["stem"] + ".txt"), "w") as f:
+        f.write("\n".join(lines).rstrip("\n") + "\n")
     print("\n".join(lines))
 
 
@@ -274,9 +301,9 @@ if __name__ == "__main__":
     elif len(sys.argv) >= 6 and sys.argv[1] == "stats":
         kernel_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     elif len(sys.argv) >= 3 and sys.argv[1] == "collect-sq":
-        collect_sq(sys.argv[2])
+        collect_sq(sys.argv[2], *sys.argv[3:4])
     elif len(sys.argv) >= 3 and sys.argv[1] == "summarize-sq":
-        summarize_sq(sys.argv[2])
+        summarize_sq(sys.argv[2], *sys.argv[3:4])
     else:
         print(__doc__)
         sys.exit(2)
