@@ -116,7 +116,21 @@ __device__ __forceinline__ uint32_t kd_slot(int r, int c) {
   return (uint32_t)(r * (D * 2) + 16 * (c ^ kd_swizzle<D>(r)));
 }
 
-enum TileLayout { kRowLayout, kTrLayout, kKdLayout };
+// ... and of the output pass's V tile, read transposed both by the state update
+// (4 rows x 64 bytes per 16 lanes) and by the products with the scores (16 lanes
+// at 4 rows x 32 bytes, the lane groups 4 rows apart): a map linear in the bits
+// of r mod 8 under which both fall on distinct banks (32 lanes x 8 bytes; 32
+// and 64 banks, checked by enumeration on the host)
+template <int D>
+__device__ __forceinline__ int pv_swizzle(int r) {
+  if constexpr (D == 128) {
+    return (4 * (r & 1)) ^ (10 * ((r >> 1) & 1)) ^ (2 * ((r >> 2) & 1));
+  } else {
+    return (2 * (r & 1)) ^ (4 * ((r >> 1) & 1)) ^ (2 * ((r >> 2) & 1));
+  }
+}
+
+enum TileLayout { kRowLayout, kTrLayout, kKdLayout, kPvLayout };
 
 // x, hidden from the optimiser: per-lane offsets derived from it are computed
 // where they are used instead of being kept live (or spilled) across a loop
@@ -129,6 +143,7 @@ template <int D, int LAYOUT>
 __device__ __forceinline__ int tile_swizzle(int r) {
   if constexpr (LAYOUT == kRowLayout) return r & (D / 8 - 1);
   else if constexpr (LAYOUT == kTrLayout) return v_swizzle<D>(r);
+  else if constexpr (LAYOUT == kPvLayout) return pv_swizzle<D>(r);
   else return kd_swizzle<D>(r);
 }
 
@@ -146,6 +161,21 @@ __device__ __forceinline__ bf16x8 read_tr(const YOCO_LDS char* tile, int base_ro
   const YOCO_LDS char* p8 = tile + (r + 8) * (D * 2) + 16 * (chunk ^ tile_swizzle<D, LAYOUT>(r + 8)) + 8 * (w & 1);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p8));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Transposing read of a 16 x 32 A operand V^T of a 16 x 16 x 32 product from a
+// kPvLayout tile: dims 16t + (lane & 15) at rows base + 4g + {0..3} and
+// base + 16 + 4g + {0..3}, g = lane / 16 (k slots 8g .. 8g + 7 in that order).
+template <int D>
+__device__ __forceinline__ bf16x8 read_pv(const YOCO_LDS char* tile, int base_row, int t, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const int r = base_row + 4 * g + (i >> 2);
+  const int chunk = 2 * t + ((i & 3) >> 1);
+  const YOCO_LDS char* p = tile + r * (D * 2) + 16 * (chunk ^ pv_swizzle<D>(r)) + 8 * (i & 1);
+  const YOCO_LDS char* p16 = tile + (r + 16) * (D * 2) + 16 * (chunk ^ pv_swizzle<D>(r + 16)) + 8 * (i & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(p16));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -292,7 +322,7 @@ struct StepOps {
   bf16x8 k;
   f32x4 w0, w1;
   bf16x8 v[PER];
-  template <int D, int KLAYOUT>
+  template <int D, int KLAYOUT, int VLAYOUT = kTrLayout>
   __device__ __forceinline__ void read(const YOCO_LDS char* kt, const YOCO_LDS char* vt, const YOCO_LDS float* w,
                                        int key0, int base_row, const StateBlocks<D>& sb, int lane) {
     const int hf = lane >> 5;
@@ -300,7 +330,7 @@ struct StepOps {
     w0 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 4 * hf);
     w1 = *reinterpret_cast<const YOCO_LDS f32x4*>(w + key0 + base_row + 8 + 4 * hf);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) v[e] = read_tr<D>(vt, base_row, sb.bj(e), lane);
+    for (int e = 0; e < PER; ++e) v[e] = read_tr<D, VLAYOUT>(vt, base_row, sb.bj(e), lane);
   }
   __device__ __forceinline__ void mfma(f32x16 (&acc)[PER]) const {
     const bf16x8 kw = weight_keys(k, w0, w1);
@@ -559,6 +589,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
   const __bf16* vg = static_cast<const __bf16*>(p.v);
   const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
   constexpr int L = 2 * (kGT * D / 8 / kGThreads);   // copies per thread and tile
+  constexpr int kQHalf = (kGC / 2) * D / 8 / kGThreads;   // copies per thread of half a chunk's Q^ rows
 
   // the running state S (fp32): the segment's incoming state, then after each chunk
   const StateBlocks<D> sb(wave);
@@ -583,24 +614,31 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
     // the per-lane LDS offsets of the chunk's prologue and epilogue are
     // recomputed per chunk (kept live across the loop they would not fit)
     const int tid = opaque(tid0), lane = tid & 63;
-    const int qj = lane & 31, hf = lane >> 5;
+    const int hf = lane >> 5;
     const ChunkInfo ci = chunk_of(sr, c0 + cc);
     const bool has_state = has_state0 || cc > 0;
     const int n_tiles = (ci.n + kGT - 1) / kGT;
     YOCO_LDS float* A_lds = (YOCO_LDS float*)(smem + LY::kA + (cc & 1) * (kGC * 4));
     // the gates and Q^ rows of chunk c (one dword per row; Q^ in the row_slot layout)
-    auto issue_q = [&](const ChunkInfo& c, int parity) {
-      if (tid < kGC) {
-        const int r = tid < c.n ? tid : c.n - 1;
+    // (in two halves: Q^ rows 0 .. kGC/2 - 1, then the rest and the gates)
+    auto issue_q_half = [&](const ChunkInfo& c, int parity, int half) {
+      const int tq = opaque(tid0);   // offsets computed here, not kept live across the tile loop
+      if (half == 1 && tq < kGC) {
+        const int r = tq < c.n ? tq : c.n - 1;
         dma4(p.gamma + (c.row0 + r) * H + h, base_lds + LY::kA + parity * (kGC * 4) + wv * 256);
       }
-      load_tile<D, kRowLayout, true>(static_cast<const __bf16*>(p.q), c.row0, c.n, 0, kGC, H, h, base_lds + LY::kQ, tid);
+      load_tile<D, kRowLayout, true>(static_cast<const __bf16*>(p.q), c.row0, c.n, half * (kGC / 2), kGC / 2, H, h,
+                                     base_lds + LY::kQ + half * (kGC / 2) * (D * 2), tq);
+    };
+    auto issue_q = [&](const ChunkInfo& c, int parity) {
+      issue_q_half(c, parity, 0);
+      issue_q_half(c, parity, 1);
     };
     auto issue = [&](int t) {
       const uint32_t st = base_lds + out_stage_off(t, kStage);
       const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
       load_tile<D, kKdLayout>(kg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st, tid);
-      load_tile<D, kTrLayout>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile, tid);
+      load_tile<D, kPvLayout>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile, tid);
     };
     // S_c^T into the state area as bf16 (row dv, 16-byte chunk dk / 8; each lane
     // 4 consecutive dk of one dv), once the previous chunk's staged outputs are
@@ -638,36 +676,49 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       W_lds[tid] = tid < ci.n ? exp2f(a_last - A) : 0.f;
     }
 
-    // Q^T as the B operand: query row qj of this wave, dims 16kk + 8hf .. +7
-    const int j_row = 32 * wave + qj;                         // row within the chunk
-    const int j_load = j_row < ci.n ? j_row : ci.n - 1;
-    bf16x8 qf[D / 16];
+    // This wave's query rows: two blocks of 16, lo = chunk rows 16w .. 16w + 15
+    // and hi = rows 16(15 - w) .., so that every wave meets the same share of the
+    // causal triangle (2.5 of the chunk's 64-key tiles; blocks of 32 rows would
+    // meet 1 to 4). Products on 16 x 16 x 32 MFMAs with query row 16 blk + (lane
+    // & 15) as the column: Q^T as the B operand, dims 32ks + 8qg .. +7.
+    constexpr int KS = D / 32;   // 32-dim steps
+    constexpr int NT = D / 16;   // 16-dim output blocks
+    const int ql = lane & 15, qg = lane >> 4;
+    const int blo = wave, bhi = 15 - wave;
+    const int jr0 = 16 * blo + ql, jr1 = 16 * bhi + ql;   // rows within the chunk
+    const int jl0 = jr0 < ci.n ? jr0 : ci.n - 1, jl1 = jr1 < ci.n ? jr1 : ci.n - 1;
+    bf16x8 qf[2][KS];
     {
       const YOCO_LDS char* qs = smem + LY::kQ;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        qf[kk] = *reinterpret_cast<const YOCO_LDS bf16x8*>(qs + row_slot<D>(j_load, 2 * kk + hf));
+      for (int ks = 0; ks < KS; ++ks) {
+        qf[0][ks] = *reinterpret_cast<const YOCO_LDS bf16x8*>(qs + row_slot<D>(jl0, 4 * ks + qg));
+        qf[1][ks] = *reinterpret_cast<const YOCO_LDS bf16x8*>(qs + row_slot<D>(jl1, 4 * ks + qg));
+      }
     }
-    lds_barrier();   // Q^ read by every wave (its area takes tiles 1 and 2); A and the weights in LDS
+    lds_barrier();   // Q^ read by every wave (its area takes tiles 1 and 2); A in LDS
     if (n_tiles > 1) issue(1);
     if (n_tiles > 2) issue(2);
     const bool prefetch = cc + 1 < nc;   // then this chunk is whole: four tiles
 
-    const bool wave_active = 32 * wave < ci.n;
-    const float Aj = A_lds[j_load];
-    f32x16 acc[D / 32];
+    // block hi holds rows only if block lo does; a block without rows is still
+    // computed beside a block with rows (on clamped rows, never stored)
+    const bool lo_rows = 16 * blo < ci.n, hi_rows = 16 * bhi < ci.n;
+    const float Aj0 = A_lds[jl0], Aj1 = A_lds[jl1];
+    f32x4 acc[2][NT];   // O^T of block b: dims 16t + 4qg + r (register r), query row jr_b
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-    if (has_state && wave_active) {
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (has_state && lo_rows) {
       // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j;
-      // steps (kk, t) with the output block t fastest (consecutive MFMAs update
-      // different accumulators), the state reads kGReadsAhead steps ahead
-      constexpr int NT = D / 32;
-      constexpr int NS = NT * (D / 16);
+      // steps (ks, t) with the output block t fastest, each state operand serving
+      // both query blocks, the state reads kGReadsAhead steps ahead
+      constexpr int NS = KS * NT;
       constexpr int RA = kGReadsAhead;
       const YOCO_LDS char* sl = smem + LY::kS;
       auto read_s = [&](int i) {
-        return *reinterpret_cast<const YOCO_LDS bf16x8*>(sl + row_slot<D>(32 * (i % NT) + qj, 2 * (i / NT) + hf));
+        return *reinterpret_cast<const YOCO_LDS bf16x8*>(sl + row_slot<D>(16 * (i % NT) + ql, 4 * (i / NT) + qg));
       };
       bf16x8 sa[NS];
 #pragma unroll
@@ -675,12 +726,16 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         if (i + RA < NS) sa[i + RA] = read_s(i + RA);
-        acc[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[i], qf[i / NT], acc[i % NT], 0, 0, 0);
+        acc[0][i % NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[i], qf[0][i / NT], acc[0][i % NT], 0, 0, 0);
+        acc[1][i % NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[i], qf[1][i / NT], acc[1][i % NT], 0, 0, 0);
         sched_fence();
       }
-      const float e = exp2f(Aj);
+      const float e0 = exp2f(Aj0), e1 = exp2f(Aj1);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) acc[t] *= e;
+      for (int t = 0; t < NT; ++t) {
+        acc[0][t] *= e0;
+        acc[1][t] *= e1;
+      }
     }
     if (n_tiles > 3) {
       lds_barrier();   // the state is read by every wave: its area takes tile 3
@@ -691,6 +746,81 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) sacc[e] *= G;
 
+    // One key tile against the query blocks in MASK (bit 0: lo, bit 1: hi)
+    auto tile_body = [&](auto mask_c, const YOCO_LDS char* kt, const YOCO_LDS char* vt, int key0) {
+      constexpr int MASK = decltype(mask_c)::value;
+      constexpr int RA = kGReadsAhead;
+      // S^T[m][j] = K Q^T per group kb of 16 keys: steps (ks, kb) with kb fastest,
+      // each K operand serving the blocks in MASK, the reads RA steps ahead
+      constexpr int NQ = 4 * KS;
+      auto read_k = [&](int i) {
+        return *reinterpret_cast<const YOCO_LDS bf16x8*>(kt + kd_slot<D>(16 * (i & 3) + ql, 4 * (i >> 2) + qg));
+      };
+      f32x4 sc[2][4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sc[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 ka[NQ];
+#pragma unroll
+      for (int i = 0; i < RA; ++i) ka[i] = read_k(i);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        if (i + RA < NQ) ka[i + RA] = read_k(i + RA);
+        if constexpr ((MASK & 1) != 0)
+          sc[0][i & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qf[0][i >> 2], sc[0][i & 3], 0, 0, 0);
+        if constexpr ((MASK & 2) != 0)
+          sc[1][i & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qf[1][i >> 2], sc[1][i & 3], 0, 0, 0);
+        sched_fence();
+      }
+      // O^T += V^T P^T in steps (s, t), t fastest: the A operand is V^T at dims
+      // 16t .. 16t + 15 and keys 32s + 4qg + {0..3}, 32s + 16 + 4qg + {0..3}; the
+      // first V reads go out before the decay, whose VALU work hides their latency
+      constexpr int NV = 2 * NT;
+      auto read_v = [&](int j) { return read_pv<D>(vt, 32 * (j / NT), j % NT, lane); };
+      bf16x8 va[NV];
+#pragma unroll
+      for (int j = 0; j < RA; ++j) va[j] = read_v(j);
+      sched_fence();
+      // P^T = S^T * 2^(A_j - A_m) for m <= j, else 0; register r of group kb is key
+      // key0 + 16kb + 4qg + r, so words 0..3 of w[b][s] are the B operand of step s
+      uint32_t w[2][2][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int m0 = key0 + 16 * kb + 4 * qg;
+        const f32x4 am = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)A_lds + 4 * m0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          if (((MASK >> b) & 1) == 0) continue;
+          const float Ajb = b == 0 ? Aj0 : Aj1;
+          const int jrb = b == 0 ? jr0 : jr1;
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float d = __builtin_amdgcn_exp2f(Ajb - am[e]);   // below 2^-126: 0 or denormal, as the product vanishes
+            pv[e] = (m0 + e <= jrb) ? sc[b][kb][e] * d : 0.f;
+          }
+          w[b][kb >> 1][2 * (kb & 1)] = pack2(pv[0], pv[1]);
+          w[b][kb >> 1][2 * (kb & 1) + 1] = pack2(pv[2], pv[3]);
+        }
+      }
+      sched_fence();
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int s = j / NT, tt = j % NT;
+        if (j + RA < NV) va[j + RA] = read_v(j + RA);
+        if constexpr ((MASK & 1) != 0) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[0][s][0], w[0][s][1], w[0][s][2], w[0][s][3]));
+          acc[0][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, acc[0][tt], 0, 0, 0);
+        }
+        if constexpr ((MASK & 2) != 0) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[1][s][0], w[1][s][1], w[1][s][2], w[1][s][3]));
+          acc[1][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb, acc[1][tt], 0, 0, 0);
+        }
+        sched_fence();
+      }
+    };
+
     // intra-chunk term and state update, tile by tile; tile t is in when at
     // most the copies of the tiles requested after it (n_tiles - 1 - t of them)
     // are in flight
@@ -700,80 +830,29 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       if (after >= 3) wait_vm_lgkm0<3 * L>();
       else if (after == 2) wait_vm_lgkm0<2 * L>();
       else if (after == 1) wait_vm_lgkm0<L>();
+      else if (prefetch) wait_vm_lgkm0<kQHalf>();   // the next chunk's first Q^ rows may stay in flight
       else wait_vm_lgkm0<0>();
       barrier_only();
-      // tiles 1 and 2 are done with: the next chunk's gates and Q^ go out now
-      if (t == 3 && prefetch) issue_q(chunk_of(sr, c0 + cc + 1), (cc + 1) & 1);
+      // the next chunk's Q^ rows go out as their stages free up: the first half
+      // once tile 1 is done with, the rest and the gates once tile 2 is
+      if (t == 2 && prefetch) issue_q_half(chunk_of(sr, c0 + cc + 1), (cc + 1) & 1, 0);
+      if (t == 3 && prefetch) issue_q_half(chunk_of(sr, c0 + cc + 1), (cc + 1) & 1, 1);
       const int key0 = t * kGT;
       const YOCO_LDS char* ks = smem + out_stage_off(t, kStage);
       const YOCO_LDS char* vs = ks + kTile;
-      if (wave_active && key0 <= j_row) {
-        // S^T[m][j] = K Q^T: two 32-key chains, steps (kk, kb) with kb fastest;
-        // the K reads run kGReadsAhead steps ahead of their MFMAs
-        constexpr int NQ = D / 8;
-        constexpr int RA = kGReadsAhead;
-        auto read_k = [&](int i) {
-          return *reinterpret_cast<const YOCO_LDS bf16x8*>(ks + kd_slot<D>(32 * (i & 1) + qj, 2 * (i >> 1) + hf));
-        };
-        f32x16 sc[2] = {f32x16{}, f32x16{}};
-        bf16x8 ka[NQ];
-#pragma unroll
-        for (int i = 0; i < RA; ++i) ka[i] = read_k(i);
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          if (i + RA < NQ) ka[i + RA] = read_k(i + RA);
-          sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1], sc[i & 1], 0, 0, 0);
-          sched_fence();
-        }
-        // O^T += V^T P^T in steps (kb, cc2, tt) with tt fastest; the first V reads
-        // go out before the decay, whose VALU work hides their latency
-        constexpr int NT = D / 32;
-        constexpr int NV = 4 * NT;
-        auto read_v = [&](int j) { return read_tr<D>(vs, 32 * (j / (2 * NT)) + 16 * ((j / NT) & 1), j % NT, lane); };
-        bf16x8 va[NV];
-#pragma unroll
-        for (int j = 0; j < RA; ++j) va[j] = read_v(j);
-        sched_fence();
-        // P^T = S^T * 2^(A_j - A_m) for m <= j, else 0; register r of chain kb is
-        // key key0 + 32kb + 8(r/4) + 4hf + r%4
-        uint32_t w[2][2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int m0 = key0 + 32 * kb + 8 * g4 + 4 * hf;
-            const f32x4 am = *reinterpret_cast<const YOCO_LDS f32x4*>((const YOCO_LDS char*)A_lds + 4 * m0);
-            float pv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float d = __builtin_amdgcn_exp2f(Aj - am[e]);   // below 2^-126: 0 or denormal, as the product vanishes
-              pv[e] = (m0 + e <= j_row) ? sc[kb][4 * g4 + e] * d : 0.f;
-            }
-            w[kb][g4 >> 1][2 * (g4 & 1)] = pack2(pv[0], pv[1]);
-            w[kb][g4 >> 1][2 * (g4 & 1) + 1] = pack2(pv[2], pv[3]);
-          }
-        }
-        sched_fence();
-        // B operand of step (kb, cc2) = registers 8cc2 .. 8cc2 + 7 of chain kb
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const int kb = j / (2 * NT), cc2 = (j / NT) & 1, tt = j % NT;
-          if (j + RA < NV) va[j + RA] = read_v(j + RA);
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[kb][cc2][0], w[kb][cc2][1], w[kb][cc2][2],
-                                                                  w[kb][cc2][3]));
-          acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[tt], 0, 0, 0);
-          sched_fence();
-        }
-      }
+      // the blocks whose rows reach this tile (hi's whenever lo's do)
+      if (lo_rows && key0 <= 16 * blo + 15) tile_body(std::integral_constant<int, 3>{}, ks, vs, key0);
+      else if (hi_rows && key0 <= 16 * bhi + 15) tile_body(std::integral_constant<int, 2>{}, ks, vs, key0);
       // the state update from this tile: S += (w ⊙ K)^T V over its 64 keys (rows
       // past the chunk's end have weight 0), in steps of 16 keys whose LDS reads
       // are issued one step ahead of their MFMAs
       if (!sb.idle) {
         StepOps<PER> op[2];
-        op[0].template read<D, kKdLayout>(ks, vs, W_lds, key0, 0, sb, lane);
+        op[0].template read<D, kKdLayout, kPvLayout>(ks, vs, W_lds, key0, 0, sb, lane);
 #pragma unroll
         for (int s4 = 0; s4 < kGT / 16; ++s4) {
-          if (s4 + 1 < kGT / 16) op[(s4 + 1) & 1].template read<D, kKdLayout>(ks, vs, W_lds, key0, 16 * (s4 + 1), sb, lane);
+          if (s4 + 1 < kGT / 16)
+            op[(s4 + 1) & 1].template read<D, kKdLayout, kPvLayout>(ks, vs, W_lds, key0, 16 * (s4 + 1), sb, lane);
           sched_fence();
           op[s4 & 1].mfma(sacc);
           sched_fence();
@@ -782,13 +861,14 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
     }
     lds_barrier();   // tiles 0 and 3 are done with: stage the outputs there (the next chunk's copies stay in flight)
 
+    // staged row 16b + ql holds block b's row; then whole rows are stored
     YOCO_LDS __bf16* ot = (YOCO_LDS __bf16*)(smem + LY::kO) + wave * (32 * kOStride);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const u32x2 w2 = {pack2(acc[t][4 * g4 + 0], acc[t][4 * g4 + 1]), pack2(acc[t][4 * g4 + 2], acc[t][4 * g4 + 3])};
-        *reinterpret_cast<YOCO_LDS u32x2*>(ot + qj * kOStride + 32 * t + 8 * g4 + 4 * hf) = w2;
+      for (int t = 0; t < NT; ++t) {
+        const u32x2 w2 = {pack2(acc[b][t][0], acc[b][t][1]), pack2(acc[b][t][2], acc[b][t][3])};
+        *reinterpret_cast<YOCO_LDS u32x2*>(ot + (16 * b + ql) * kOStride + 16 * t + 4 * qg) = w2;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -799,7 +879,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
     for (int i = 0; i < 32 * (D / 8) / 64; ++i) {
       const int ci8 = lane + 64 * i;
       const int row = ci8 / (D / 8), c8 = ci8 % (D / 8);
-      const int jr = 32 * wave + row;
+      const int jr = row < 16 ? 16 * blo + row : 16 * bhi + (row - 16);
       if (jr < ci.n)
         __builtin_nontemporal_store(*reinterpret_cast<const YOCO_LDS u32x4*>(ot + row * kOStride + 8 * c8),
                                     reinterpret_cast<u32x4*>(obase + ((ci.row0 + jr) * H + h) * D + 8 * c8));
