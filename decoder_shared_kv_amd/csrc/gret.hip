@@ -746,9 +746,12 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) sacc[e] *= G;
 
-    // One key tile against the query blocks in MASK (bit 0: lo, bit 1: hi)
-    auto tile_body = [&](auto mask_c, const YOCO_LDS char* kt, const YOCO_LDS char* vt, int key0) {
+    // One key tile against the query blocks in MASK (bit 0: lo, bit 1: hi), the
+    // causal mask applied to those in CAUSAL (the others lie wholly below the
+    // diagonal)
+    auto tile_body = [&](auto mask_c, auto causal_c, const YOCO_LDS char* kt, const YOCO_LDS char* vt, int key0) {
       constexpr int MASK = decltype(mask_c)::value;
+      constexpr int CAUSAL = decltype(causal_c)::value;
       constexpr int RA = kGReadsAhead;
       // S^T[m][j] = K Q^T per group kb of 16 keys: steps (ks, kb) with kb fastest,
       // each K operand serving the blocks in MASK, the reads RA steps ahead
@@ -798,7 +801,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float d = __builtin_amdgcn_exp2f(Ajb - am[e]);   // below 2^-126: 0 or denormal, as the product vanishes
-            pv[e] = (m0 + e <= jrb) ? sc[b][kb][e] * d : 0.f;
+            if (((CAUSAL >> b) & 1) != 0) pv[e] = (m0 + e <= jrb) ? sc[b][kb][e] * d : 0.f;
+            else pv[e] = sc[b][kb][e] * d;
           }
           w[b][kb >> 1][2 * (kb & 1)] = pack2(pv[0], pv[1]);
           w[b][kb >> 1][2 * (kb & 1) + 1] = pack2(pv[2], pv[3]);
@@ -840,9 +844,19 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       const int key0 = t * kGT;
       const YOCO_LDS char* ks = smem + out_stage_off(t, kStage);
       const YOCO_LDS char* vs = ks + kTile;
-      // the blocks whose rows reach this tile (hi's whenever lo's do)
-      if (lo_rows && key0 <= 16 * blo + 15) tile_body(std::integral_constant<int, 3>{}, ks, vs, key0);
-      else if (hi_rows && key0 <= 16 * bhi + 15) tile_body(std::integral_constant<int, 2>{}, ks, vs, key0);
+      // the blocks whose rows reach this tile (hi's whenever lo's do; a tile
+      // that reaches lo's rows lies wholly below hi's)
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      if (lo_rows && key0 <= 16 * blo + 15) {
+        if (key0 + kGT - 1 > 16 * blo) tile_body(I3{}, I1{}, ks, vs, key0);
+        else tile_body(I3{}, I0{}, ks, vs, key0);
+      } else if (hi_rows && key0 <= 16 * bhi + 15) {
+        if (key0 + kGT - 1 > 16 * bhi) tile_body(I2{}, I2{}, ks, vs, key0);
+        else tile_body(I2{}, I0{}, ks, vs, key0);
+      }
       // the state update from this tile: S += (w ⊙ K)^T V over its 64 keys (rows
       // past the chunk's end have weight 0), in steps of 16 keys whose LDS reads
       // are issued one step ahead of their MFMAs
