@@ -188,19 +188,24 @@ __device__ __forceinline__ bf16x8 read_pv(const YOCO_LDS char* tile, int base_ro
 // soon (the state pass's K and V, the output pass's Q rows: measured 7% faster
 // per call at 32K rows than cached copies; the output pass's K and V tiles stay
 // cached, the hint there was slower on ragged batches).
+// (copy i of this thread alone: load_tile_one)
+template <int D, int LAYOUT, bool STREAM = false>
+__device__ __forceinline__ void load_tile_one(const __bf16* src, int64_t row0, int n_rows, int first, int H, int h,
+                                              uint32_t lds, int tid, int i) {
+  constexpr int cpr = D / 8;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int p = i * kGThreads + tid;
+  const int r = first + p / cpr, slot = p % cpr;
+  const int c = slot ^ tile_swizzle<D, LAYOUT>(r);
+  const int rr = r < n_rows ? r : n_rows - 1;
+  if constexpr (STREAM) dma16_nt(src + ((row0 + rr) * H + h) * D + 8 * c, lds + (i * kGThreads + wave * 64) * 16);
+  else dma16(src + ((row0 + rr) * H + h) * D + 8 * c, lds + (i * kGThreads + wave * 64) * 16);
+}
 template <int D, int LAYOUT, bool STREAM = false>
 __device__ __forceinline__ void load_tile(const __bf16* src, int64_t row0, int n_rows, int first, int rows, int H,
                                           int h, uint32_t lds, int tid) {
-  constexpr int cpr = D / 8;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int i = 0; i < rows * cpr / kGThreads; ++i) {
-    const int p = i * kGThreads + tid;
-    const int r = first + p / cpr, slot = p % cpr;
-    const int c = slot ^ tile_swizzle<D, LAYOUT>(r);
-    const int rr = r < n_rows ? r : n_rows - 1;
-    if constexpr (STREAM) dma16_nt(src + ((row0 + rr) * H + h) * D + 8 * c, lds + (i * kGThreads + wave * 64) * 16);
-    else dma16(src + ((row0 + rr) * H + h) * D + 8 * c, lds + (i * kGThreads + wave * 64) * 16);
-  }
+  for (int i = 0; i < rows * (D / 8) / kGThreads; ++i)
+    load_tile_one<D, LAYOUT, STREAM>(src, row0, n_rows, first, H, h, lds, tid, i);
 }
 
 // The A operand of a state-update product, U += (w ⊙ K)^T V over 16 keys: the
@@ -640,6 +645,13 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       load_tile<D, kKdLayout>(kg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st, tid);
       load_tile<D, kPvLayout>(vg, ci.row0 + t * kGT, n_t, 0, kGT, H, h, st + kTile, tid);
     };
+    // copy j (of L) of tile t: K's copies first, then V's
+    auto issue_one = [&](int t, int j) {
+      const uint32_t st = base_lds + out_stage_off(t, kStage);
+      const int n_t = ci.n - t * kGT < kGT ? ci.n - t * kGT : kGT;
+      if (j < L / 2) load_tile_one<D, kKdLayout>(kg, ci.row0 + t * kGT, n_t, 0, H, h, st, tid, j);
+      else load_tile_one<D, kPvLayout>(vg, ci.row0 + t * kGT, n_t, 0, H, h, st + kTile, tid, j - L / 2);
+    };
     // S_c^T into the state area as bf16 (row dv, 16-byte chunk dk / 8; each lane
     // 4 consecutive dk of one dv), once the previous chunk's staged outputs are
     // read (they cover this area for head_dim 128)
@@ -697,8 +709,6 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
       }
     }
     lds_barrier();   // Q^ read by every wave (its area takes tiles 1 and 2); A in LDS
-    if (n_tiles > 1) issue(1);
-    if (n_tiles > 2) issue(2);
     const bool prefetch = cc + 1 < nc;   // then this chunk is whole: four tiles
 
     // block hi holds rows only if block lo does; a block without rows is still
@@ -713,8 +723,12 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
     if (has_state && lo_rows) {
       // inter-chunk term: O^T[dv][j] = sum_dk S^T[dv][dk] q_j[dk], then times 2^A_j;
       // steps (ks, t) with the output block t fastest, each state operand serving
-      // both query blocks, the state reads kGReadsAhead steps ahead
+      // both query blocks, the state reads kGReadsAhead steps ahead. The copies
+      // of tiles 1 and 2 go out one every kEvery steps (issued together, they
+      // held every wave at the load unit)
       constexpr int NS = KS * NT;
+      constexpr int kEvery = NS / (2 * L);
+      static_assert(NS % (2 * L) == 0, "the inter-chunk steps spread the copies of two tiles");
       constexpr int RA = kGReadsAhead;
       const YOCO_LDS char* sl = smem + LY::kS;
       auto read_s = [&](int i) {
@@ -729,6 +743,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
         acc[0][i % NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[i], qf[0][i / NT], acc[0][i % NT], 0, 0, 0);
         acc[1][i % NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa[i], qf[1][i / NT], acc[1][i % NT], 0, 0, 0);
         sched_fence();
+        if (i % kEvery == 0 && 1 + (i / kEvery) / L < n_tiles) issue_one(1 + (i / kEvery) / L, (i / kEvery) % L);
       }
       const float e0 = exp2f(Aj0), e1 = exp2f(Aj1);
 #pragma unroll
@@ -736,6 +751,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gret_out_kernel(GretParams p) {
         acc[0][t] *= e0;
         acc[1][t] *= e1;
       }
+    } else {
+      if (n_tiles > 1) issue(1);
+      if (n_tiles > 2) issue(2);
     }
     if (n_tiles > 3) {
       lds_barrier();   // the state is read by every wave: its area takes tile 3
