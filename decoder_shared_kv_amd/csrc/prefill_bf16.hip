@@ -23,7 +23,11 @@
 // LDS tiles are stored unpadded (the load unit writes 16 bytes per lane,
 // contiguous), with XOR swizzles of the 16-byte chunks chosen on the source
 // side: K^ row r keeps chunk c at c ^ (r mod chunks-per-row), V^ row r at
-// c ^ v_swizzle(r mod 4); both make the reads bank-conflict-free.
+// c ^ v_swizzle(r mod 4); both make the reads bank-conflict-free. The K^ tiles
+// of all stages fill the first half of the LDS and the V^ tiles the second, and
+// the tile loop is unrolled by the stage count, so every operand read is a
+// lane-constant register plus an immediate offset (no address arithmetic per
+// tile).
 //
 // Softmax: online, with the running reference moved lazily (only when a row's
 // max passed it by a slack) and the max itself taken only when the weights
@@ -35,6 +39,9 @@
 // fences stop the compiler from sinking them to their use), and spreads half
 // of the exponentials between the PV MFMAs, which execute while they issue.
 #include <hip/hip_bf16.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "internal.h"
 #include "lds_copy.h"
@@ -73,7 +80,10 @@ struct Geom {
   static constexpr int kChunks = kBN * kCpr;                 // chunks per tile and matrix
   static constexpr int kLoads = kChunks / kPrefillThreads;   // loads per thread, tile and matrix
   static constexpr int kTileBytes = kChunks * 16;
-  static constexpr int kStageBytes = 2 * kTileBytes;         // K^ tile then V^ tile
+  static constexpr int kStageBytes = 2 * kTileBytes;         // one K^ and one V^ tile
+  // V^ tiles start here, K^ tiles at 0; with kStages * kTileBytes <= 64 KB every
+  // read's stage and row offsets fit the LDS instructions' 16-bit immediate
+  static constexpr int kVRegion = kStages * kTileBytes;
   static_assert(kChunks % kPrefillThreads == 0, "every thread issues the same number of loads");
 };
 
@@ -103,12 +113,13 @@ __device__ __forceinline__ void make_issue(Issue<D>& is, int64_t row_stride) {
   }
 }
 
-// Request one K^/V^ tile into a stage. Rows past `last` repeat row `last`.
+// Request one K^/V^ tile into stage st (K^ at smem + st * tile bytes, V^ that
+// far into the V^ region). Rows past `last` repeat row `last`.
 template <int D>
 __device__ __forceinline__ void issue_tile(const Issue<D>& is, const __bf16* kbase, const __bf16* vbase,
-                                           int64_t row_stride, int key0, int last, YOCO_LDS char* stage) {
+                                           int64_t row_stride, int key0, int last, YOCO_LDS char* smem, int st) {
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)stage + wave * 64 * 16;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + st * Geom<D>::kTileBytes + wave * 64 * 16;
   if (key0 + kBN - 1 <= last) {
     // whole tile inside the sequence: one scalar base per matrix
     const int64_t toff = (int64_t)key0 * row_stride;
@@ -118,7 +129,7 @@ __device__ __forceinline__ void issue_tile(const Issue<D>& is, const __bf16* kba
     for (int i = 0; i < Geom<D>::kLoads; ++i) {
       const uint32_t kd = lds0 + i * kPrefillThreads * 16;
       dma16(kt, is.koff[i], kd);
-      dma16(vt, is.voff[i], kd + Geom<D>::kTileBytes);
+      dma16(vt, is.voff[i], kd + Geom<D>::kVRegion);
     }
   } else {
 #pragma unroll
@@ -128,12 +139,13 @@ __device__ __forceinline__ void issue_tile(const Issue<D>& is, const __bf16* kba
       const int64_t roff = (int64_t)key * row_stride;
       const uint32_t kd = lds0 + i * kPrefillThreads * 16;
       dma16(kbase + roff + is.kcol[i], kd);
-      dma16(vbase + roff + is.vcol[i], kd + Geom<D>::kTileBytes);
+      dma16(vbase + roff + is.vcol[i], kd + Geom<D>::kVRegion);
     }
   }
 }
 
-// Lane-constant LDS byte offsets of the reads of one tile.
+// Lane-constant LDS byte offsets of the reads of one tile, relative to its
+// stage's K^ tile (the V^ offsets include the distance to the V^ region).
 template <int D>
 struct ReadOffs {
   int k[D / 16];   // K^ A operand, step kk: row qj, chunk (2kk + hf) swizzled (+ kb * 32 rows)
@@ -152,8 +164,14 @@ __device__ __forceinline__ void make_read_offs(ReadOffs<D>& ro, int lane) {
   for (int t = 0; t < D / 32; ++t) {
     // source row 4h + q of the 4-key group; dims 32t + 16(g%2) + 4w .. +3
     const int chunk = (4 * t + 2 * (g & 1) + (w >> 1)) ^ v_swizzle<D>(q);   // row 4h + q: r & 3 = q
-    ro.v[t] = (4 * h + q) * (D * 2) + 16 * chunk + 8 * (w & 1);
+    ro.v[t] = Geom<D>::kVRegion + (4 * h + q) * (D * 2) + 16 * chunk + 8 * (w & 1);
   }
+}
+
+// Calls f(integral_constant<int, 0>), f(..1>), ... in order while it returns true.
+template <class F, int... I>
+__device__ __forceinline__ bool each_stage(F& f, std::integer_sequence<int, I...>) {
+  return (f(std::integral_constant<int, I>{}) && ...);
 }
 
 // Keeps the compiler's scheduler from moving instructions across this point,
@@ -171,10 +189,10 @@ __device__ __forceinline__ bf16x8 read_k(const YOCO_LDS char* ks, const ReadOffs
 }
 
 // V^T A operand of PV step j (keys 32kb + 16cc + {0..3, 8..11} + 4h, dims of
-// tile t): two transposing reads, rows +0 and +8.
+// tile t): two transposing reads, rows +0 and +8. `tile` is the stage's K^ tile.
 template <int D>
-__device__ __forceinline__ bf16x8 read_v(const YOCO_LDS char* vs, const ReadOffs<D>& ro, int kb, int cc, int t) {
-  const YOCO_LDS char* base = vs + (32 * kb + 16 * cc) * (D * 2) + ro.v[t];
+__device__ __forceinline__ bf16x8 read_v(const YOCO_LDS char* tile, const ReadOffs<D>& ro, int kb, int cc, int t) {
+  const YOCO_LDS char* base = tile + (32 * kb + 16 * cc) * (D * 2) + ro.v[t];
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(base));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YOCO_LDS s16x4*)(base + 8 * (D * 2)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -291,10 +309,11 @@ __device__ __forceinline__ void pv_index(int j, int& kb, int& cc, int& t) {
 // yet (m = -inf) takes the max at once. Either way the weights that reach the
 // MFMAs and the row sum use one m, and the running max itself is no longer
 // computed on most tiles (about 20 VALU instructions per tile and wave fewer).
+// neg_m is kept with m (-m, or 0 while m = -inf) and changes only with it.
 template <int D, int MASK>
-__device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<D>& ro, f32x16 (&s)[2],
-                                        f32x16 (&acc)[D / 32], float& m, float& l, int key0, int pos, int window,
-                                        float c, int hf) {
+__device__ __forceinline__ void sv_step(const YOCO_LDS char* tile, const ReadOffs<D>& ro, f32x16 (&s)[2],
+                                        f32x16 (&acc)[D / 32], float& m, float& neg_m, float& l, int key0, int pos,
+                                        int window, float c, int hf) {
   constexpr int NV = D / 8;        // PV steps: (kb, cc, t)
   constexpr int RA = kReadsAhead;
   // the first V^ operands go out before the softmax, which hides their latency
@@ -303,27 +322,24 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
   for (int j = 0; j < RA; ++j) {
     int kb, cc, t;
     pv_index<D>(j, kb, cc, t);
-    va[j] = read_v<D>(vs, ro, kb, cc, t);
+    va[j] = read_v<D>(tile, ro, kb, cc, t);
   }
   sched_fence();
   apply_mask<MASK>(s, key0, pos, window, hf);
   uint32_t w[2][2][4];
   // a row without a reference yet (m = -inf: its first keys) takes the max first
   bool exact = __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
-  float neg_m = -m;
   float la;
   for (;;) {   // at most twice: after a rescale the weights are taken as they are
     if (exact) neg_m = rescale_to_max<D>(s, 0, acc, m, l, c);
-    la = 0.f;
+    la = softmax_word(s, w, c, neg_m, 0, 0, 0);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) la += softmax_word(s, w, c, neg_m, 0, cc, i);
+    for (int wi = 1; wi < 8; ++wi) la += softmax_word(s, w, c, neg_m, 0, wi >> 2, wi & 3);
     if (exact || __builtin_amdgcn_ballot_w64(!(la <= kWeightCap)) == 0) break;
     exact = true;
   }
   l += la;
-  float lb = 0.f;
+  float lb;
   sched_fence();
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -333,9 +349,9 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
       // the second half's weights are checked before its first MFMA
       if (__builtin_amdgcn_ballot_w64(!(lb <= kWeightCap)) != 0) {
         neg_m = rescale_to_max<D>(s, 1, acc, m, l, c);
-        lb = 0.f;
+        lb = softmax_word(s, w, c, neg_m, 1, 0, 0);
 #pragma unroll
-        for (int wi = 0; wi < 8; ++wi) lb += softmax_word(s, w, c, neg_m, 1, wi >> 2, wi & 3);
+        for (int wi = 1; wi < 8; ++wi) lb += softmax_word(s, w, c, neg_m, 1, wi >> 2, wi & 3);
       }
       l += lb;
       sched_fence();
@@ -343,7 +359,7 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
     if (j + RA < NV) {
       int kb2, cc2, t2;
       pv_index<D>(j + RA, kb2, cc2, t2);
-      va[j + RA] = read_v<D>(vs, ro, kb2, cc2, t2);
+      va[j + RA] = read_v<D>(tile, ro, kb2, cc2, t2);
     }
     const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[kb][cc][0], w[kb][cc][1], w[kb][cc][2], w[kb][cc][3]));
     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb, acc[t], 0, 0, 0);
@@ -352,7 +368,8 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* vs, const ReadOffs<
 #pragma unroll
       for (int q = 0; q < 8 / (NV / 2); ++q) {
         const int wi = j * (8 / (NV / 2)) + q;
-        lb += softmax_word(s, w, c, neg_m, 1, wi >> 2, wi & 3);
+        const float e = softmax_word(s, w, c, neg_m, 1, wi >> 2, wi & 3);
+        lb = wi == 0 ? e : lb + e;
       }
     }
     sched_fence();
@@ -510,11 +527,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     const int wave_key_lo = win > 0 ? max(0, min(r0 + offset, n_kv - 1) - win + 1) : 0;
     const int band_full = win > 0 ? min(wave_max_pos, n_kv - 1) - win + 1 : 0;
 
-    // the tiles ahead go out first: they have the longest way
+    // the tiles ahead go out first: they have the longest way. Tile kt of this
+    // pass goes to stage (kt - kt_lo) mod S
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
       if (kt_lo + st < n_tiles)
-        issue_tile<D>(is, kbase, vbase, row_stride, (kt_lo + st) * kBN, n_kv - 1, smem + ((kt_lo + st) % kStages) * kStage);
+        issue_tile<D>(is, kbase, vbase, row_stride, (kt_lo + st) * kBN, n_kv - 1, smem, st);
 
     bf16x8 qf[D / 16];
     {
@@ -532,30 +550,38 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     f32x16 acc[D / 32];
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, neg_m = 0.f, l = 0.f;
 
-    for (int kt = kt_lo; kt < n_tiles; ++kt) {
+    // One tile, from stage U (a constant, so every operand read is a register
+    // plus an immediate offset); false once the pass has no tile kt0 + U.
+    int kt0 = kt_lo;
+    auto tile_step = [&](auto stage) __attribute__((always_inline)) -> bool {
+      constexpr int u = decltype(stage)::value;
+      const int kt = kt0 + u;
+      if (kt >= n_tiles) return false;
       // tile kt has landed in LDS (this thread's part): at most the tiles
       // requested after it may still be in flight
       wait_tiles<L>(min(kStages - 2, n_tiles - 1 - kt));
-      barrier_only();  // every thread's part of tile kt is in; stage (kt - 1) % S is free
+      barrier_only();  // every thread's part of tile kt is in; the stage of tile kt - 1 is free
       if (kt + kStages - 1 < n_tiles)
-        issue_tile<D>(is, kbase, vbase, row_stride, (kt + kStages - 1) * kBN, n_kv - 1,
-                      smem + ((kt + kStages - 1) % kStages) * kStage);
+        issue_tile<D>(is, kbase, vbase, row_stride, (kt + kStages - 1) * kBN, n_kv - 1, smem,
+                      (u + kStages - 1) % kStages);
       const int key0 = kt * kBN;
       if (wave_active && key0 <= wave_max_pos && key0 + kBN > wave_key_lo) {
-        const YOCO_LDS char* ks = smem + (kt % kStages) * kStage;
-        const YOCO_LDS char* vs = ks + Geom<D>::kTileBytes;
+        const YOCO_LDS char* tile = smem + u * Geom<D>::kTileBytes;   // K^ here, V^ by the offsets in ro.v
         f32x16 s[2];
-        qk_step<D>(ks, ro, qf, s);
+        qk_step<D>(tile, ro, qf, s);
         if (win > 0 && key0 < band_full)
-          sv_step<D, 2>(vs, ro, s, acc, m, l, key0, my_pos, win, c, hf);
+          sv_step<D, 2>(tile, ro, s, acc, m, neg_m, l, key0, my_pos, win, c, hf);
         else if (kt >= full_tiles)
-          sv_step<D, 1>(vs, ro, s, acc, m, l, key0, my_pos, win, c, hf);
+          sv_step<D, 1>(tile, ro, s, acc, m, neg_m, l, key0, my_pos, win, c, hf);
         else
-          sv_step<D, 0>(vs, ro, s, acc, m, l, key0, my_pos, win, c, hf);
+          sv_step<D, 0>(tile, ro, s, acc, m, neg_m, l, key0, my_pos, win, c, hf);
       }
-    }
+      return true;
+    };
+    for (; kt0 < n_tiles; kt0 += kStages)
+      if (!each_stage(tile_step, std::make_integer_sequence<int, kStages>{})) break;
     wait_vm_lgkm0<0>();
     barrier_only();  // every wave is done with the tiles: the stages become the output staging area
 
