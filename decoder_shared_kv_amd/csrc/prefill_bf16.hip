@@ -376,6 +376,17 @@ __device__ __forceinline__ void sv_step(const YOCO_LDS char* tile, const ReadOff
   }
 }
 
+// 0 in a vector register, unknown to the optimiser. Added to the address of the
+// claim made ahead, it keeps the compiler from combining that atomic across the
+// wave (which reads its result back at once and so waits for its round trip
+// and every copy in flight): the result is then first awaited where it is used,
+// at the end of the item.
+__device__ __forceinline__ int lane_zero() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
 // Work-queue fetch (thread 0 of a workgroup): the next item of this XCD's
 // queue, else of the first other queue that still has items; n_items when all
 // are empty. The counters of all queues are read in one round trip, then one
@@ -546,7 +557,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     // tile copies, which the loop awaits by count
     wait_vm_lgkm0<0>();
     if (dyn && threadIdx.x == 0 && pw == pw0 && seen < own - 4 * (int)(gridDim.x / kXcds))
-      spec = __hip_atomic_fetch_add(p.queue + xcd * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      spec = __hip_atomic_fetch_add(p.queue + xcd * kQueueStride + lane_zero(), 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
