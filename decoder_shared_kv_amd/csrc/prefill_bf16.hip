@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(AttnPa
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
     float m = -INFINITY, neg_m = 0.f, l = 0.f;
 
-    // One tile, from stage u (a constant, so every operand read is a register
+    // One tile, from stage U (a constant, so every operand read is a register
     // plus an immediate offset); false once the pass has no tile kt0 + U.
     int kt0 = kt_lo;
     auto tile_step = [&](auto stage) __attribute__((always_inline)) -> bool {
